@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4 mixture-of-experts block on one MI355X.
+
+Default workload (one JSON line on stdout): decode, T=1 token per layer-call,
+hidden 2048, 256 experts top-8 + one shared expert, intermediate 512, 4-bit
+weights in groups of 64, over 40 independently seeded layers used in rotation
+(18.3 GB of packed weights, so every layer-call reads its experts from HBM, not
+from the 256 MiB Infinity Cache) with a fresh activation row per layer-call.
+
+A step is one decode token through all 40 layers: 40 x (route + forward).
+value = MoE-layer tokens per second = 40 * T * steps / elapsed.
+
+The same line carries:
+  roofline      the dominant kernel's algorithmic bytes (or flops) per launch over
+                its average duration, timed with HIP events recorded around each
+                kernel on the launch stream in a second pass over the same steps
+  cpu_baseline  the CPU oracle (float64 NumPy) timed on a bounded sample of the
+                same workload on this host
+  prefill       the T=2048 Zipf-skewed prefill layer-call (8 layers rotated):
+                tokens/s and the MFMA roofline of its dominant kernel
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MoE-layer tokens/sec + %HBM roofline (T=1) and %MFMA peak (T=2048)"
+
+ROUTE_SMALL = ["route_small"]
+ROUTE_LARGE = ["router_logits", "router_topk", "router_perm"]
+FWD_DECODE = ["decode_gateup", "decode_down"]
+FWD_GROUPED = ["grouped_gateup", "grouped_down", "finalize"]
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the runtime's C API (the library launches on the stream
+# passed to it; events recorded there bracket its kernels)
+# ---------------------------------------------------------------------------
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4_dequant_grouped_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str, launches_per_unit=1):
+    """HBM bytes per launch measured with rocprofv3 counters, if a summary for this
+    kernel, this workload and the current kernel sources exists under profiles/."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    ent = doc.get(f"{workload}:{kernel}")
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def expert_bytes(H, I, G=64):
+    mat = lambda N, K: N * K // 2 + 2 * 2 * N * (K // G)   # noqa: E731
+    return mat(I, H), mat(H, I)      # one of gate/up, down
+
+
+def make_layers(shape, n_layers, seed0, device):
+    from w4_dequant_grouped_amd import synth
+    return [synth.draw_layer(shape, seed0 + l, device=device) for l in range(n_layers)]
+
+
+def time_steps(step_fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step_fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step_fn(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def kernel_times(blocks, xs, steps, ev: HipEvents, route_names, fwd_names):
+    """Average duration per kernel name over `steps` passes over all blocks."""
+    import torch
+    nr, nf = len(route_names), len(fwd_names)
+    per_call = []
+    events = []
+    for s in range(steps):
+        for l, blk in enumerate(blocks):
+            re_ = ev.create(2 * nr)
+            fe_ = ev.create(2 * nf)
+            kr, kf = blk.timed(xs[s % len(xs)][l], re_, fe_)
+            assert kr == nr and kf == nf, (kr, kf)
+            events.append((re_, fe_))
+    torch.cuda.synchronize()
+    sums = {n: 0.0 for n in route_names + fwd_names}
+    for re_, fe_ in events:
+        for i, n in enumerate(route_names):
+            sums[n] += ev.elapsed_ms(re_[2 * i], re_[2 * i + 1])
+        for i, n in enumerate(fwd_names):
+            sums[n] += ev.elapsed_ms(fe_[2 * i], fe_[2 * i + 1])
+        ev.destroy(re_)
+        ev.destroy(fe_)
+    ncalls = len(events)
+    return {n: 1e3 * v / ncalls for n, v in sums.items()}   # microseconds per launch
+
+
+def run_decode(args, ev):
+    import torch
+    from w4_dequant_grouped_amd import moe_w4 as B
+    from w4_dequant_grouped_amd import synth
+
+    T, H, I, E, k = args.tokens, 2048, 512, 256, 8
+    L = args.layers
+    shape = synth.BlockShape(T=T, H=H, I=I, E=E, top_k=k)
+    layers = make_layers(shape, L, 1000, "cuda")
+    ws = B.alloc_workspace(B.make_dims(T, H, I, E, k))
+    blocks = [B.Block(layer, T, k, workspace=ws) for layer in layers]
+    nx = args.steps + args.warmup
+    g = synth.generator(77, "cuda")
+    xs = [[torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16) for _ in range(L)]
+          for _ in range(nx)]
+
+    def step(i=0):
+        for l, blk in enumerate(blocks):
+            blk(xs[i % nx][l])
+
+    elapsed = time_steps(step, args.steps, args.warmup)
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = L * T * args.steps / elapsed
+
+    kt = kernel_times(blocks, xs, min(args.steps, 10), ev, ROUTE_SMALL, FWD_DECODE)
+    # algorithmic bytes per launch from the routing each layer produced
+    gu_b, dn_b = expert_bytes(H, I)
+    active = []
+    for blk in blocks:
+        active.append(int((blk.routing.counts > 0).sum().item()))
+    n_act = sum(active) / len(active)
+    alg = {
+        "route_small": E * H * 4 + T * H * 2 + T * k * 8 + (2 * E + 1 + T * k) * 4,
+        "decode_gateup": (n_act + 1) * 2 * gu_b + T * H * 2 + (T * k + T) * I * 2,
+        "decode_down": (n_act + 1) * dn_b + (T * k + T) * I * 2 + T * H * 2,
+    }
+    dom = max(FWD_DECODE + ROUTE_SMALL, key=lambda n: kt[n])
+    achieved = alg[dom] / (kt[dom] * 1e-6) / 1e9
+    layer_bytes = E * H * 4 + (n_act + 1) * (2 * gu_b + dn_b) + 2 * T * H * 2
+    roofline = {
+        "bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic_from_profiles(dom, "decode"),
+        "alg_bytes_per_launch": int(alg[dom]), "avg_launch_us": round(kt[dom], 3),
+        "kernel_us": {n: round(v, 3) for n, v in kt.items()},
+        "layer_call_alg_bytes": int(layer_bytes),
+        "layer_call_hbm_frac": round(layer_bytes / (ms_per_step / L * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "active_experts_per_call": n_act,
+    }
+    config = {"workload": f"decode T={T} (40-layer rotation), H={H}, I={I}, E={E} top-{k} + shared, "
+                          f"W4 group 64", "T": T, "H": H, "I": I, "E": E, "top_k": k,
+              "layers": L, "shared_expert": True}
+    return value, ms_per_step, roofline, config
+
+
+def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
+    import torch
+    from w4_dequant_grouped_amd import moe_w4 as B
+    from w4_dequant_grouped_amd import synth
+
+    H, I, E, k = 2048, 512, 256, 8
+    shape = synth.BlockShape(T=T, H=H, I=I, E=E, top_k=k, router_bias="zipf")
+    layers = make_layers(shape, L, 3000, "cuda")
+    ws = B.alloc_workspace(B.make_dims(T, H, I, E, k))
+    blocks = [B.Block(layer, T, k, workspace=ws) for layer in layers]
+    g = synth.generator(78, "cuda")
+    xs = [[torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16) for _ in range(L)]]
+
+    def step(i=0):
+        for l, blk in enumerate(blocks):
+            blk(xs[0][l])
+
+    elapsed = time_steps(step, steps, warmup)
+    per_call_ms = 1e3 * elapsed / (steps * L)
+    kt = kernel_times(blocks, xs, steps, ev, ROUTE_LARGE, FWD_GROUPED)
+    rows = T * k + T
+    flops = {"grouped_gateup": 2.0 * rows * H * 2 * I, "grouped_down": 2.0 * rows * I * H}
+    dom = max(flops, key=lambda n: kt[n])
+    tflops = flops[dom] / (kt[dom] * 1e-6) / 1e12
+    layer_flops = flops["grouped_gateup"] + flops["grouped_down"]
+    return {
+        "workload": f"prefill T={T} Zipf-skewed router bias, 8-layer rotation, same shapes",
+        "tokens_per_s": round(T / (per_call_ms * 1e-3), 1),
+        "ms_per_layer_call": round(per_call_ms, 4),
+        "layer_call_mfma_frac": round(layer_flops / (per_call_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_from_profiles(dom, "prefill2048"),
+                     "alg_flops_per_launch": flops[dom], "avg_launch_us": round(kt[dom], 3),
+                     "kernel_us": {n: round(v, 3) for n, v in kt.items()}},
+    }
+
+
+def cpu_baseline(T=1, max_calls=24, budget_s=20.0):
+    """The oracle as it stands, on this host's cores, on a bounded sample."""
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_w4_oracle as O
+    from w4_dequant_grouped_amd import synth
+
+    shape = synth.BlockShape(T=T, H=2048, I=512, E=256, top_k=8)
+    layer = synth.draw_layer(shape, 1000, device="cpu")
+    calls = 0
+    t0 = time.perf_counter()
+    while calls < max_calls and time.perf_counter() - t0 < budget_s:
+        x = synth.draw_x(T, shape.H, 500 + calls)
+        r = O.route(x, layer.router_w, layer.router_b, shape.top_k)
+        O.forward_grouped(x, layer, r, shape.group)
+        calls += 1
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(calls * T / el, 3), "unit": "layer-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{calls} decode layer-calls (T={T}) of one seeded full-size layer, "
+                      f"float64 NumPy oracle (route + grouped forward), {el:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--tokens", type=int, default=1, help="decode rows per layer-call (1..5)")
+    ap.add_argument("--layers", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the block's multi-GPU sharding is a design note, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from w4_dequant_grouped_amd import moe_w4 as B
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.load_library()          # raises if the HIP library is missing: there is no fallback
+    ev = HipEvents()
+
+    print(f"[bench] decode: {args.layers} layers, T={args.tokens}, steps={args.steps}", file=sys.stderr, flush=True)
+    value, ms_per_step, roofline, config = run_decode(args, ev)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "layer-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded W4 layers and activations)", "config": config,
+        "roofline": roofline,
+    }
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        print("[bench] prefill T=2048 zipf", file=sys.stderr, flush=True)
+        line["prefill"] = run_prefill(args, ev)
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(T=args.tokens)
+    line["source_hash"] = source_hash()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+"""The C ABI on the host: the library loads, exports what include/moe_w4.h
+declares, sizes its workspace, and rejects bad arguments before launching
+anything.  No call here reaches a kernel launch (each has one defect that the
+host-side checks catch first), so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4_dequant_grouped_amd import moe_w4 as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4.h")
+
+OK, ERR_NULL, ERR_DIMS, ERR_TOPK, ERR_GROUP, ERR_ALIGN, ERR_WS, ERR_LAUNCH, ERR_FLAGS = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
+
+FAKE = 0x7F0000000000          # aligned, never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("library not built")
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_w4_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(B.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (OK, ERR_NULL, ERR_DIMS, ERR_TOPK, ERR_GROUP, ERR_ALIGN, ERR_WS, ERR_LAUNCH, ERR_FLAGS):
+        s = B.moe_w4_status_string(code)
+        assert s and s != "unknown status"
+    assert B.moe_w4_status_string(12345) == "unknown status"
+    assert B.moe_w4_last_error() == ""
+
+
+def _dims(**kw):
+    d = dict(T=16, H=256, I=128, E=16, top_k=2, group=64, flags=0)
+    d.update(kw)
+    return B.make_dims(**d)
+
+
+def test_workspace_bytes(lib):
+    small = B.moe_w4_workspace_bytes(_dims())
+    big = B.moe_w4_workspace_bytes(_dims(T=2048, H=2048, I=512, E=256, top_k=8))
+    assert small > 0 and small % 256 == 0
+    # logits + bitmask + h (T*k + T rows) + fp32 accumulator; no expanded-weight term
+    T, H, I, E, k = 2048, 2048, 512, 256, 8
+    expect_min = T * E * 4 + (T * k + T) * I * 2 + T * H * 4
+    assert expect_min <= big <= expect_min + 256 * 8 + E * ((T + 31) // 32) * 4 + 4096
+    assert big < E * I * H * 2 // 10      # far below one bf16 copy of the routed weights
+    for bad in (_dims(group=32), _dims(H=300), _dims(I=100), _dims(top_k=0), _dims(top_k=17),
+                _dims(E=1025), _dims(T=-1), _dims(flags=1), _dims(top_k=20, E=16)):
+        assert B.moe_w4_workspace_bytes(bad) == 0
+
+
+def _route(lib, dims, x=FAKE, wr=FAKE, br=None, ids=FAKE, w=FAKE, cnt=FAKE, off=FAKE, perm=FAKE,
+           ws=FAKE, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return lib.moe_w4_route(ctypes.byref(dims) if dims is not None else None, x, wr, br, ids, w, cnt,
+                            off, perm, ws, ws_bytes, stream)
+
+
+def _weights(codes=FAKE, scales=FAKE, biases=FAKE):
+    m = B.moe_w4_mat(codes, scales, biases)
+    good = B.moe_w4_mat(FAKE, FAKE, FAKE)
+    return B.moe_w4_weights(m, good, good)
+
+
+def _forward(lib, dims, x=FAKE, routed=None, shared=None, w=FAKE, off=FAKE, perm=FAKE, out=FAKE + 4096,
+             ws=FAKE, ws_bytes=None):
+    routed = routed if routed is not None else _weights()
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return lib.moe_w4_forward(ctypes.byref(dims) if dims is not None else None, x,
+                              ctypes.byref(routed), None if shared is None else ctypes.byref(shared),
+                              None, w, off, perm, out, ws, ws_bytes, None)
+
+
+def test_route_rejects_bad_arguments(lib):
+    assert _route(lib, None) == ERR_NULL
+    assert _route(lib, _dims(T=0)) == OK                    # empty batch: nothing to do
+    assert _route(lib, _dims(flags=2)) == ERR_FLAGS
+    assert _route(lib, _dims(T=70000)) == ERR_DIMS
+    assert _route(lib, _dims(E=0)) == ERR_DIMS
+    assert _route(lib, _dims(top_k=17)) == ERR_TOPK
+    assert _route(lib, _dims(top_k=17, E=32)) == ERR_TOPK
+    assert _route(lib, _dims(top_k=0)) == ERR_TOPK
+    assert _route(lib, _dims(group=128)) == ERR_GROUP
+    assert _route(lib, _dims(H=384)) == ERR_GROUP
+    assert _route(lib, _dims(), x=None) == ERR_NULL
+    assert _route(lib, _dims(), wr=None) == ERR_NULL
+    assert _route(lib, _dims(), perm=None) == ERR_NULL
+    assert _route(lib, _dims(), ws=None) == ERR_NULL
+    assert _route(lib, _dims(), x=FAKE + 2) == ERR_ALIGN
+    assert _route(lib, _dims(), wr=FAKE + 4) == ERR_ALIGN
+    assert _route(lib, _dims(), ws=FAKE + 64) == ERR_ALIGN
+    assert _route(lib, _dims(), br=FAKE + 1) == ERR_ALIGN
+    d = _dims()
+    assert _route(lib, d, ws_bytes=B.moe_w4_workspace_bytes(d) - 1) == ERR_WS
+
+
+def test_forward_rejects_bad_arguments(lib):
+    assert _forward(lib, None) == ERR_NULL
+    assert _forward(lib, _dims(T=0)) == OK
+    assert _forward(lib, _dims(flags=1)) == ERR_FLAGS
+    assert _forward(lib, _dims(I=192)) == ERR_GROUP
+    assert _forward(lib, _dims(top_k=3, E=2)) == ERR_TOPK
+    assert _forward(lib, _dims(), x=None) == ERR_NULL
+    assert _forward(lib, _dims(), out=None) == ERR_NULL
+    assert _forward(lib, _dims(), routed=_weights(codes=None)) == ERR_NULL
+    assert _forward(lib, _dims(), routed=_weights(scales=None)) == ERR_NULL
+    assert _forward(lib, _dims(), shared=_weights(biases=None)) == ERR_NULL
+    assert _forward(lib, _dims(), routed=_weights(codes=FAKE + 8)) == ERR_ALIGN
+    assert _forward(lib, _dims(), shared=_weights(scales=FAKE + 1)) == ERR_ALIGN
+    assert _forward(lib, _dims(), out=FAKE + 2) == ERR_ALIGN
+    assert _forward(lib, _dims(), x=FAKE + 8) == ERR_ALIGN
+    d = _dims()
+    assert _forward(lib, d, ws_bytes=B.moe_w4_workspace_bytes(d) - 256) == ERR_WS

@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Routing ids, counts, offsets and the permutation are compared bit for bit on
+inputs whose k-th/(k+1)-th logit gap is at least 1e-3; routing weights within
+1e-5; block outputs within max|gpu - ref| / max|ref| <= 1e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_w4_oracle as O
+from w4_dequant_grouped_amd import moe_w4 as B
+from w4_dequant_grouped_amd import synth
+
+from parity_util import (check_output, check_routing, full_check, make_inputs, note, run_block,
+                         sampled_rows)
+
+pytestmark = pytest.mark.gpu
+
+S = synth.BlockShape
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load_library()
+
+
+# --- small configurations, full oracle -------------------------------------------
+
+def test_tiny_workload():
+    wl = synth.WORKLOADS["tiny"]
+    full_check(wl.shape, wl.seed, what="tiny")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5])
+def test_decode_small_dims(T):
+    full_check(S(T=T, H=512, I=256, E=32, top_k=4), 40 + T, what=f"decode-small T={T}")
+
+
+@pytest.mark.parametrize("T", [6, 8, 9, 33])
+def test_grouped_small_dims(T):
+    # T=6: smallest grouped call; T=8/9: last one-launch router / first tiled router
+    full_check(S(T=T, H=512, I=256, E=32, top_k=4), 50 + T, what=f"grouped-small T={T}")
+
+
+def test_grouped_multi_tile_ragged():
+    # 1200 routed rows over 32 experts, shared expert 300 rows = 3 M-tiles (ragged)
+    full_check(S(T=300, H=512, I=256, E=32, top_k=4), 61, what="multi-tile")
+
+
+def test_one_expert_takes_every_token():
+    shape = S(T=700, H=256, I=128, E=8, top_k=2)
+    layer = synth.draw_layer(shape, 62)
+    layer.router_b = torch.zeros(8, dtype=torch.float32)
+    layer.router_b[3] = 40.0            # every token picks expert 3: 700 rows, 6 M-tiles
+    full_check(shape, 62, layer=layer, what="one hot expert")
+
+
+@pytest.mark.parametrize("T", [1, 40])
+def test_all_experts_selected(T):
+    full_check(S(T=T, H=256, I=128, E=8, top_k=8), 63 + T, what=f"k=E T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 20])
+def test_top1_no_shared(T):
+    full_check(S(T=T, H=256, I=128, E=16, top_k=1, shared=False), 65 + T, what=f"top1 T={T}")
+
+
+@pytest.mark.parametrize("T", [4, 64])
+def test_top16(T):
+    full_check(S(T=T, H=256, I=128, E=64, top_k=16), 67 + T, what=f"top16 T={T}")
+
+
+def test_zero_tokens_is_a_no_op():
+    shape = S(T=0, H=256, I=128, E=8, top_k=2)
+    layer = synth.draw_layer(S(T=1, H=256, I=128, E=8, top_k=2), 70).to("cuda")
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    dims = B.make_dims(0, 256, 128, 8, 2)
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    r = B.alloc_routing(0, 8, 2)
+    B.moe_w4_route(dims, x, layer.router_w, None, r, ws)
+    out = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    B.moe_w4_forward(dims, x, layer.routed, layer.shared, r, out, ws)
+    torch.cuda.synchronize()
+
+
+# --- full-size configurations ---------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def full_layer():
+    note("[gpu] drawing one full-size layer (H=2048, I=512, E=256)")
+    return synth.draw_layer(S(T=1, H=2048, I=512, E=256, top_k=8), synth.WORKLOADS["decode"].seed)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5])
+def test_decode_full_size(full_layer, T):
+    shape = S(T=T, H=2048, I=512, E=256, top_k=8)
+    full_check(shape, 100 + T, layer=full_layer, what=f"decode full T={T}")
+
+
+def _sampled_full(shape, seed, layer, what, nrows=12):
+    note(f"[gpu] {what}: {synth.describe(shape)} seed={seed}")
+    layer, x = make_inputs(shape, seed, layer)
+    ref_r = O.route(x, layer.router_w, layer.router_b, shape.top_k)
+    r, out = run_block(layer.to("cuda"), x.cuda(), shape)
+    check_routing(r, ref_r, what)
+    rows = sampled_rows(shape.T, nrows, seed)
+    y = O.forward_dense(x, layer, ref_r, shape.group, rows=rows)
+    check_output(out, y, rows=rows, what=what)
+    return ref_r
+
+
+def test_prefill_512_full_size(full_layer):
+    wl = synth.WORKLOADS["prefill512"]
+    _sampled_full(wl.shape, wl.seed, full_layer, "prefill T=512")
+
+
+def test_prefill_2048_zipf_full_size():
+    wl = synth.WORKLOADS["prefill2048_zipf"]
+    layer = synth.draw_layer(wl.shape, wl.seed)
+    ref_r = _sampled_full(wl.shape, wl.seed, layer, "prefill T=2048 zipf")
+    counts = ref_r.counts
+    assert (counts == 0).any() and counts.max() > 4 * counts.mean()
+
+
+# --- properties -------------------------------------------------------------------------
+
+def test_repeat_calls_and_workspace_reuse(full_layer):
+    """Same workspace for a T=2048 call, then T=1, then T=2048 again: the control
+    block returns to zero and results repeat (routing bit-identical)."""
+    big = S(T=2048, H=2048, I=512, E=256, top_k=8)
+    layer = full_layer.to("cuda")
+    _, xb = make_inputs(big, 301, full_layer)
+    _, x1 = make_inputs(S(T=1, H=2048, I=512, E=256, top_k=8), 302, full_layer)
+    ws = B.alloc_workspace(B.make_dims(2048, 2048, 512, 256, 8))
+    r1, o1 = run_block(layer, xb.cuda(), big, workspace=ws)
+    r1 = [t.clone() for t in (r1.ids, r1.counts, r1.offsets, r1.perm)]
+    o1 = o1.clone()
+    rs, os_ = run_block(layer, x1.cuda(), S(T=1, H=2048, I=512, E=256, top_k=8), workspace=ws)
+    ref1 = O.route(x1, full_layer.router_w, None, 8)
+    check_routing(rs, ref1, "T=1 after T=2048")
+    assert int(ws[:256].cpu().sum()) == 0
+    r2, o2 = run_block(layer, xb.cuda(), big, workspace=ws)
+    for a, b in zip(r1, (r2.ids, r2.counts, r2.offsets, r2.perm)):
+        assert torch.equal(a, b)
+    diff = (o1.float() - o2.float()).abs().max().item()
+    assert diff <= 1e-2 * o1.float().abs().max().item()
+
+
+def test_decode_is_deterministic(full_layer):
+    shape = S(T=3, H=2048, I=512, E=256, top_k=8)
+    layer = full_layer.to("cuda")
+    _, x = make_inputs(shape, 303, full_layer)
+    _, o1 = run_block(layer, x.cuda(), shape)
+    o1 = o1.clone()
+    _, o2 = run_block(layer, x.cuda(), shape)
+    assert torch.equal(o1, o2)
+
+
+def test_token_permutation_invariance_gpu():
+    shape = S(T=96, H=512, I=256, E=32, top_k=4)
+    layer, x = make_inputs(shape, 304)
+    p = torch.randperm(shape.T, generator=synth.generator(5))
+    lg = layer.to("cuda")
+    r1, o1 = run_block(lg, x.cuda(), shape)
+    o1 = o1.clone()
+    c1 = r1.counts.clone()
+    r2, o2 = run_block(lg, x[p].cuda(), shape)
+    assert torch.equal(r2.counts, c1)
+    ref = o1.float()[p.cuda()]
+    assert (o2.float() - ref).abs().max().item() <= 1e-2 * ref.abs().max().item()

@@ -1,0 +1,101 @@
+// Device-side helpers shared by the gfx950 kernels of the W4 MoE block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_w4 {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 64;   // quantisation group along K
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// --- scalar conversions ----------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf16lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+// Two floats -> one dword of two bf16 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// --- 4-bit code unpacking -----------------------------------------------------
+// A dword of packed codes holds k = 0..7 of a row: byte i = (c[2i+1] << 4) | c[2i].
+
+// Dequantise 8 codes to bf16 with w = c * s + b (fp32 FMA, one RNE rounding).
+// Natural k order: element i of the result is k = i.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t d, float s, float b) {
+    const uint32_t lo = d & 0x0F0F0F0Fu;          // c0 c2 c4 c6 in bytes 0..3
+    const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;   // c1 c3 c5 c7
+    float w0 = fmaf((float)(lo & 0xFF), s, b);
+    float w1 = fmaf((float)(hi & 0xFF), s, b);
+    float w2 = fmaf((float)((lo >> 8) & 0xFF), s, b);
+    float w3 = fmaf((float)((hi >> 8) & 0xFF), s, b);
+    float w4 = fmaf((float)((lo >> 16) & 0xFF), s, b);
+    float w5 = fmaf((float)((hi >> 16) & 0xFF), s, b);
+    float w6 = fmaf((float)(lo >> 24), s, b);
+    float w7 = fmaf((float)(hi >> 24), s, b);
+    u32x4 p = {pack_bf16x2(w0, w1), pack_bf16x2(w2, w3), pack_bf16x2(w4, w5), pack_bf16x2(w6, w7)};
+    return __builtin_bit_cast(bf16x8, p);
+}
+
+// Codes as bf16 "magic" pairs: bf16(128 + c) has bit pattern 0x4300 | c, exactly.
+// Pair j (j = 0..3) of a dword holds (c[j], c[j+4]) in (bits 0..15, bits 16..31).
+__device__ __forceinline__ uint32_t magic_pair(uint32_t d, int j) {
+    return ((d >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// Reorder 8 consecutive bf16 values x0..x7 (given as 4 dwords of natural pairs)
+// into the pairs (x[j], x[j+4]) that line up with magic_pair(d, j).
+__device__ __forceinline__ uint32_t interleave_pair(uint32_t a, uint32_t b, int hi) {
+    // hi = 0: (lo16(a), lo16(b)); hi = 1: (hi16(a), hi16(b))
+    return hi ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+}
+
+// fp32 dot of two bf16 pairs plus accumulator.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// --- wave reductions ----------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64);
+// every lane of a group receives the group's sum.
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// --- memory -------------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 load_u32x4(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+}  // namespace moe_w4

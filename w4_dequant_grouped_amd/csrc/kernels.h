@@ -1,0 +1,73 @@
+// Host-side launch interface between the C ABI (moe_w4.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe_w4 {
+
+constexpr int kSmallRouteMaxT = 8;   // largest T the one-launch router serves
+constexpr int kDecodeMaxT = 8;       // largest T the GEMV kernels are built for
+
+struct W4 {                  // E matrices [N][K], packed as in moe_w4.h
+    const uint8_t* codes;
+    const uint16_t* scales;
+    const uint16_t* biases;
+};
+
+struct W4Set {               // SwiGLU experts
+    W4 gate, up, down;
+};
+
+struct RouteArgs {
+    const uint16_t* x;
+    const float* Wr;
+    const float* br;
+    int T, H, E, k;
+    int32_t* ids;
+    float* w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    float* ws_logits;        // [T][E]
+    uint32_t* ws_ticket;     // control block (zero between calls)
+    uint32_t* ws_bitmask;    // [E][ceil(T/32)]
+};
+
+struct ForwardArgs {
+    const uint16_t* x;
+    int T, H, I, E, k;
+    W4Set routed;
+    W4Set shared;
+    int has_shared;
+    const float* topk_w;     // [T*k]
+    const int32_t* offsets;  // [E+1]
+    const int32_t* perm;     // [T*k]
+    uint16_t* out;           // [T][H] bf16
+    uint16_t* ws_h;          // [T*k + T][I] bf16: expert-sorted rows, then shared rows
+    float* ws_acc;           // [T][H] fp32 (grouped path)
+};
+
+// Optional per-kernel timing: events[2i] / events[2i+1] are recorded on the launch
+// stream before / after the i-th kernel of a call (while capacity allows).
+struct KernelTimer {
+    hipEvent_t* events = nullptr;
+    int capacity = 0;
+    int count = 0;
+    hipStream_t stream = nullptr;
+    void before() {
+        if (events && 2 * count + 1 < capacity) (void)hipEventRecord(events[2 * count], stream);
+    }
+    void after() {
+        if (events && 2 * count + 1 < capacity) (void)hipEventRecord(events[2 * count + 1], stream);
+        ++count;
+    }
+};
+
+hipError_t launch_route_small(const RouteArgs& a, hipStream_t st, KernelTimer& tm);
+hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& tm);
+hipError_t launch_forward_decode(const ForwardArgs& a, hipStream_t st, KernelTimer& tm);
+hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTimer& tm);
+
+}  // namespace moe_w4

@@ -1,0 +1,217 @@
+// C ABI of the W4 MoE block: argument checks, workspace layout, dispatch.
+// Declared and documented in include/moe_w4.h.
+#include "../../include/moe_w4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kAlign = 256;
+constexpr size_t kCtrlBytes = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t logits, bitmask, h, acc, total;
+};
+
+bool dims_ok(const moe_w4_dims* d, int* status) {
+    if (!d) { *status = MOE_W4_ERR_NULL; return false; }
+    if (d->flags != 0u) { *status = MOE_W4_ERR_FLAGS; return false; }
+    if (d->T < 0 || d->T > 65536 || d->E < 1 || d->E > 1024 || d->H < 256 || d->H > 16384 ||
+        d->I < 128 || d->I > 16384) {
+        *status = MOE_W4_ERR_DIMS;
+        return false;
+    }
+    if (d->group != 64 || d->H % 256 != 0 || d->I % 128 != 0) { *status = MOE_W4_ERR_GROUP; return false; }
+    if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->E) { *status = MOE_W4_ERR_TOPK; return false; }
+    *status = MOE_W4_OK;
+    return true;
+}
+
+Layout layout(const moe_w4_dims* d) {
+    Layout L;
+    const size_t T = (size_t)d->T, E = (size_t)d->E;
+    size_t off = kCtrlBytes;
+    L.logits = off;
+    off = align_up(off + T * E * sizeof(float));
+    L.bitmask = off;
+    off = align_up(off + E * ((T + 31) / 32) * sizeof(uint32_t));
+    L.h = off;
+    off = align_up(off + (T * (size_t)d->top_k + T) * (size_t)d->I * 2);
+    L.acc = off;
+    off = align_up(off + T * (size_t)d->H * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int launch_status(hipError_t err) {
+    if (err == hipSuccess) return MOE_W4_OK;
+    g_last_error = hipGetErrorString(err);
+    return MOE_W4_ERR_LAUNCH;
+}
+
+bool mat_ok(const moe_w4_mat& m, int* status) {
+    if (!m.codes || !m.scales || !m.biases) { *status = MOE_W4_ERR_NULL; return false; }
+    if (!aligned(m.codes, 16) || !aligned(m.scales, 2) || !aligned(m.biases, 2)) {
+        *status = MOE_W4_ERR_ALIGN;
+        return false;
+    }
+    return true;
+}
+
+moe_w4::W4 to_w4(const moe_w4_mat& m) { return moe_w4::W4{m.codes, m.scales, m.biases}; }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_w4_workspace_bytes(const moe_w4_dims* dims) {
+    int st;
+    if (!dims_ok(dims, &st)) return 0;
+    return layout(dims).total;
+}
+
+int moe_w4_route_timed(const moe_w4_dims* dims, const void* x, const float* router_w,
+                       const float* router_b, int32_t* topk_ids, float* topk_w,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                       void* workspace, size_t workspace_bytes, void* hip_stream, void** events,
+                       int capacity, int* n_kernels) {
+    if (n_kernels) *n_kernels = 0;
+    int st;
+    if (!dims_ok(dims, &st)) return st;
+    if (dims->T == 0) return MOE_W4_OK;
+    if (!x || !router_w || !topk_ids || !topk_w || !expert_counts || !expert_offsets || !perm ||
+        !workspace)
+        return MOE_W4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(workspace, kAlign) ||
+        !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_counts, 4) ||
+        !aligned(expert_offsets, 4) || !aligned(perm, 4) || (router_b && !aligned(router_b, 4)))
+        return MOE_W4_ERR_ALIGN;
+    const Layout L = layout(dims);
+    if (workspace_bytes < L.total) return MOE_W4_ERR_WORKSPACE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    moe_w4::RouteArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.Wr = router_w;
+    a.br = router_b;
+    a.T = dims->T;
+    a.H = dims->H;
+    a.E = dims->E;
+    a.k = dims->top_k;
+    a.ids = topk_ids;
+    a.w = topk_w;
+    a.counts = expert_counts;
+    a.offsets = expert_offsets;
+    a.perm = perm;
+    a.ws_ticket = reinterpret_cast<uint32_t*>(ws);
+    a.ws_logits = reinterpret_cast<float*>(ws + L.logits);
+    a.ws_bitmask = reinterpret_cast<uint32_t*>(ws + L.bitmask);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    moe_w4::KernelTimer tm;
+    tm.events = reinterpret_cast<hipEvent_t*>(events);
+    tm.capacity = events ? capacity : 0;
+    tm.stream = stream;
+    const hipError_t err = (a.T <= moe_w4::kSmallRouteMaxT) ? moe_w4::launch_route_small(a, stream, tm)
+                                                            : moe_w4::launch_route_large(a, stream, tm);
+    if (n_kernels) *n_kernels = tm.count;
+    return launch_status(err);
+}
+
+int moe_w4_route(const moe_w4_dims* dims, const void* x, const float* router_w,
+                 const float* router_b, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                 int32_t* expert_offsets, int32_t* perm, void* workspace, size_t workspace_bytes,
+                 void* hip_stream) {
+    return moe_w4_route_timed(dims, x, router_w, router_b, topk_ids, topk_w, expert_counts,
+                              expert_offsets, perm, workspace, workspace_bytes, hip_stream, nullptr,
+                              0, nullptr);
+}
+
+int moe_w4_forward_timed(const moe_w4_dims* dims, const void* x, const moe_w4_weights* routed,
+                         const moe_w4_weights* shared, const int32_t* topk_ids, const float* topk_w,
+                         const int32_t* expert_offsets, const int32_t* perm, void* out,
+                         void* workspace, size_t workspace_bytes, void* hip_stream, void** events,
+                         int capacity, int* n_kernels) {
+    (void)topk_ids;
+    if (n_kernels) *n_kernels = 0;
+    int st;
+    if (!dims_ok(dims, &st)) return st;
+    if (dims->T == 0) return MOE_W4_OK;
+    if (!x || !routed || !topk_w || !expert_offsets || !perm || !out || !workspace)
+        return MOE_W4_ERR_NULL;
+    st = MOE_W4_OK;
+    if (!mat_ok(routed->gate, &st) || !mat_ok(routed->up, &st) || !mat_ok(routed->down, &st))
+        return st;
+    if (shared && (!mat_ok(shared->gate, &st) || !mat_ok(shared->up, &st) || !mat_ok(shared->down, &st)))
+        return st;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, kAlign) || !aligned(topk_w, 4) ||
+        !aligned(expert_offsets, 4) || !aligned(perm, 4))
+        return MOE_W4_ERR_ALIGN;
+    const Layout L = layout(dims);
+    if (workspace_bytes < L.total) return MOE_W4_ERR_WORKSPACE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    moe_w4::ForwardArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.T = dims->T;
+    a.H = dims->H;
+    a.I = dims->I;
+    a.E = dims->E;
+    a.k = dims->top_k;
+    a.routed = moe_w4::W4Set{to_w4(routed->gate), to_w4(routed->up), to_w4(routed->down)};
+    a.has_shared = shared ? 1 : 0;
+    a.shared = shared ? moe_w4::W4Set{to_w4(shared->gate), to_w4(shared->up), to_w4(shared->down)}
+                      : a.routed;
+    a.topk_w = topk_w;
+    a.offsets = expert_offsets;
+    a.perm = perm;
+    a.out = static_cast<uint16_t*>(out);
+    a.ws_h = reinterpret_cast<uint16_t*>(ws + L.h);
+    a.ws_acc = reinterpret_cast<float*>(ws + L.acc);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    moe_w4::KernelTimer tm;
+    tm.events = reinterpret_cast<hipEvent_t*>(events);
+    tm.capacity = events ? capacity : 0;
+    tm.stream = stream;
+    const hipError_t err = (a.T <= MOE_W4_DECODE_MAX_T) ? moe_w4::launch_forward_decode(a, stream, tm)
+                                                         : moe_w4::launch_forward_grouped(a, stream, tm);
+    if (n_kernels) *n_kernels = tm.count;
+    return launch_status(err);
+}
+
+int moe_w4_forward(const moe_w4_dims* dims, const void* x, const moe_w4_weights* routed,
+                   const moe_w4_weights* shared, const int32_t* topk_ids, const float* topk_w,
+                   const int32_t* expert_offsets, const int32_t* perm, void* out, void* workspace,
+                   size_t workspace_bytes, void* hip_stream) {
+    return moe_w4_forward_timed(dims, x, routed, shared, topk_ids, topk_w, expert_offsets, perm, out,
+                                workspace, workspace_bytes, hip_stream, nullptr, 0, nullptr);
+}
+
+const char* moe_w4_status_string(int status) {
+    switch (status) {
+        case MOE_W4_OK: return "ok";
+        case MOE_W4_ERR_NULL: return "a required pointer is NULL";
+        case MOE_W4_ERR_DIMS: return "T, H, I or E outside the supported range";
+        case MOE_W4_ERR_TOPK: return "top_k must satisfy 1 <= top_k <= min(16, E)";
+        case MOE_W4_ERR_GROUP: return "group must be 64, H a multiple of 256 and I a multiple of 128";
+        case MOE_W4_ERR_ALIGN: return "a pointer is not aligned as required";
+        case MOE_W4_ERR_WORKSPACE: return "workspace smaller than moe_w4_workspace_bytes()";
+        case MOE_W4_ERR_LAUNCH: return "a HIP kernel launch failed";
+        case MOE_W4_ERR_FLAGS: return "unknown bits set in dims->flags";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_w4_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
