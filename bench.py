@@ -37,7 +37,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MoE-layer tokens/sec + %HBM roofline (T=1) and %MFMA peak (T=2048)"
 
 ROUTE_SMALL = ["route_small"]
-ROUTE_LARGE = ["router_logits", "router_topk", "router_perm"]
+ROUTE_LARGE = ["router_split", "router_logits", "router_topk", "router_group"]
 FWD_DECODE = ["decode_gateup", "decode_down"]
 FWD_GROUPED = ["grouped_gateup", "grouped_down", "finalize"]
 

@@ -56,6 +56,45 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t d, float s, float b) {
     return __builtin_bit_cast(bf16x8, p);
 }
 
+// (a & m) | c in one instruction.  gfx9 VOP3 may read one SGPR, so the constant
+// c is kept in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+    return r;
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Per (row, group) constants of the fp16-magic dequantisation below.
+struct DqConst {
+    float s0, b0;   // nibble in bits 0..3 of a half: value 1024 + c
+    float s1, b1;   // nibble in bits 4..7 of a half: value 1024 + 16 c
+};
+__device__ __forceinline__ DqConst make_dq(float s, float b) {
+    // b - 1024 s and b - 64 s are exact in fp32 for bf16 s and b of similar
+    // magnitude, so each weight below is c*s + b rounded once
+    return DqConst{s, fmaf(-1024.0f, s, b), s * 0.0625f, fmaf(-64.0f, s, b)};
+}
+
+// Dequantise 8 codes (one dword, natural k order) to bf16 w = c*s + b.
+// fp16(1024 + c) has bit pattern 0x6400 | c and fp16(1024 + 16c) is 0x6400 | (c << 4),
+// so one AND-OR per pair of codes builds exact fp16 operands and v_fma_mix_f32
+// applies the affine map in fp32 with a single rounding: 17 VALU ops per 8 weights.
+__device__ __forceinline__ bf16x8 dequant8_mix(uint32_t d, const DqConst& q, uint32_t magic) {
+    const uint32_t t = d >> 8;
+    const f16x2 h0 = __builtin_bit_cast(f16x2, and_or(d, 0x000F000Fu, magic));   // c0, c4
+    const f16x2 h1 = __builtin_bit_cast(f16x2, and_or(d, 0x00F000F0u, magic));   // c1, c5 (x16)
+    const f16x2 h2 = __builtin_bit_cast(f16x2, and_or(t, 0x000F000Fu, magic));   // c2, c6
+    const f16x2 h3 = __builtin_bit_cast(f16x2, and_or(t, 0x00F000F0u, magic));   // c3, c7 (x16)
+    const float w0 = fmaf((float)h0.x, q.s0, q.b0), w4 = fmaf((float)h0.y, q.s0, q.b0);
+    const float w1 = fmaf((float)h1.x, q.s1, q.b1), w5 = fmaf((float)h1.y, q.s1, q.b1);
+    const float w2 = fmaf((float)h2.x, q.s0, q.b0), w6 = fmaf((float)h2.y, q.s0, q.b0);
+    const float w3 = fmaf((float)h3.x, q.s1, q.b1), w7 = fmaf((float)h3.y, q.s1, q.b1);
+    u32x4 p = {pack_bf16x2(w0, w1), pack_bf16x2(w2, w3), pack_bf16x2(w4, w5), pack_bf16x2(w6, w7)};
+    return __builtin_bit_cast(bf16x8, p);
+}
+
 // Codes as bf16 "magic" pairs: bf16(128 + c) has bit pattern 0x4300 | c, exactly.
 // Pair j (j = 0..3) of a dword holds (c[j], c[j+4]) in (bits 0..15, bits 16..31).
 __device__ __forceinline__ uint32_t magic_pair(uint32_t d, int j) {

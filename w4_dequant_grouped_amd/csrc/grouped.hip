@@ -40,10 +40,9 @@ namespace moe_w4 {
 constexpr int kBM = 128;               // rows per M-tile
 constexpr int kMB = kBM / 16;          // 16-row MFMA blocks per M-tile
 constexpr int kKC = 128;               // K per chunk (4 MFMA steps of 32)
-constexpr int kARowBytes = kKC * 2;    // bf16 bytes of one A row per chunk
-constexpr int kAStride = kARowBytes + 16;   // padded LDS row stride
 constexpr int kMaxSeg = 1025;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;                // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;
 
 struct TileCtx {
     int seg;        // segment index (E = shared)
@@ -118,69 +117,259 @@ __device__ __forceinline__ void tile_coords(int i, int NT, int& mt, int& nt) {
     nt = (i >> 3) % NT;
 }
 
-// Stage one K chunk of A (kBM rows x kKC bf16) into LDS.  row_ptr(r) gives the
-// start of row r's chunk; rows >= rows are zero-filled.
-template <class RowPtr>
-__device__ __forceinline__ void stage_a(uint8_t* s_a, int rows, RowPtr row_ptr) {
-    const int tid = threadIdx.x;
-    const int r = tid >> 1;                // 2 threads per row, 128 bytes each
-    const int half = tid & 1;
-    u32x4 v[8];
-    if (r < rows) {
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(row_ptr(r)) + half * 128;
+// ---------------------------------------------------------------------------
+// The K-loop of one tile, software-pipelined:
+//   A (kBM rows x kKC bf16 per chunk) is copied global -> LDS by the direct
+//   global_load_lds_dwordx4 path (no registers), double buffered, one barrier
+//   per chunk.  Each lane supplies its own source address, so the rows are
+//   gathered by token on the fly and the 16-byte chunks of a row are stored
+//   XOR-swizzled by row, which keeps the MFMA operand reads conflict-free.
+//   B (codes, 128 bits per lane per 16-row block, plus the group's scale and
+//   bias) goes straight to registers and is dequantised there.  The next
+//   chunk's A and B are in flight while the current chunk's MFMAs run.
+// ---------------------------------------------------------------------------
+constexpr int kARow = kKC * 2;               // bytes of one A row per chunk (256)
+constexpr int kABuf = kBM * kARow;           // bytes of one A buffer (32 KiB)
+constexpr int kStages = 4;                   // K-loop pipeline depth
+constexpr int kRowsPerWaveDma = kBM / kWaves;   // A rows copied by each wavefront
+constexpr int kDmaPerWave = kRowsPerWaveDma / 4;  // 4 rows (1 KiB) per DMA instruction
+
+template <int NMAT, int NBW>
+struct BRegs {
+    u32x4 c[NMAT][NBW];
+    uint32_t s[NMAT][NBW];      // bf16 scale bits (combined only at use, so that
+    uint32_t b[NMAT][NBW];      // issuing the loads never waits for them)
+};
+
+// Per-lane B addressing: element offsets of the lane's row within its matrix set.
+template <int NMAT, int NBW>
+struct BAddr {
+    const uint8_t* codes[NMAT];      // matrix base (wave-uniform)
+    const uint16_t* scales[NMAT];
+    const uint16_t* biases[NMAT];
+    uint32_t row[NBW];               // row index (expert * N + n) of each 16-row block
+    int K;
+    int lane;
+};
+
+// Loads of chunk kc; a dummy chunk (past the end of K) loads the first bytes of
+// each matrix in every lane, one cache line per instruction, so that the number
+// of loads per chunk never varies.
+template <int NMAT, int NBW>
+__device__ __forceinline__ void load_b_chunk(BRegs<NMAT, NBW>& r, const BAddr<NMAT, NBW>& a, int kc,
+                                             bool dummy) {
+    const int kq = a.K / kGroup;
+    const int g = kc / kGroup + ((a.lane >> 4) >> 1);         // lanes 32..63 use the odd group
+    const int cb = (kc >> 1) + (a.lane >> 4) * 16;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = load_u32x4(src + 16 * q);
-    } else {
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
-    }
-    uint8_t* dst = s_a + r * kAStride + half * 128;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4*>(dst + 16 * q) = v[q];
+        for (int nb = 0; nb < NBW; ++nb) {
+            const size_t row = a.row[nb];
+            const size_t co = dummy ? 0 : row * (size_t)(a.K / 2) + cb;
+            const size_t so = dummy ? 0 : row * kq + g;
+            r.c[m][nb] = load_u32x4(a.codes[m] + co);
+            r.s[m][nb] = a.scales[m][so];
+            r.b[m][nb] = a.biases[m][so];
+        }
 }
 
-// One K chunk of MFMAs: NMAT matrices x NBW 16-column blocks per wavefront.
-template <int NMAT, int NBW>
-__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, int rows, int lane,
-                                          const u32x4 (&codes)[NMAT][NBW],
-                                          const float (&sc)[NMAT][NBW], const float (&bi)[NMAT][NBW],
-                                          f32x4 (&acc)[kMB][NMAT][NBW]) {
+// 16 bytes per lane, global -> LDS, written at lds + 16 * lane (lds is the same for
+// the whole wavefront).  Issued through inline assembly so that the compiler's
+// wait insertion does not see it: it would otherwise wait for every in-flight
+// copy at each barrier, which serialises the pipeline.  The K-loop waits for the
+// copies explicitly with vmcnt; M0 is restored after use.
+__device__ __forceinline__ void dma16_to_lds(const void* src, void* lds) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(l)
+        : "memory");
+}
+
+// A rows of a tile: row r starts at base + rowidx(r) * row_bytes, where rowidx is
+// the token (gathered rows) or the consecutive h row.
+struct ASrc {
+    const uint8_t* base;
+    size_t row_bytes;
+    int rowidx[kDmaPerWave];   // row index of the lane's row in each DMA instruction
+};
+
+// Issue the DMA of one A chunk: wavefront w copies rows [16w, 16w+16), four rows
+// (64 lanes x 16 bytes) per instruction.  Rows past the tile's valid rows re-read
+// its last valid row, so every address stays inside the operand.
+__device__ __forceinline__ void issue_a_dma(uint8_t* s_buf, int wave, int lane, const ASrc& a,
+                                            int kc_bytes, bool dummy) {
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+        const int r0 = wave * kRowsPerWaveDma + i * 4;
+        const int lrow = r0 + (lane >> 4);
+        const int logical = (lane & 15) ^ (lrow & 15);
+        const uint8_t* src = dummy ? a.base
+                                   : a.base + (size_t)a.rowidx[i] * a.row_bytes + kc_bytes + logical * 16;
+        dma16_to_lds(src, s_buf + r0 * kARow);
+    }
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// One K chunk of MFMAs over MB valid 16-row blocks (compile-time, so each step
+// is branch-free and the A-fragment reads of a step are issued together).
+template <int NMAT, int NBW, int MB>
+__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, int lane, const BRegs<NMAT, NBW>& br,
+                                          f32x4 (&acc)[MB][NMAT][NBW]) {
     const int arow = lane & 15;
-    const int acol = (lane >> 4) * 64;     // byte offset of the lane's 32 k values
+    const int agrp = (lane >> 4) * 4;      // logical 16-byte chunk of the lane's 32 k values
+    const uint32_t magic = 0x64006400u;
+    DqConst q[NMAT][NBW];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+            q[m][nb] = make_dq(bf16_to_f32(br.s[m][nb]), bf16_to_f32(br.b[m][nb]));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+        const int col = ((agrp + j) ^ arow) * 16;
+        bf16x8 a[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            a[mb] = *reinterpret_cast<const bf16x8*>(s_a + (mb * 16 + arow) * kARow + col);
         bf16x8 b[NMAT][NBW];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
-                const uint32_t d = (j == 0) ? codes[m][nb].x : (j == 1) ? codes[m][nb].y
-                                 : (j == 2) ? codes[m][nb].z : codes[m][nb].w;
-                b[m][nb] = dequant8(d, sc[m][nb], bi[m][nb]);
+                const uint32_t d = (j == 0) ? br.c[m][nb].x : (j == 1) ? br.c[m][nb].y
+                                 : (j == 2) ? br.c[m][nb].z : br.c[m][nb].w;
+                b[m][nb] = dequant8_mix(d, q[m][nb], magic);
             }
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-            if (mb * 16 >= rows) break;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                s_a + (mb * 16 + arow) * kAStride + acol + j * 16);
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb)
-                    acc[mb][m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[m][nb],
+                    acc[mb][m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[m][nb],
                                                                             acc[mb][m][nb], 0, 0, 0);
-        }
     }
 }
 
-// Load the lane's codes (128 bits) and group scale/bias for one K chunk.
-__device__ __forceinline__ void load_b(const W4& W, int e, int N, int K, int n, int kc, int lane,
-                                       u32x4& codes, float& s, float& b) {
-    const size_t row = (size_t)e * N + n;
-    codes = load_u32x4(W.codes + row * (K / 2) + (kc >> 1) + (lane >> 4) * 16);
-    const size_t gi = row * (K / kGroup) + ((kc + (lane >> 4) * 32) / kGroup);
-    s = bf16_to_f32(W.scales[gi]);
-    b = bf16_to_f32(W.biases[gi]);
+// Issue the loads of one K chunk: the A DMA first, then B to registers.  The
+// order matters for the vmcnt accounting in tile_kloop.
+template <int NMAT, int NBW>
+__device__ __forceinline__ void issue_chunk(BRegs<NMAT, NBW>& br, const BAddr<NMAT, NBW>& ba,
+                                            uint8_t* s_stage, int wave, int lane, const ASrc& src,
+                                            int kc, bool dummy) {
+    issue_a_dma(s_stage, wave, lane, src, 2 * kc, dummy);
+    load_b_chunk(br, ba, kc, dummy);
+}
+
+// Vector-memory instructions one issue_chunk emits per wavefront.
+template <int NMAT, int NBW>
+constexpr int kLoadsPerChunk = kDmaPerWave + 3 * NMAT * NBW;
+
+// K-loop with a D-stage ring: chunk c lives in LDS stage c % D and register set
+// c % D; chunks c+1 .. c+D-2 are in flight while chunk c is multiplied.  Every
+// iteration issues exactly one chunk (a dummy one past the end of K), so the
+// number of loads queued behind chunk c is always the same: its own B loads and
+// D-2 whole chunks.  Loads complete in order, so waiting until at most that many
+// are outstanding means chunk c has landed.
+template <int NMAT, int NBW, int D, int MB>
+__device__ __forceinline__ void tile_kloop(uint8_t* s_a, int K, int wave, int lane,
+                                           const ASrc& src, const BAddr<NMAT, NBW>& ba,
+                                           f32x4 (&acc)[MB][NMAT][NBW]) {
+    static_assert(D >= 2 && D <= 4, "pipeline depth");
+    constexpr int kBehind = 3 * NMAT * NBW + (D - 2) * kLoadsPerChunk<NMAT, NBW>;
+    static_assert(kBehind < 64, "pipeline too deep for vmcnt");
+    const int nch = K / kKC;
+    BRegs<NMAT, NBW> br[D];
+#pragma unroll
+    for (int st = 0; st < D - 1; ++st)
+        issue_chunk(br[st], ba, s_a + st * kABuf, wave, lane, src, st * kKC, st >= nch);
+    const int nit = (nch + D - 1) / D * D;
+    for (int base = 0; base < nit; base += D) {
+#pragma unroll
+        for (int st = 0; st < D; ++st) {
+            const int c = base + st;
+            wait_vmcnt<kBehind>();
+            __syncthreads();       // chunk c visible to all; chunk c-1's stage is free
+            const int nxt = (st + D - 1) % D;
+            issue_chunk(br[nxt], ba, s_a + nxt * kABuf, wave, lane, src, (c + D - 1) * kKC,
+                        c + D - 1 >= nch);
+            if (c < nch) mma_chunk<NMAT, NBW, MB>(s_a + st * kABuf, lane, br[st], acc);
+        }
+    }
+    wait_vmcnt<0>();               // drain the dummy loads
+    __syncthreads();               // all stages free for the next tile
+}
+
+// ---------------------------------------------------------------------------
+// Per-tile bodies, specialised on the number MB of valid 16-row blocks
+// ---------------------------------------------------------------------------
+template <int NBW, int MB>
+__device__ __forceinline__ void gateup_tile(uint8_t* s_a, int H, int I, int wave, int lane,
+                                            const ASrc& src, const BAddr<2, NBW>& ba, int rows,
+                                            int rowbase, int nbase, uint16_t* __restrict__ h) {
+    f32x4 acc[MB][2][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) acc[mb][m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tile_kloop<2, NBW, kStages, MB>(s_a, H, wave, lane, src, ba, acc);
+    // epilogue: h = silu(gate) * up, bf16, expert-sorted rows
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const int n = nbase + nb * 16 + (lane & 15);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = mb * 16 + (lane >> 4) * 4 + q;
+                if (m < rows) {
+                    const float g = acc[mb][0][nb][q], u = acc[mb][1][nb][q];
+                    h[(size_t)(rowbase + m) * I + n] = (uint16_t)f32_to_bf16(silu(g) * u);
+                }
+            }
+        }
+}
+
+template <int NBW, int MB>
+__device__ __forceinline__ void down_tile(uint8_t* s_a, int H, int I, int wave, int lane,
+                                          const ASrc& src, const BAddr<1, NBW>& ba, int rows,
+                                          int nbase, const int* s_tok, const float* s_w,
+                                          float* __restrict__ accum) {
+    f32x4 acc[MB][1][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) acc[mb][0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tile_kloop<1, NBW, kStages, MB>(s_a, I, wave, lane, src, ba, acc);
+    // epilogue: routing-weighted add into the token's fp32 accumulator row
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const int n = nbase + nb * 16 + (lane & 15);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = mb * 16 + (lane >> 4) * 4 + q;
+                if (m < rows) unsafeAtomicAdd(accum + (size_t)s_tok[m] * H + n, s_w[m] * acc[mb][0][nb][q]);
+            }
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -192,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
     W4Set routed, W4Set shared, int has_shared,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     uint16_t* __restrict__ h, float* __restrict__ acc_zero, long acc_elems) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_a[kBM * kAStride];
+    __shared__ __attribute__((aligned(16))) uint8_t s_a[kStages * kABuf];
     __shared__ int s_pre[kMaxSeg + 1];
     __shared__ int s_tmp[kThreads];
     __shared__ int s_tok[kBM];
@@ -204,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
 
     const int nseg = E + (has_shared ? 1 : 0);
     const int n_mt = build_mtile_prefix(offsets, E, T, k, has_shared, s_pre, s_tmp);
-    constexpr int BN = 4 * 16 * NBW;
+    constexpr int BN = kWaves * 16 * NBW;
     const int NT = I / BN;
     const int total = ((n_mt + 7) / 8) * 8 * NT;
     const int lane = threadIdx.x & (kWave - 1);
@@ -216,49 +405,36 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
         if (mt >= n_mt) continue;
         const TileCtx c = locate(mt, s_pre, nseg, E, T, k, offsets);
         const W4Set& Wset = c.shared ? shared : routed;
-        __syncthreads();
+        __syncthreads();                 // previous tile's readers are done
         for (int r = threadIdx.x; r < c.rows; r += kThreads)
             s_tok[r] = c.shared ? (c.m0 + r) : min(max(perm[c.hbase + c.m0 + r], 0), T * k - 1) / k;
+        __syncthreads();
         const int nbase = nt * BN + wave * 16 * NBW;
 
-        f32x4 acc[kMB][2][NBW];
+        BAddr<2, NBW> ba;
+        ba.codes[0] = Wset.gate.codes; ba.scales[0] = Wset.gate.scales; ba.biases[0] = Wset.gate.biases;
+        ba.codes[1] = Wset.up.codes;   ba.scales[1] = Wset.up.scales;   ba.biases[1] = Wset.up.biases;
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
+        for (int nb = 0; nb < NBW; ++nb) ba.row[nb] = (uint32_t)(c.e * I + nbase + nb * 16 + (lane & 15));
+        ba.K = H;
+        ba.lane = lane;
+        ASrc src;
+        src.base = reinterpret_cast<const uint8_t*>(x);
+        src.row_bytes = (size_t)H * 2;
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb) acc[mb][m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < kDmaPerWave; ++q)
+            src.rowidx[q] = s_tok[min(wave * kRowsPerWaveDma + q * 4 + (lane >> 4), c.rows - 1)];
 
-        for (int kc = 0; kc < H; kc += kKC) {
-            __syncthreads();               // previous chunk consumed; s_tok visible
-            stage_a(s_a, c.rows, [&](int r) { return x + (size_t)s_tok[r] * H + kc; });
-            u32x4 codes[2][NBW];
-            float sc[2][NBW], bi[2][NBW];
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int n = nbase + nb * 16 + (lane & 15);
-                load_b(Wset.gate, c.e, I, H, n, kc, lane, codes[0][nb], sc[0][nb], bi[0][nb]);
-                load_b(Wset.up, c.e, I, H, n, kc, lane, codes[1][nb], sc[1][nb], bi[1][nb]);
-            }
-            __syncthreads();
-            mma_chunk<2, NBW>(s_a, c.rows, lane, codes, sc, bi, acc);
-        }
-        // epilogue: h = silu(gate) * up
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-            if (mb * 16 >= c.rows) break;
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int n = nbase + nb * 16 + (lane & 15);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int m = mb * 16 + (lane >> 4) * 4 + q;
-                    if (m < c.rows) {
-                        const float g = acc[mb][0][nb][q], u = acc[mb][1][nb][q];
-                        h[(size_t)(c.hbase + c.m0 + m) * I + n] = (uint16_t)f32_to_bf16(silu(g) * u);
-                    }
-                }
-            }
+        const int rowbase = c.hbase + c.m0;
+        switch ((c.rows + 15) >> 4) {
+            case 1: gateup_tile<NBW, 1>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 2: gateup_tile<NBW, 2>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 3: gateup_tile<NBW, 3>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 4: gateup_tile<NBW, 4>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 5: gateup_tile<NBW, 5>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 6: gateup_tile<NBW, 6>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 7: gateup_tile<NBW, 7>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            default: gateup_tile<NBW, 8>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
         }
     }
 }
@@ -271,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
     int T, int H, int I, int E, int k, W4Set routed, W4Set shared, int has_shared,
     const float* __restrict__ topk_w, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const uint16_t* __restrict__ h, float* __restrict__ accum) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_a[kBM * kAStride];
+    __shared__ __attribute__((aligned(16))) uint8_t s_a[kStages * kABuf];
     __shared__ int s_pre[kMaxSeg + 1];
     __shared__ int s_tmp[kThreads];
     __shared__ int s_tok[kBM];
@@ -279,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
 
     const int nseg = E + (has_shared ? 1 : 0);
     const int n_mt = build_mtile_prefix(offsets, E, T, k, has_shared, s_pre, s_tmp);
-    constexpr int BN = 4 * 16 * NBW;
+    constexpr int BN = kWaves * 16 * NBW;
     const int NT = H / BN;
     const int total = ((n_mt + 7) / 8) * 8 * NT;
     const int lane = threadIdx.x & (kWave - 1);
@@ -301,40 +477,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
             }
         }
         const int nbase = nt * BN + wave * 16 * NBW;
-        const uint16_t* hrow0 = h + (size_t)(c.hbase + c.m0) * I;
+        BAddr<1, NBW> ba;
+        ba.codes[0] = Wset.down.codes; ba.scales[0] = Wset.down.scales; ba.biases[0] = Wset.down.biases;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) ba.row[nb] = (uint32_t)(c.e * H + nbase + nb * 16 + (lane & 15));
+        ba.K = I;
+        ba.lane = lane;
+        ASrc src;
+        src.base = reinterpret_cast<const uint8_t*>(h + (size_t)(c.hbase + c.m0) * I);
+        src.row_bytes = (size_t)I * 2;
+#pragma unroll
+        for (int q = 0; q < kDmaPerWave; ++q)
+            src.rowidx[q] = min(wave * kRowsPerWaveDma + q * 4 + (lane >> 4), c.rows - 1);
 
-        f32x4 acc[kMB][1][NBW];
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) acc[mb][0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        for (int kc = 0; kc < I; kc += kKC) {
-            __syncthreads();
-            stage_a(s_a, c.rows, [&](int r) { return hrow0 + (size_t)r * I + kc; });
-            u32x4 codes[1][NBW];
-            float sc[1][NBW], bi[1][NBW];
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int n = nbase + nb * 16 + (lane & 15);
-                load_b(Wset.down, c.e, H, I, n, kc, lane, codes[0][nb], sc[0][nb], bi[0][nb]);
-            }
-            __syncthreads();
-            mma_chunk<1, NBW>(s_a, c.rows, lane, codes, sc, bi, acc);
-        }
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-            if (mb * 16 >= c.rows) break;
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int n = nbase + nb * 16 + (lane & 15);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int m = mb * 16 + (lane >> 4) * 4 + q;
-                    if (m < c.rows)
-                        unsafeAtomicAdd(accum + (size_t)s_tok[m] * H + n, s_w[m] * acc[mb][0][nb][q]);
-                }
-            }
+        switch ((c.rows + 15) >> 4) {
+            case 1: down_tile<NBW, 1>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 2: down_tile<NBW, 2>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 3: down_tile<NBW, 3>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 4: down_tile<NBW, 4>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 5: down_tile<NBW, 5>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 6: down_tile<NBW, 6>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 7: down_tile<NBW, 7>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            default: down_tile<NBW, 8>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
         }
     }
 }
@@ -364,13 +528,13 @@ static int cu_count() {
 }
 
 hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTimer& tm) {
-    constexpr int NBW_GU = 2, NBW_DN = 2;
+    constexpr int NBW_GU = 1, NBW_DN = 2;
     const int nseg = a.E + (a.has_shared ? 1 : 0);
     // upper bound of M-tiles: every routed row tile-padded, plus one partial per segment
     const long mt_bound = ((long)a.T * a.k) / kBM + nseg + (a.has_shared ? a.T / kBM + 1 : 0);
-    const int slots = cu_count() * 2;
-    const long gu_tiles = mt_bound * (a.I / (64 * NBW_GU)) + 8;
-    const long dn_tiles = mt_bound * (a.H / (64 * NBW_DN)) + 8;
+    const int slots = cu_count();          // one 8-wave workgroup per CU
+    const long gu_tiles = mt_bound * (a.I / (kWaves * 16 * NBW_GU)) + 8;
+    const long dn_tiles = mt_bound * (a.H / (kWaves * 16 * NBW_DN)) + 8;
     const int g_gu = (int)(((gu_tiles < slots ? gu_tiles : slots) + 7) / 8 * 8);
     const int g_dn = (int)(((dn_tiles < slots ? dn_tiles : slots) + 7) / 8 * 8);
     const long acc_elems = (long)a.T * a.H;

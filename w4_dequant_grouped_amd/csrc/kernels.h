@@ -32,7 +32,7 @@ struct RouteArgs {
     int32_t* perm;
     float* ws_logits;        // [T][E]
     uint32_t* ws_ticket;     // control block (zero between calls)
-    uint32_t* ws_bitmask;    // [E][ceil(T/32)]
+    uint16_t* ws_planes;     // [3][E][H] bf16 split of the router weight (large T)
 };
 
 struct ForwardArgs {

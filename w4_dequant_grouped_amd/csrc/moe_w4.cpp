@@ -19,7 +19,7 @@ constexpr size_t kCtrlBytes = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t logits, bitmask, h, acc, total;
+    size_t logits, planes, h, acc, total;
 };
 
 bool dims_ok(const moe_w4_dims* d, int* status) {
@@ -40,10 +40,10 @@ Layout layout(const moe_w4_dims* d) {
     Layout L;
     const size_t T = (size_t)d->T, E = (size_t)d->E;
     size_t off = kCtrlBytes;
-    L.logits = off;
-    off = align_up(off + T * E * sizeof(float));
-    L.bitmask = off;
-    off = align_up(off + E * ((T + 31) / 32) * sizeof(uint32_t));
+    L.logits = off;   // small T: [T][E] logits; large T: 4 K-split partial planes
+    off = align_up(off + T * E * sizeof(float) * (d->T > moe_w4::kSmallRouteMaxT ? 4 : 1));
+    L.planes = off;
+    if (d->T > moe_w4::kSmallRouteMaxT) off = align_up(off + 3 * E * (size_t)d->H * 2);
     L.h = off;
     off = align_up(off + (T * (size_t)d->top_k + T) * (size_t)d->I * 2);
     L.acc = off;
@@ -116,7 +116,7 @@ int moe_w4_route_timed(const moe_w4_dims* dims, const void* x, const float* rout
     a.perm = perm;
     a.ws_ticket = reinterpret_cast<uint32_t*>(ws);
     a.ws_logits = reinterpret_cast<float*>(ws + L.logits);
-    a.ws_bitmask = reinterpret_cast<uint32_t*>(ws + L.bitmask);
+    a.ws_planes = reinterpret_cast<uint16_t*>(ws + L.planes);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     moe_w4::KernelTimer tm;
     tm.events = reinterpret_cast<hipEvent_t*>(events);

@@ -11,9 +11,10 @@
 //    grid streams a slice of the router weight (reading W_r is a large share of
 //    a decode step's bytes, so it is spread over many CUs); the last workgroup to
 //    finish (ticket counter in the workspace control block) selects and groups.
-//  * large T (prefill): logits tile kernel -> per-token top-k kernel (wavefront
-//    per token, atomic histogram and token bitmask) -> per-expert kernel that
-//    derives its offset and writes its permutation segment in token order.
+//  * large T (prefill): exact three-way bf16 split of W_r -> logits on bf16
+//    MFMA -> per-token top-k (wavefront per token) -> per-expert kernel that
+//    derives its own offset and writes its permutation segment in token order
+//    (no atomics, no histogram shared between workgroups).
 #include "device.h"
 #include "kernels.h"
 
@@ -228,83 +229,102 @@ __global__ __launch_bounds__(kSmallRouteThreads) void k_route_small(
 // ---------------------------------------------------------------------------
 // large-T router
 // ---------------------------------------------------------------------------
-constexpr int kLogTileT = 64;
-constexpr int kLogTileE = 64;
-constexpr int kLogTileK = 32;
+// x is bf16, so x . w for fp32 w equals x . hi + x . mid + x . lo exactly when
+// w = hi + mid + lo with hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid)
+// (24 significand bits = 3 x 8; each product of two bf16 is exact in fp32).  The
+// logits then run on bf16 MFMA with fp32 accumulation.
 
-// logits[t][e] for a 64x64 tile, fp32 FMA; also clears the histogram and bitmask.
-__global__ __launch_bounds__(256) void k_router_logits(
-    const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ br,
-    int T, int H, int E, float* __restrict__ logits,
-    int32_t* __restrict__ counts, uint32_t* __restrict__ bitmask, int bitmask_words) {
-    __shared__ float xs[kLogTileT][kLogTileK + 1];
-    __shared__ float ws[kLogTileE][kLogTileK + 1];
-    const int tid = threadIdx.x;
-    const int t0 = blockIdx.y * kLogTileT;
-    const int e0 = blockIdx.x * kLogTileE;
-
-    // clearing of the histogram state used by the next kernel
-    {
-        const int nblk = gridDim.x * gridDim.y;
-        const int b = blockIdx.y * gridDim.x + blockIdx.x;
-        for (int i = b * 256 + tid; i < bitmask_words; i += nblk * 256) bitmask[i] = 0u;
-        for (int i = b * 256 + tid; i < E; i += nblk * 256) counts[i] = 0;
-    }
-
-    const int tx = tid & 15, ty = tid >> 4;
-    float acc[4][4] = {};
-    const int lr = tid >> 2, lk = (tid & 3) * 8;
-    for (int kb = 0; kb < H; kb += kLogTileK) {
-        {   // stage x (bf16 -> fp32) and W_r
-            const int t = t0 + lr;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (t < T) v = load_u32x4(x + (size_t)t * H + kb + lk);
-            xs[lr][lk + 0] = bf16lo(v.x); xs[lr][lk + 1] = bf16hi(v.x);
-            xs[lr][lk + 2] = bf16lo(v.y); xs[lr][lk + 3] = bf16hi(v.y);
-            xs[lr][lk + 4] = bf16lo(v.z); xs[lr][lk + 5] = bf16hi(v.z);
-            xs[lr][lk + 6] = bf16lo(v.w); xs[lr][lk + 7] = bf16hi(v.w);
-            const int e = e0 + lr;
-            float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-            if (e < E) {
-                a = *reinterpret_cast<const float4*>(Wr + (size_t)e * H + kb + lk);
-                b = *reinterpret_cast<const float4*>(Wr + (size_t)e * H + kb + lk + 4);
-            }
-            ws[lr][lk + 0] = a.x; ws[lr][lk + 1] = a.y; ws[lr][lk + 2] = a.z; ws[lr][lk + 3] = a.w;
-            ws[lr][lk + 4] = b.x; ws[lr][lk + 5] = b.y; ws[lr][lk + 6] = b.z; ws[lr][lk + 7] = b.w;
+// W_r [E][H] fp32 -> three bf16 planes [3][E][H].
+__global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ Wr, long n,
+                                                      uint16_t* __restrict__ planes) {
+    for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (long)gridDim.x * 256 * 4) {
+        const float4 w = *reinterpret_cast<const float4*>(Wr + i);
+        const float v[4] = {w.x, w.y, w.z, w.w};
+        uint32_t hi[2], mid[2], lo[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float h0 = bf16_to_f32(f32_to_bf16(v[2 * q])), h1 = bf16_to_f32(f32_to_bf16(v[2 * q + 1]));
+            float r0 = v[2 * q] - h0, r1 = v[2 * q + 1] - h1;
+            float m0 = bf16_to_f32(f32_to_bf16(r0)), m1 = bf16_to_f32(f32_to_bf16(r1));
+            hi[q] = pack_bf16x2(h0, h1);
+            mid[q] = pack_bf16x2(m0, m1);
+            lo[q] = pack_bf16x2(r0 - m0, r1 - m1);
         }
-        __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < kLogTileK; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[ty * 4 + i][kk];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ws[tx * 4 + j][kk];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
+        *reinterpret_cast<u32x2*>(planes + i) = u32x2{hi[0], hi[1]};
+        *reinterpret_cast<u32x2*>(planes + n + i) = u32x2{mid[0], mid[1]};
+        *reinterpret_cast<u32x2*>(planes + 2 * n + i) = u32x2{lo[0], lo[1]};
     }
+}
+
+// Partial logits over one quarter of H for a tile of 64 tokens x 64 experts:
+// wavefront w owns tokens 16w..16w+15 and all 64 experts (four 16-expert blocks,
+// three planes each).  MFMA 16x16x32 bf16 operands come straight from global
+// memory: lane l holds row (token or expert) l%16 and the 8 consecutive k at
+// 8*(l/16) of each 32-k step.  The K split gives four times the wavefronts;
+// the top-k kernel adds the partials in a fixed order.
+constexpr int kLgTok = 64;
+constexpr int kLgExp = 64;
+constexpr int kLgSplit = 4;      // K split (partial logit planes)
+constexpr int kLgUnroll = 2;     // K steps whose loads are issued together (H/kLgSplit % 64 == 0)
+
+__global__ __launch_bounds__(256) void k_router_logits_mfma(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes, int T, int H, int E,
+    float* __restrict__ partial) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int t0 = blockIdx.y * kLgTok + wave * 16;
+    const int e0 = blockIdx.x * kLgExp;
+    const int ks = H / kLgSplit;
+    const int kbeg = blockIdx.z * ks;
+    const size_t plane = (size_t)E * H;
+    const int trow = min(t0 + (lane & 15), T - 1);           // rows past T re-read row T-1
+    const uint16_t* xa = x + (size_t)trow * H + kbeg + (lane >> 4) * 8;
+    const uint16_t* wb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + ty * 4 + i;
-        if (t >= T) continue;
+    for (int nb = 0; nb < 4; ++nb)
+        wb[nb] = planes + (size_t)min(e0 + nb * 16 + (lane & 15), E - 1) * H + kbeg + (lane >> 4) * 8;
+    f32x4 acc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = e0 + tx * 4 + j;
-            if (e < E) logits[(size_t)t * E + e] = acc[i][j] + (br ? br[e] : 0.f);
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kc = 0; kc < ks; kc += 32 * kLgUnroll) {
+        bf16x8 a[kLgUnroll], b[kLgUnroll][4][3];
+#pragma unroll
+        for (int u = 0; u < kLgUnroll; ++u) {
+            a[u] = *reinterpret_cast<const bf16x8*>(xa + kc + 32 * u);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    b[u][nb][p] = *reinterpret_cast<const bf16x8*>(wb[nb] + p * plane + kc + 32 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < kLgUnroll; ++u)
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][nb][p], acc[nb], 0, 0, 0);
+    }
+    float* out = partial + (size_t)blockIdx.z * T * E;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        const int e = e0 + nb * 16 + (lane & 15);
+        if (e >= E) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = t0 + (lane >> 4) * 4 + q;
+            if (t < T) out[(size_t)t * E + e] = acc[nb][q];
         }
     }
 }
 
-// One wavefront per token: top-k, weights, histogram, token bitmask per expert.
+// One wavefront per token: logits = bias + the K-split partials (fixed order),
+// then top-k and renormalised weights (no shared state).
 template <int EPL>
-__global__ __launch_bounds__(256) void k_router_topk(
-    const float* __restrict__ logits, int T, int E, int k,
-    int32_t* __restrict__ ids, float* __restrict__ tw, int32_t* __restrict__ counts,
-    uint32_t* __restrict__ bitmask, int words_per_expert) {
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ partial,
+                                                     const float* __restrict__ br, int T, int E,
+                                                     int k, int32_t* __restrict__ ids,
+                                                     float* __restrict__ tw) {
     const int lane = threadIdx.x & (kWave - 1);
     const int t = blockIdx.x * 4 + (threadIdx.x / kWave);
     if (t >= T) return;
@@ -312,64 +332,80 @@ __global__ __launch_bounds__(256) void k_router_topk(
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
         const int e = lane + kWave * j;
-        vals[j] = (e < E) ? logits[(size_t)t * E + e] : -INFINITY;
+        float v = -INFINITY;
+        if (e < E) {
+            float p[kLgSplit];
+#pragma unroll
+            for (int q = 0; q < kLgSplit; ++q) p[q] = partial[((size_t)q * T + t) * E + e];
+            v = (p[0] + p[1]) + (p[2] + p[3]);
+            if (br) v += br[e];
+        }
+        vals[j] = v;
     }
-    const int e = wave_topk<EPL>(vals, E, k, lane, ids + (size_t)t * k, tw + (size_t)t * k, nullptr);
-    if (lane < k) {
-        atomicAdd(&counts[e], 1);
-        atomicOr(&bitmask[(size_t)e * words_per_expert + (t >> 5)], 1u << (t & 31));
-    }
+    wave_topk<EPL>(vals, E, k, lane, ids + (size_t)t * k, tw + (size_t)t * k, nullptr);
 }
 
-// One workgroup per expert: offset from the histogram, permutation segment in token order.
-__global__ __launch_bounds__(256) void k_router_perm(
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
-    const uint32_t* __restrict__ bitmask, int T, int E, int k, int words_per_expert,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
-    __shared__ int s_red[256];
-    __shared__ int s_scan[256];
+// One workgroup per expert e.  Every token's ids are ascending, so
+//   offsets[e] = sum over tokens of #{j : ids[t][j] < e}
+// and the expert's segment lists, in token order, the tokens whose ids contain
+// e.  Each workgroup reads all ids (T*k ints, L2-resident) and needs nothing
+// from the others: no histogram, no atomics.
+__global__ __launch_bounds__(256) void k_router_group(const int32_t* __restrict__ ids, int T, int E,
+                                                      int k, int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm) {
+    __shared__ int s_below[256];
+    __shared__ int s_hits[256];
     const int e = blockIdx.x;
     const int tid = threadIdx.x;
-    int part = 0;
-    for (int i = tid; i < e; i += 256) part += counts[i];
-    s_red[tid] = part;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) s_red[tid] += s_red[tid + s];
-        __syncthreads();
-    }
-    const int base = s_red[0];
-    if (tid == 0) {
-        offsets[e] = base;
-        if (e == E - 1) offsets[E] = T * k;
-    }
-    // contiguous word range per thread, exclusive scan of popcounts
-    const int W = words_per_expert;
-    const int per = (W + 255) / 256;
-    const int w0 = min(tid * per, W), w1 = min(w0 + per, W);
-    const uint32_t* row = bitmask + (size_t)e * W;
-    int c = 0;
-    for (int w = w0; w < w1; ++w) c += __popc(row[w]);
-    s_scan[tid] = c;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        const int v = (tid >= o) ? s_scan[tid - o] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    int pos = base + s_scan[tid] - c;
-    for (int w = w0; w < w1; ++w) {
-        uint32_t bits = row[w];
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1;
-            const int t = w * 32 + b;
-            int slot = 0;
-            for (int j = 0; j < k; ++j) slot = (ids[(size_t)t * k + j] == e) ? j : slot;
-            perm[pos++] = t * k + slot;
+    // contiguous run of the flattened (t, j) entries per thread, 4 at a time
+    const int n = T * k;
+    const int n4 = (n + 3) / 4;
+    const int per4 = (n4 + 255) / 256;
+    const int q0 = min(tid * per4, n4), q1 = min(q0 + per4, n4);
+    int below = 0, hits = 0;
+    for (int q = q0; q < q1; ++q) {
+        const int i = 4 * q;
+        int v[4];
+        if (i + 3 < n) {
+            const int4 w = *reinterpret_cast<const int4*>(ids + i);
+            v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = (i + u < n) ? ids[i + u] : 0x7FFFFFFF;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            below += (v[u] < e) ? 1 : 0;
+            hits += (v[u] == e) ? 1 : 0;
         }
     }
+    s_below[tid] = below;
+    s_hits[tid] = hits;
+    __syncthreads();
+    // inclusive scan of hits; sum of below
+    for (int o = 1; o < 256; o <<= 1) {
+        const int vh = (tid >= o) ? s_hits[tid - o] : 0;
+        const int vb = (tid >= o) ? s_below[tid - o] : 0;
+        __syncthreads();
+        s_hits[tid] += vh;
+        s_below[tid] += vb;
+        __syncthreads();
+    }
+    const int base = s_below[255];
+    int pos = base + s_hits[tid] - hits;
+    if (tid == 255) {
+        offsets[e] = base;
+        counts[e] = s_hits[255];
+        if (e == E - 1) offsets[E] = n;
+    }
+    if (hits == 0) return;
+    for (int q = q0; q < q1; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = 4 * q + u;
+            if (i < n && ids[i] == e) perm[pos++] = i;
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -397,30 +433,36 @@ hipError_t launch_route_small(const RouteArgs& a, hipStream_t st, KernelTimer& t
 }
 
 hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& tm) {
-    const int wpe = (a.T + 31) / 32;
-    dim3 g1((a.E + kLogTileE - 1) / kLogTileE, (a.T + kLogTileT - 1) / kLogTileT);
+    const long n = (long)a.E * a.H;
     tm.before();
-    hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, st, a.x, a.Wr, a.br, a.T, a.H, a.E,
-                       a.ws_logits, a.counts, a.ws_bitmask, wpe * a.E);
+    hipLaunchKernelGGL(k_router_split, dim3((unsigned)min((n / 4 + 255) / 256, 1024L)), dim3(256), 0, st,
+                       a.Wr, n, a.ws_planes);
     tm.after();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    if (a.E <= 256)
-        hipLaunchKernelGGL(k_router_topk<4>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits,
-                           a.T, a.E, a.k, a.ids, a.w, a.counts, a.ws_bitmask, wpe);
-    else if (a.E <= 512)
-        hipLaunchKernelGGL(k_router_topk<8>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits,
-                           a.T, a.E, a.k, a.ids, a.w, a.counts, a.ws_bitmask, wpe);
-    else
-        hipLaunchKernelGGL(k_router_topk<16>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits,
-                           a.T, a.E, a.k, a.ids, a.w, a.counts, a.ws_bitmask, wpe);
+    hipLaunchKernelGGL(k_router_logits_mfma,
+                       dim3((a.E + kLgExp - 1) / kLgExp, (a.T + kLgTok - 1) / kLgTok, kLgSplit),
+                       dim3(256), 0, st, a.x, a.ws_planes, a.T, a.H, a.E, a.ws_logits);
     tm.after();
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL(k_router_perm, dim3(a.E), dim3(256), 0, st, a.ids, a.counts, a.ws_bitmask,
-                       a.T, a.E, a.k, wpe, a.offsets, a.perm);
+    if (a.E <= 256)
+        hipLaunchKernelGGL(k_router_topk<4>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
+                           a.T, a.E, a.k, a.ids, a.w);
+    else if (a.E <= 512)
+        hipLaunchKernelGGL(k_router_topk<8>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
+                           a.T, a.E, a.k, a.ids, a.w);
+    else
+        hipLaunchKernelGGL(k_router_topk<16>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
+                           a.T, a.E, a.k, a.ids, a.w);
+    tm.after();
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    tm.before();
+    hipLaunchKernelGGL(k_router_group, dim3(a.E), dim3(256), 0, st, a.ids, a.T, a.E, a.k, a.counts,
+                       a.offsets, a.perm);
     tm.after();
     return hipGetLastError();
 }
