@@ -124,30 +124,35 @@ def time_steps(step_fn, steps, warmup):
     return time.perf_counter() - t0
 
 
-def kernel_times(blocks, xs, steps, ev: HipEvents, route_names, fwd_names):
-    """Average duration per kernel name over `steps` passes over all blocks."""
+def kernel_times(blocks, xs, steps, ev: HipEvents, names, timed):
+    """Average duration per kernel name over `steps` passes over all blocks.
+
+    ``timed(block, x, events)`` runs one block call recording an event pair
+    around each kernel and returns the kernel count."""
     import torch
-    nr, nf = len(route_names), len(fwd_names)
-    per_call = []
+    n = len(names)
     events = []
     for s in range(steps):
         for l, blk in enumerate(blocks):
-            re_ = ev.create(2 * nr)
-            fe_ = ev.create(2 * nf)
-            kr, kf = blk.timed(xs[s % len(xs)][l], re_, fe_)
-            assert kr == nr and kf == nf, (kr, kf)
-            events.append((re_, fe_))
+            e = ev.create(2 * n)
+            got = timed(blk, xs[s % len(xs)][l], e)
+            assert got == n, (got, names)
+            events.append(e)
     torch.cuda.synchronize()
-    sums = {n: 0.0 for n in route_names + fwd_names}
-    for re_, fe_ in events:
-        for i, n in enumerate(route_names):
-            sums[n] += ev.elapsed_ms(re_[2 * i], re_[2 * i + 1])
-        for i, n in enumerate(fwd_names):
-            sums[n] += ev.elapsed_ms(fe_[2 * i], fe_[2 * i + 1])
-        ev.destroy(re_)
-        ev.destroy(fe_)
-    ncalls = len(events)
-    return {n: 1e3 * v / ncalls for n, v in sums.items()}   # microseconds per launch
+    sums = {name: 0.0 for name in names}
+    for e in events:
+        for i, name in enumerate(names):
+            sums[name] += ev.elapsed_ms(e[2 * i], e[2 * i + 1])
+        ev.destroy(e)
+    return {name: 1e3 * v / len(events) for name, v in sums.items()}   # microseconds per launch
+
+
+def split_timed(nr):
+    """Timing callback of route + forward as two calls (first nr event pairs: route)."""
+    def timed(blk, x, e):
+        kr, kf = blk.timed(x, e[:2 * nr], e[2 * nr:])
+        return kr + kf
+    return timed
 
 
 def run_decode(args, ev):
@@ -174,21 +179,24 @@ def run_decode(args, ev):
     ms_per_step = 1e3 * elapsed / args.steps
     value = L * T * args.steps / elapsed
 
-    kt = kernel_times(blocks, xs, min(args.steps, 10), ev, ROUTE_SMALL, FWD_DECODE)
+    names = ROUTE_SMALL + FWD_DECODE
+    kt = kernel_times(blocks, xs, min(args.steps, 10), ev, names,
+                      lambda blk, x, e: blk.block_timed(x, e))
     # algorithmic bytes per launch from the routing each layer produced
     gu_b, dn_b = expert_bytes(H, I)
     active = []
     for blk in blocks:
         active.append(int((blk.routing.counts > 0).sum().item()))
     n_act = sum(active) / len(active)
+    routing_bytes = T * k * 8 + (2 * E + 1 + T * k) * 4
+    layer_bytes = E * H * 4 + (n_act + 1) * (2 * gu_b + dn_b) + 2 * T * H * 2 + routing_bytes
     alg = {
-        "route_small": E * H * 4 + T * H * 2 + T * k * 8 + (2 * E + 1 + T * k) * 4,
+        "route_small": E * H * 4 + T * H * 2 + routing_bytes,
         "decode_gateup": (n_act + 1) * 2 * gu_b + T * H * 2 + (T * k + T) * I * 2,
         "decode_down": (n_act + 1) * dn_b + (T * k + T) * I * 2 + T * H * 2,
     }
-    dom = max(FWD_DECODE + ROUTE_SMALL, key=lambda n: kt[n])
+    dom = max(names, key=lambda n: kt[n])
     achieved = alg[dom] / (kt[dom] * 1e-6) / 1e9
-    layer_bytes = E * H * 4 + (n_act + 1) * (2 * gu_b + dn_b) + 2 * T * H * 2
     roofline = {
         "bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -224,7 +232,7 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
 
     elapsed = time_steps(step, steps, warmup)
     per_call_ms = 1e3 * elapsed / (steps * L)
-    kt = kernel_times(blocks, xs, steps, ev, ROUTE_LARGE, FWD_GROUPED)
+    kt = kernel_times(blocks, xs, steps, ev, ROUTE_LARGE + FWD_GROUPED, split_timed(len(ROUTE_LARGE)))
     rows = T * k + T
     flops = {"grouped_gateup": 2.0 * rows * H * 2 * I, "grouped_down": 2.0 * rows * I * H}
     dom = max(flops, key=lambda n: kt[n])
@@ -238,7 +246,7 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profiles(dom, "prefill2048"),
+                     "traffic": traffic_from_profiles(dom, "prefill"),
                      "alg_flops_per_launch": flops[dom], "avg_launch_us": round(kt[dom], 3),
                      "kernel_us": {n: round(v, 3) for n, v in kt.items()}},
     }
@@ -279,6 +287,9 @@ def main():
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy (fp32 negate) of MIB MiB three times: the "
+                         "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -291,6 +302,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        n = args.copy_probe << 18                      # fp32 elements in MIB MiB
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                          "launches": 3}), flush=True)
+        return
     B.load_library()          # raises if the HIP library is missing: there is no fallback
     ev = HipEvents()
 

@@ -151,7 +151,21 @@ int moe_w4_forward(const moe_w4_dims* dims, const void* x,
                    void* out, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * The same two calls with per-kernel timing.  When `events` is not NULL it holds
+ * moe_w4_route() followed by moe_w4_forward() in one call, with the same
+ * arguments, outputs and errors as the pair: every argument is validated before
+ * anything is enqueued, and both stages are enqueued on `hip_stream` in order.
+ * The routing outputs are written as by moe_w4_route() (callers that do not
+ * need them still pass the buffers: the forward stage reads them).
+ */
+int moe_w4_block(const moe_w4_dims* dims, const void* x,
+                 const float* router_w, const float* router_b,
+                 const moe_w4_weights* routed, const moe_w4_weights* shared,
+                 int32_t* topk_ids, float* topk_w,
+                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                 void* out, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * The same calls with per-kernel timing.  When `events` is not NULL it holds
  * `capacity` hipEvent_t handles created by the caller; the call records
  * events[2i] on `hip_stream` just before, and events[2i+1] just after, the i-th
  * kernel it launches (while 2i+1 < capacity).  *n_kernels (if not NULL) receives
@@ -171,6 +185,14 @@ int moe_w4_forward_timed(const moe_w4_dims* dims, const void* x,
                          const int32_t* expert_offsets, const int32_t* perm,
                          void* out, void* workspace, size_t workspace_bytes, void* hip_stream,
                          void** events, int capacity, int* n_kernels);
+
+int moe_w4_block_timed(const moe_w4_dims* dims, const void* x,
+                       const float* router_w, const float* router_b,
+                       const moe_w4_weights* routed, const moe_w4_weights* shared,
+                       int32_t* topk_ids, float* topk_w,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                       void* out, void* workspace, size_t workspace_bytes, void* hip_stream,
+                       void** events, int capacity, int* n_kernels);
 
 /* Static description of a status code. */
 const char* moe_w4_status_string(int status);

@@ -1,5 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
+Block calls go through moe_w4_block (route + forward in one library call); the
+split tests call moe_w4_route and moe_w4_forward separately.
+
 Routing ids, counts, offsets and the permutation are compared bit for bit on
 inputs whose k-th/(k+1)-th logit gap is at least 1e-3; routing weights within
 1e-5; block outputs within max|gpu - ref| / max|ref| <= 1e-2.
@@ -58,17 +61,17 @@ def test_one_expert_takes_every_token():
     full_check(shape, 62, layer=layer, what="one hot expert")
 
 
-@pytest.mark.parametrize("T", [1, 40])
+@pytest.mark.parametrize("T", [1, 2, 40])
 def test_all_experts_selected(T):
     full_check(S(T=T, H=256, I=128, E=8, top_k=8), 63 + T, what=f"k=E T={T}")
 
 
-@pytest.mark.parametrize("T", [1, 20])
+@pytest.mark.parametrize("T", [1, 2, 20])
 def test_top1_no_shared(T):
     full_check(S(T=T, H=256, I=128, E=16, top_k=1, shared=False), 65 + T, what=f"top1 T={T}")
 
 
-@pytest.mark.parametrize("T", [4, 64])
+@pytest.mark.parametrize("T", [2, 4, 64])
 def test_top16(T):
     full_check(S(T=T, H=256, I=128, E=64, top_k=16), 67 + T, what=f"top16 T={T}")
 
@@ -83,7 +86,16 @@ def test_zero_tokens_is_a_no_op():
     B.moe_w4_route(dims, x, layer.router_w, None, r, ws)
     out = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     B.moe_w4_forward(dims, x, layer.routed, layer.shared, r, out, ws)
+    B.moe_w4_block(dims, x, layer.router_w, None, B.weights_struct(layer.routed),
+                   B.weights_struct(layer.shared), r, out, ws)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_decode_router_bias_small_h(T):
+    # H=256: only 8 of 64 lanes hold gate/up codes; Zipf router bias
+    full_check(S(T=T, H=256, I=256, E=64, top_k=8, router_bias="zipf"), 72 + T,
+               what=f"bias H=256 T={T}")
 
 
 # --- full-size configurations ---------------------------------------------------------
@@ -171,3 +183,43 @@ def test_token_permutation_invariance_gpu():
     assert torch.equal(r2.counts, c1)
     ref = o1.float()[p.cuda()]
     assert (o2.float() - ref).abs().max().item() <= 1e-2 * ref.abs().max().item()
+
+
+# --- the single-call entry point against the two separate calls ---------------------
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_split_entry_points_full_size(full_layer, T):
+    shape = S(T=T, H=2048, I=512, E=256, top_k=8)
+    full_check(shape, 110 + T, layer=full_layer, what=f"split full T={T}", split=True)
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_block_and_split_agree(full_layer, T):
+    shape = S(T=T, H=2048, I=512, E=256, top_k=8)
+    layer = full_layer.to("cuda")
+    _, x = make_inputs(shape, 120 + T, full_layer)
+    ra, oa = run_block(layer, x.cuda(), shape)
+    ra = [t.clone() for t in (ra.ids, ra.weights, ra.counts, ra.offsets, ra.perm)]
+    oa = oa.clone()
+    rb, ob = run_block(layer, x.cuda(), shape, split=True)
+    for a, b in zip(ra, (rb.ids, rb.weights, rb.counts, rb.offsets, rb.perm)):
+        assert torch.equal(a, b)
+    diff = (oa.float() - ob.float()).abs().max().item()
+    assert diff <= 1e-2 * ob.float().abs().max().item()
+
+
+def test_block_calls_leave_control_block_clear(full_layer):
+    """Forty single-call blocks in a row on one workspace (T = 1, 2, 1, ...) with
+    fresh inputs: sampled results match the oracle's routing, and the control
+    block ends all zero."""
+    layer = full_layer.to("cuda")
+    dims2 = B.make_dims(2, 2048, 512, 256, 8)
+    ws = B.alloc_workspace(dims2)
+    for i in range(40):
+        T = 1 + (i % 2)
+        shape = S(T=T, H=2048, I=512, E=256, top_k=8)
+        _, x = make_inputs(shape, 200 + i, full_layer)
+        r, _ = run_block(layer, x.cuda(), shape, workspace=ws)
+        if i % 8 == 0:
+            check_routing(r, O.route(x, full_layer.router_w, None, 8), f"call {i}")
+    assert int(ws[:256].cpu().sum()) == 0

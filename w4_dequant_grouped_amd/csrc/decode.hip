@@ -17,10 +17,11 @@
 //
 //   k_decode_gateup: (slot, 16 rows of I) per workgroup -> h = silu(g) * u (bf16)
 //   k_decode_down:   8 output rows per workgroup, every slot -> out (bf16)
-// A slot is an expert with a non-empty segment (ascending id), then the shared
-// expert.  Both kernels read the routing from the device; the grid depends only
-// on T.
+// A slot is the shared expert (first: it needs no routing, so its workgroups
+// start streaming at once) or an expert with a non-empty segment (ascending id).
+// Both kernels read the routing from the device; the grid depends only on T.
 #include "device.h"
+#include "gemv.h"
 #include "kernels.h"
 
 namespace moe_w4 {
@@ -33,63 +34,90 @@ struct Slot {
     int cnt;    // rows (tokens) in the slot
 };
 
-// Wavefront 0 lists the non-empty experts (ascending) and then the shared expert.
+// Lane l owns experts [l*per, l*per + per), per = ceil(E / 64) <= 16: it loads
+// their offsets in one go (one memory round trip for the whole scan), flags the
+// non-empty segments and gets an exclusive prefix count over the lanes.
+// Segments are clipped to the T*k routed rows, so malformed offsets cannot send
+// a row index out of range.
+struct ActiveScan {
+    int lo[17];        // clipped offsets of the lane's experts (lo[j]..lo[j+1])
+    int first;         // first expert of the lane
+    int per;           // experts per lane
+    int count;         // non-empty segments of the lane
+    int before;        // non-empty segments of lower lanes
+    int total;         // non-empty segments overall
+};
+
+__device__ __forceinline__ void scan_active(const int32_t* __restrict__ offsets, int E, int T, int k,
+                                            int lane, ActiveScan& a) {
+    const int lim = T * k;
+    a.per = (E + kWave - 1) / kWave;
+    a.first = lane * a.per;
+#pragma unroll
+    for (int j = 0; j < 17; ++j) {
+        const int e = a.first + j;
+        const int v = (j <= a.per && e <= E) ? offsets[min(e, E)] : lim;
+        a.lo[j] = min(max(v, 0), lim);
+    }
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (j < a.per && a.first + j < E) {
+            a.lo[j + 1] = max(a.lo[j + 1], a.lo[j]);
+            c += (a.lo[j + 1] > a.lo[j]) ? 1 : 0;
+        }
+    }
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
+    }
+    a.count = c;
+    a.before = incl - c;
+    a.total = __shfl(incl, kWave - 1, kWave);
+}
+
+// Slot list: the shared expert first (it needs no routing), then the experts
+// with a non-empty segment in ascending id.  Built by wavefront 0.
 __device__ __forceinline__ void build_slots(const int32_t* __restrict__ offsets, int E, int T, int k,
                                             int has_shared, Slot* s_slots, int* s_n, int lane) {
-    int base = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-        const int e = e0 + lane;
-        int a = 0, b = 0;
-        if (e < E) { a = offsets[e]; b = offsets[e + 1]; }
-        // a segment is clipped to the T*k routed rows, so malformed offsets cannot
-        // send a row index out of range
-        const int lim = T * k;
-        a = min(max(a, 0), lim);
-        b = min(max(b, a), lim);
-        const bool active = b > a;
-        const uint64_t mask = __ballot(active);
-        const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
-        if (active && pos < kMaxSlots - 1) s_slots[pos] = Slot{e, a, min(b - a, T)};
-        base += __popcll(mask);
+    ActiveScan a;
+    scan_active(offsets, E, T, k, lane, a);
+    const int base = has_shared ? 1 : 0;
+    if (has_shared && lane == 0) s_slots[0] = Slot{-1, T * k, T};
+    int pos = base + a.before;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (j < a.per && a.first + j < E && a.lo[j + 1] > a.lo[j]) {
+            if (pos < kMaxSlots) s_slots[pos] = Slot{a.first + j, a.lo[j], min(a.lo[j + 1] - a.lo[j], T)};
+            ++pos;
+        }
     }
-    base = min(base, kMaxSlots - 1);
-    if (lane == 0) {
-        if (has_shared) s_slots[base] = Slot{-1, T * k, T};
-        *s_n = base + (has_shared ? 1 : 0);
-    }
+    if (lane == 0) *s_n = min(base + a.total, kMaxSlots);
 }
 
-// 32 bf16 of a row (64 bytes at p) -> 16 dwords paired as (x[j], x[j+4]) per 8,
-// plus their sum.
-__device__ __forceinline__ void load_interleaved32(const uint16_t* p, uint32_t (&xi)[16], float& sum) {
-    const u32x4* q = reinterpret_cast<const u32x4*>(p);
-    float s = 0.f;
+// The idx-th non-empty expert (ascending id), found by one wavefront;
+// Slot{-2, 0, 0} if there are fewer.
+__device__ __forceinline__ Slot find_slot(const int32_t* __restrict__ offsets, int E, int T, int k,
+                                          int idx, int lane) {
+    ActiveScan a;
+    scan_active(offsets, E, T, k, lane, a);
+    if (idx >= a.total) return Slot{-2, 0, 0};
+    const bool mine = idx >= a.before && idx < a.before + a.count;
+    Slot r{0, 0, 0};
+    if (mine) {
+        int n = idx - a.before;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const u32x4 v = q[b];   // x[8b .. 8b+7] as 4 natural pairs
-        xi[4 * b + 0] = interleave_pair(v.x, v.z, 0);
-        xi[4 * b + 1] = interleave_pair(v.x, v.z, 1);
-        xi[4 * b + 2] = interleave_pair(v.y, v.w, 0);
-        xi[4 * b + 3] = interleave_pair(v.y, v.w, 1);
-        s = dot2_bf16(v.x, 0x3F803F80u, s);
-        s = dot2_bf16(v.y, 0x3F803F80u, s);
-        s = dot2_bf16(v.z, 0x3F803F80u, s);
-        s = dot2_bf16(v.w, 0x3F803F80u, s);
+        for (int j = 0; j < 16; ++j) {
+            if (j < a.per && a.first + j < E && a.lo[j + 1] > a.lo[j]) {
+                if (n == 0) r = Slot{a.first + j, a.lo[j], min(a.lo[j + 1] - a.lo[j], T)};
+                --n;
+            }
+        }
     }
-    sum = s;
-}
-
-// sum_k (128 + c_k) x_k over 32 codes (4 dwords) and the matching interleaved x.
-__device__ __forceinline__ float dot32_magic(const u32x4& c, const uint32_t (&xi)[16]) {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        a0 = dot2_bf16(magic_pair(c.x, j), xi[j], a0);
-        a1 = dot2_bf16(magic_pair(c.y, j), xi[4 + j], a1);
-        a0 = dot2_bf16(magic_pair(c.z, j), xi[8 + j], a0);
-        a1 = dot2_bf16(magic_pair(c.w, j), xi[12 + j], a1);
-    }
-    return a0 + a1;
+    const int src = __ffsll((long long)__ballot(mine)) - 1;
+    return Slot{__shfl(r.e, src, kWave), __shfl(r.off, src, kWave), __shfl(r.cnt, src, kWave)};
 }
 
 // ---------------------------------------------------------------------------
@@ -104,14 +132,21 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
     W4Set routed, W4Set shared, int has_shared,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     uint16_t* __restrict__ h) {
-    __shared__ Slot s_slots[kMaxSlots];
-    __shared__ int s_n;
+    __shared__ Slot s_slot;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    if (wave == 0) build_slots(offsets, E, T, k, has_shared, s_slots, &s_n, lane);
-    __syncthreads();
-    if ((int)blockIdx.x >= s_n) return;
-    const Slot sl = s_slots[blockIdx.x];
+    Slot sl;
+    if (has_shared && blockIdx.x == 0) {
+        sl = Slot{-1, T * k, T};                 // no dependence on the routing
+    } else {
+        if (wave == 0) {
+            const Slot f = find_slot(offsets, E, T, k, blockIdx.x - (has_shared ? 1 : 0), lane);
+            if (lane == 0) s_slot = f;
+        }
+        __syncthreads();
+        sl = s_slot;
+        if (sl.e < -1) return;                   // fewer active experts than blocks
+    }
     const bool is_shared = sl.e < 0;
     const int e = is_shared ? 0 : sl.e;
     const W4 G = is_shared ? shared.gate : routed.gate;
@@ -122,7 +157,8 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
 #pragma unroll
     for (int i = 0; i < TMAX; ++i) {
         tok[i] = 0;
-        if (i < sl.cnt) tok[i] = is_shared ? i : min(max(perm[sl.off + i], 0), T * k - 1) / k;
+        if (TMAX > 1 && i < sl.cnt)
+            tok[i] = is_shared ? i : min(max(perm[sl.off + i], 0), T * k - 1) / k;
     }
 
     const int n0 = blockIdx.y * kGuRowsPerBlock + wave * kGuRowsPerWave;
@@ -136,30 +172,35 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
 
     for (int c = lane; c < nchunks; c += kWave) {
         u32x4 cg[kGuRowsPerWave], cu[kGuRowsPerWave];
-        float sg[kGuRowsPerWave], bg[kGuRowsPerWave], su[kGuRowsPerWave], bu[kGuRowsPerWave];
+        uint32_t sg[kGuRowsPerWave], bg[kGuRowsPerWave], su[kGuRowsPerWave], bu[kGuRowsPerWave];
+        u32x4 xv[TMAX][4];
 #pragma unroll
         for (int r = 0; r < kGuRowsPerWave; ++r) {
             const size_t row = (size_t)e * I + (n0 + r);
             cg[r] = load_u32x4(G.codes + row * (H / 2) + c * 16);
             cu[r] = load_u32x4(U.codes + row * (H / 2) + c * 16);
             const size_t gi = row * ngroups + (c >> 1);
-            sg[r] = bf16_to_f32(G.scales[gi]);
-            bg[r] = bf16_to_f32(G.biases[gi]);
-            su[r] = bf16_to_f32(U.scales[gi]);
-            bu[r] = bf16_to_f32(U.biases[gi]);
+            sg[r] = G.scales[gi];
+            bg[r] = G.biases[gi];
+            su[r] = U.scales[gi];
+            bu[r] = U.biases[gi];
         }
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i)
+            if (i < sl.cnt) load64(x + (size_t)tok[i] * H + c * 32, xv[i]);
 #pragma unroll
         for (int i = 0; i < TMAX; ++i) {
             if (i >= sl.cnt) break;
             uint32_t xi[16];
             float xs;
-            load_interleaved32(x + (size_t)tok[i] * H + c * 32, xi, xs);
+            interleave32(xv[i], xi, xs);
 #pragma unroll
             for (int r = 0; r < kGuRowsPerWave; ++r) {
+                const float s0 = bf16_to_f32(sg[r]), s1 = bf16_to_f32(su[r]);
                 const float pg = dot32_magic(cg[r], xi);
                 const float pu = dot32_magic(cu[r], xi);
-                ag[r][i] += fmaf(sg[r], pg, (bg[r] - 128.0f * sg[r]) * xs);
-                au[r][i] += fmaf(su[r], pu, (bu[r] - 128.0f * su[r]) * xs);
+                ag[r][i] += fmaf(s0, pg, (bf16_to_f32(bg[r]) - 128.0f * s0) * xs);
+                au[r][i] += fmaf(s1, pu, (bf16_to_f32(bu[r]) - 128.0f * s1) * xs);
             }
         }
     }
@@ -181,6 +222,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
 // ---------------------------------------------------------------------------
 constexpr int kDnRowsPerWave = 2;
 constexpr int kDnRowsPerBlock = 4 * kDnRowsPerWave;
+constexpr int kDnUnroll = 3;     // (slot, chunk) items per lane whose loads are issued together
 
 template <int TMAX>
 __global__ __launch_bounds__(256) void k_decode_down(
@@ -198,6 +240,7 @@ __global__ __launch_bounds__(256) void k_decode_down(
     const int n0 = blockIdx.x * kDnRowsPerBlock + wave * kDnRowsPerWave;
     const int cpr = I / 32;            // 32-code chunks per down row
     const int ngroups = I / kGroup;
+    const int nitems = nslots * cpr;
 
     float acc[kDnRowsPerWave][TMAX];
 #pragma unroll
@@ -205,36 +248,53 @@ __global__ __launch_bounds__(256) void k_decode_down(
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) acc[r][t] = 0.f;
 
-    for (int idx = lane; idx < nslots * cpr; idx += kWave) {
-        const int a = idx / cpr, c = idx - a * cpr;
-        const Slot sl = s_slots[a];
-        const bool is_shared = sl.e < 0;
-        const int e = is_shared ? 0 : sl.e;
-        const W4 D = is_shared ? shared.down : routed.down;
-        u32x4 cd[kDnRowsPerWave];
-        float sd[kDnRowsPerWave], bd[kDnRowsPerWave];
+    for (int base = 0; base < nitems; base += kWave * kDnUnroll) {
+        u32x4 cd[kDnUnroll][kDnRowsPerWave];
+        uint32_t sd[kDnUnroll][kDnRowsPerWave], bd[kDnUnroll][kDnRowsPerWave];
+        Slot sl[kDnUnroll];
+        int cc[kDnUnroll];
 #pragma unroll
-        for (int r = 0; r < kDnRowsPerWave; ++r) {
-            const size_t row = (size_t)e * H + (n0 + r);
-            cd[r] = load_u32x4(D.codes + row * (I / 2) + c * 16);
-            const size_t gi = row * ngroups + (c >> 1);
-            sd[r] = bf16_to_f32(D.scales[gi]);
-            bd[r] = bf16_to_f32(D.biases[gi]) - 128.0f * sd[r];
-        }
-        for (int i = 0; i < sl.cnt; ++i) {
-            const int hrow = sl.off + i;
-            int t;
-            float w;
-            if (is_shared) { t = i; w = 1.0f; }
-            else { const int f = min(max(perm[hrow], 0), T * k - 1); t = f / k; w = topk_w[f]; }
-            uint32_t xi[16];
-            float hs;
-            load_interleaved32(h + (size_t)hrow * I + c * 32, xi, hs);
+        for (int u = 0; u < kDnUnroll; ++u) {
+            const int idx = base + u * kWave + lane;
+            const bool ok = idx < nitems;
+            const int a = ok ? idx / cpr : 0;
+            cc[u] = ok ? idx - a * cpr : 0;
+            sl[u] = s_slots[a];
+            if (!ok) sl[u].cnt = 0;
+            const bool is_shared = sl[u].e < 0;
+            const int e = is_shared ? 0 : sl[u].e;
+            const W4 D = is_shared ? shared.down : routed.down;
 #pragma unroll
             for (int r = 0; r < kDnRowsPerWave; ++r) {
-                const float v = w * fmaf(sd[r], dot32_magic(cd[r], xi), bd[r] * hs);
+                const size_t row = (size_t)e * H + (n0 + r);
+                cd[u][r] = load_u32x4(D.codes + row * (I / 2) + cc[u] * 16);
+                const size_t gi = row * ngroups + (cc[u] >> 1);
+                sd[u][r] = D.scales[gi];
+                bd[u][r] = D.biases[gi];
+            }
+        }
 #pragma unroll
-                for (int tt = 0; tt < TMAX; ++tt) acc[r][tt] += (tt == t) ? v : 0.f;
+        for (int u = 0; u < kDnUnroll; ++u) {
+            const bool is_shared = sl[u].e < 0;
+            for (int i = 0; i < sl[u].cnt; ++i) {
+                const int hrow = sl[u].off + i;
+                int t;
+                float w;
+                if (is_shared) { t = i; w = 1.0f; }
+                else { const int f = min(max(perm[hrow], 0), T * k - 1); t = f / k; w = topk_w[f]; }
+                u32x4 hv[4];
+                load64(h + (size_t)hrow * I + cc[u] * 32, hv);
+                uint32_t xi[16];
+                float hs;
+                interleave32(hv, xi, hs);
+#pragma unroll
+                for (int r = 0; r < kDnRowsPerWave; ++r) {
+                    const float s0 = bf16_to_f32(sd[u][r]);
+                    const float v = w * fmaf(s0, dot32_magic(cd[u][r], xi),
+                                             (bf16_to_f32(bd[u][r]) - 128.0f * s0) * hs);
+#pragma unroll
+                    for (int tt = 0; tt < TMAX; ++tt) acc[r][tt] += (tt == t) ? v : 0.f;
+                }
             }
         }
     }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe_w4 {
 
 constexpr int kWave = 64;
@@ -97,8 +99,9 @@ __device__ __forceinline__ bf16x8 dequant8_mix(uint32_t d, const DqConst& q, uin
 
 // Codes as bf16 "magic" pairs: bf16(128 + c) has bit pattern 0x4300 | c, exactly.
 // Pair j (j = 0..3) of a dword holds (c[j], c[j+4]) in (bits 0..15, bits 16..31).
-__device__ __forceinline__ uint32_t magic_pair(uint32_t d, int j) {
-    return ((d >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+// `magic` is 0x43004300 held in a register (one AND-OR per pair).
+__device__ __forceinline__ uint32_t magic_pair(uint32_t d, int j, uint32_t magic) {
+    return and_or(d >> (4 * j), 0x000F000Fu, magic);
 }
 
 // Reorder 8 consecutive bf16 values x0..x7 (given as 4 dwords of natural pairs)
@@ -115,20 +118,63 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // --- wave reductions ----------------------------------------------------------
+// Within each row of 16 lanes, DPP moves (quad_perm xor 1, xor 2, row_half_mirror,
+// row_mirror) pair every lane with partners covering the whole row; four
+// readlanes then combine the rows.  No LDS traffic, fixed summation order.
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+template <int ctrl>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, false);
+}
+template <int ctrl>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<ctrl>(__float_as_int(v)));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;       // lane i <-> 15-i within 16
+
+// Every lane receives the sum of its row of 16 lanes.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
     return v;
 }
 
-// Sum over groups of `width` consecutive lanes (width a power of two <= 64);
-// every lane of a group receives the group's sum.
-template <int width>
-__device__ __forceinline__ float group_sum(float v) {
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Sum over the wavefront, returned (uniform) in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+// Maximum of a 64-bit key over the wavefront, returned in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+    auto step = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+    auto mv = [](uint64_t a, auto ctrl) {
+        constexpr int c = decltype(ctrl)::value;
+        const int lo = dpp_i<c>((int)(uint32_t)a);
+        const int hi = dpp_i<c>((int)(uint32_t)(a >> 32));
+        return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+    };
+    k = step(k, mv(k, std::integral_constant<int, kDppXor1>{}));
+    k = step(k, mv(k, std::integral_constant<int, kDppXor2>{}));
+    k = step(k, mv(k, std::integral_constant<int, kDppHalfMirror>{}));
+    k = step(k, mv(k, std::integral_constant<int, kDppMirror>{}));
+    uint64_t r = 0;
 #pragma unroll
-    for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    for (int row = 0; row < 4; ++row) {
+        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, row * 16);
+        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), row * 16);
+        r = step(r, ((uint64_t)hi << 32) | lo);
+    }
+    return r;
 }
 
 // --- memory -------------------------------------------------------------------

@@ -81,15 +81,11 @@ size_t moe_w4_workspace_bytes(const moe_w4_dims* dims) {
     return layout(dims).total;
 }
 
-int moe_w4_route_timed(const moe_w4_dims* dims, const void* x, const float* router_w,
-                       const float* router_b, int32_t* topk_ids, float* topk_w,
-                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
-                       void* workspace, size_t workspace_bytes, void* hip_stream, void** events,
-                       int capacity, int* n_kernels) {
-    if (n_kernels) *n_kernels = 0;
-    int st;
-    if (!dims_ok(dims, &st)) return st;
-    if (dims->T == 0) return MOE_W4_OK;
+namespace {
+
+int check_route(const moe_w4_dims* dims, const void* x, const float* router_w, const float* router_b,
+                int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                int32_t* perm, void* workspace, size_t workspace_bytes) {
     if (!x || !router_w || !topk_ids || !topk_w || !expert_counts || !expert_offsets || !perm ||
         !workspace)
         return MOE_W4_ERR_NULL;
@@ -97,9 +93,40 @@ int moe_w4_route_timed(const moe_w4_dims* dims, const void* x, const float* rout
         !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_counts, 4) ||
         !aligned(expert_offsets, 4) || !aligned(perm, 4) || (router_b && !aligned(router_b, 4)))
         return MOE_W4_ERR_ALIGN;
-    const Layout L = layout(dims);
-    if (workspace_bytes < L.total) return MOE_W4_ERR_WORKSPACE;
+    if (workspace_bytes < layout(dims).total) return MOE_W4_ERR_WORKSPACE;
+    return MOE_W4_OK;
+}
 
+int check_forward(const moe_w4_dims* dims, const void* x, const moe_w4_weights* routed,
+                  const moe_w4_weights* shared, const float* topk_w, const int32_t* expert_offsets,
+                  const int32_t* perm, void* out, void* workspace, size_t workspace_bytes) {
+    if (!x || !routed || !topk_w || !expert_offsets || !perm || !out || !workspace)
+        return MOE_W4_ERR_NULL;
+    int st = MOE_W4_OK;
+    if (!mat_ok(routed->gate, &st) || !mat_ok(routed->up, &st) || !mat_ok(routed->down, &st))
+        return st;
+    if (shared && (!mat_ok(shared->gate, &st) || !mat_ok(shared->up, &st) || !mat_ok(shared->down, &st)))
+        return st;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, kAlign) || !aligned(topk_w, 4) ||
+        !aligned(expert_offsets, 4) || !aligned(perm, 4))
+        return MOE_W4_ERR_ALIGN;
+    if (workspace_bytes < layout(dims).total) return MOE_W4_ERR_WORKSPACE;
+    return MOE_W4_OK;
+}
+
+moe_w4::KernelTimer make_timer(void** events, int capacity, hipStream_t stream) {
+    moe_w4::KernelTimer tm;
+    tm.events = reinterpret_cast<hipEvent_t*>(events);
+    tm.capacity = events ? capacity : 0;
+    tm.stream = stream;
+    return tm;
+}
+
+hipError_t run_route(const moe_w4_dims* dims, const void* x, const float* router_w,
+                     const float* router_b, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* perm, void* workspace, hipStream_t stream,
+                     moe_w4::KernelTimer& tm) {
+    const Layout L = layout(dims);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     moe_w4::RouteArgs a;
     a.x = static_cast<const uint16_t*>(x);
@@ -117,13 +144,58 @@ int moe_w4_route_timed(const moe_w4_dims* dims, const void* x, const float* rout
     a.ws_ticket = reinterpret_cast<uint32_t*>(ws);
     a.ws_logits = reinterpret_cast<float*>(ws + L.logits);
     a.ws_planes = reinterpret_cast<uint16_t*>(ws + L.planes);
+    return (a.T <= moe_w4::kSmallRouteMaxT) ? moe_w4::launch_route_small(a, stream, tm)
+                                            : moe_w4::launch_route_large(a, stream, tm);
+}
+
+moe_w4::W4Set to_set(const moe_w4_weights* w) {
+    return moe_w4::W4Set{to_w4(w->gate), to_w4(w->up), to_w4(w->down)};
+}
+
+hipError_t run_forward(const moe_w4_dims* dims, const void* x, const moe_w4_weights* routed,
+                       const moe_w4_weights* shared, const float* topk_w,
+                       const int32_t* expert_offsets, const int32_t* perm, void* out,
+                       void* workspace, hipStream_t stream, moe_w4::KernelTimer& tm) {
+    const Layout L = layout(dims);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    moe_w4::ForwardArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.T = dims->T;
+    a.H = dims->H;
+    a.I = dims->I;
+    a.E = dims->E;
+    a.k = dims->top_k;
+    a.routed = to_set(routed);
+    a.has_shared = shared ? 1 : 0;
+    a.shared = shared ? to_set(shared) : a.routed;
+    a.topk_w = topk_w;
+    a.offsets = expert_offsets;
+    a.perm = perm;
+    a.out = static_cast<uint16_t*>(out);
+    a.ws_h = reinterpret_cast<uint16_t*>(ws + L.h);
+    a.ws_acc = reinterpret_cast<float*>(ws + L.acc);
+    return (a.T <= MOE_W4_DECODE_MAX_T) ? moe_w4::launch_forward_decode(a, stream, tm)
+                                        : moe_w4::launch_forward_grouped(a, stream, tm);
+}
+
+}  // namespace
+
+int moe_w4_route_timed(const moe_w4_dims* dims, const void* x, const float* router_w,
+                       const float* router_b, int32_t* topk_ids, float* topk_w,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                       void* workspace, size_t workspace_bytes, void* hip_stream, void** events,
+                       int capacity, int* n_kernels) {
+    if (n_kernels) *n_kernels = 0;
+    int st;
+    if (!dims_ok(dims, &st)) return st;
+    if (dims->T == 0) return MOE_W4_OK;
+    st = check_route(dims, x, router_w, router_b, topk_ids, topk_w, expert_counts, expert_offsets,
+                     perm, workspace, workspace_bytes);
+    if (st != MOE_W4_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    moe_w4::KernelTimer tm;
-    tm.events = reinterpret_cast<hipEvent_t*>(events);
-    tm.capacity = events ? capacity : 0;
-    tm.stream = stream;
-    const hipError_t err = (a.T <= moe_w4::kSmallRouteMaxT) ? moe_w4::launch_route_small(a, stream, tm)
-                                                            : moe_w4::launch_route_large(a, stream, tm);
+    moe_w4::KernelTimer tm = make_timer(events, capacity, stream);
+    const hipError_t err = run_route(dims, x, router_w, router_b, topk_ids, topk_w, expert_counts,
+                                     expert_offsets, perm, workspace, stream, tm);
     if (n_kernels) *n_kernels = tm.count;
     return launch_status(err);
 }
@@ -147,44 +219,13 @@ int moe_w4_forward_timed(const moe_w4_dims* dims, const void* x, const moe_w4_we
     int st;
     if (!dims_ok(dims, &st)) return st;
     if (dims->T == 0) return MOE_W4_OK;
-    if (!x || !routed || !topk_w || !expert_offsets || !perm || !out || !workspace)
-        return MOE_W4_ERR_NULL;
-    st = MOE_W4_OK;
-    if (!mat_ok(routed->gate, &st) || !mat_ok(routed->up, &st) || !mat_ok(routed->down, &st))
-        return st;
-    if (shared && (!mat_ok(shared->gate, &st) || !mat_ok(shared->up, &st) || !mat_ok(shared->down, &st)))
-        return st;
-    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, kAlign) || !aligned(topk_w, 4) ||
-        !aligned(expert_offsets, 4) || !aligned(perm, 4))
-        return MOE_W4_ERR_ALIGN;
-    const Layout L = layout(dims);
-    if (workspace_bytes < L.total) return MOE_W4_ERR_WORKSPACE;
-
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    moe_w4::ForwardArgs a;
-    a.x = static_cast<const uint16_t*>(x);
-    a.T = dims->T;
-    a.H = dims->H;
-    a.I = dims->I;
-    a.E = dims->E;
-    a.k = dims->top_k;
-    a.routed = moe_w4::W4Set{to_w4(routed->gate), to_w4(routed->up), to_w4(routed->down)};
-    a.has_shared = shared ? 1 : 0;
-    a.shared = shared ? moe_w4::W4Set{to_w4(shared->gate), to_w4(shared->up), to_w4(shared->down)}
-                      : a.routed;
-    a.topk_w = topk_w;
-    a.offsets = expert_offsets;
-    a.perm = perm;
-    a.out = static_cast<uint16_t*>(out);
-    a.ws_h = reinterpret_cast<uint16_t*>(ws + L.h);
-    a.ws_acc = reinterpret_cast<float*>(ws + L.acc);
+    st = check_forward(dims, x, routed, shared, topk_w, expert_offsets, perm, out, workspace,
+                       workspace_bytes);
+    if (st != MOE_W4_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    moe_w4::KernelTimer tm;
-    tm.events = reinterpret_cast<hipEvent_t*>(events);
-    tm.capacity = events ? capacity : 0;
-    tm.stream = stream;
-    const hipError_t err = (a.T <= MOE_W4_DECODE_MAX_T) ? moe_w4::launch_forward_decode(a, stream, tm)
-                                                         : moe_w4::launch_forward_grouped(a, stream, tm);
+    moe_w4::KernelTimer tm = make_timer(events, capacity, stream);
+    const hipError_t err = run_forward(dims, x, routed, shared, topk_w, expert_offsets, perm, out,
+                                       workspace, stream, tm);
     if (n_kernels) *n_kernels = tm.count;
     return launch_status(err);
 }
@@ -195,6 +236,43 @@ int moe_w4_forward(const moe_w4_dims* dims, const void* x, const moe_w4_weights*
                    size_t workspace_bytes, void* hip_stream) {
     return moe_w4_forward_timed(dims, x, routed, shared, topk_ids, topk_w, expert_offsets, perm, out,
                                 workspace, workspace_bytes, hip_stream, nullptr, 0, nullptr);
+}
+
+int moe_w4_block_timed(const moe_w4_dims* dims, const void* x, const float* router_w,
+                       const float* router_b, const moe_w4_weights* routed,
+                       const moe_w4_weights* shared, int32_t* topk_ids, float* topk_w,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm, void* out,
+                       void* workspace, size_t workspace_bytes, void* hip_stream, void** events,
+                       int capacity, int* n_kernels) {
+    if (n_kernels) *n_kernels = 0;
+    int st;
+    if (!dims_ok(dims, &st)) return st;
+    if (dims->T == 0) return MOE_W4_OK;
+    st = check_route(dims, x, router_w, router_b, topk_ids, topk_w, expert_counts, expert_offsets,
+                     perm, workspace, workspace_bytes);
+    if (st != MOE_W4_OK) return st;
+    st = check_forward(dims, x, routed, shared, topk_w, expert_offsets, perm, out, workspace,
+                       workspace_bytes);
+    if (st != MOE_W4_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    moe_w4::KernelTimer tm = make_timer(events, capacity, stream);
+    hipError_t err = run_route(dims, x, router_w, router_b, topk_ids, topk_w, expert_counts,
+                               expert_offsets, perm, workspace, stream, tm);
+    if (err == hipSuccess)
+        err = run_forward(dims, x, routed, shared, topk_w, expert_offsets, perm, out, workspace,
+                          stream, tm);
+    if (n_kernels) *n_kernels = tm.count;
+    return launch_status(err);
+}
+
+int moe_w4_block(const moe_w4_dims* dims, const void* x, const float* router_w,
+                 const float* router_b, const moe_w4_weights* routed, const moe_w4_weights* shared,
+                 int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                 int32_t* perm, void* out, void* workspace, size_t workspace_bytes,
+                 void* hip_stream) {
+    return moe_w4_block_timed(dims, x, router_w, router_b, routed, shared, topk_ids, topk_w,
+                              expert_counts, expert_offsets, perm, out, workspace, workspace_bytes,
+                              hip_stream, nullptr, 0, nullptr);
 }
 
 const char* moe_w4_status_string(int status) {

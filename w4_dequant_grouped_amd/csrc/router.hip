@@ -17,91 +17,9 @@
 //    (no atomics, no histogram shared between workgroups).
 #include "device.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe_w4 {
-
-constexpr int kMaxTopK = 16;
-
-// ---------------------------------------------------------------------------
-// top-k of one token's logits held by one wavefront
-// ---------------------------------------------------------------------------
-// vals[j] is the logit of expert e = lane + 64 * j (or -inf past E).  Chooses the
-// k largest (ties -> lower expert index); lane r < k writes chosen entry r, at its
-// rank in ascending expert order, to ids_out / w_out (global) and to ids_lds when
-// given; the weights are the renormalised softmax exp(l - lmax) / sum over the
-// chosen.  Returns, in every lane, the id chosen in round `lane` (-1 if lane >= k).
-// Order-preserving key of a float: larger float -> larger key; -0 counts as +0.
-// The order is total (NaN sorts above +inf), so every lane agrees on the result
-// and the chosen ids are always k distinct valid experts.
-__device__ __forceinline__ uint32_t order_key(float v) {
-    uint32_t b = __float_as_uint(v);
-    if (b == 0x80000000u) b = 0u;
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-template <int EPL>
-__device__ int wave_topk(float (&vals)[EPL], int E, int k, int lane,
-                         int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-                         int32_t* ids_lds) {
-    int sel_e[kMaxTopK];
-    float sel_v[kMaxTopK];
-    uint32_t key[EPL];
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) key[j] = order_key(vals[j]);
-    uint32_t taken = 0;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-        if (r >= k) { sel_e[r] = 0x7FFFFFFF; sel_v[r] = 0.f; continue; }
-        uint32_t bk = 0u;
-        int be = 0x7FFFFFFF;
-        float bv = 0.f;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = lane + kWave * j;
-            const bool ok = e < E && !((taken >> j) & 1u);
-            if (ok && (be == 0x7FFFFFFF || key[j] > bk || (key[j] == bk && e < be))) {
-                bk = key[j]; be = e; bv = vals[j];
-            }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const uint32_t ok_ = __shfl_xor(bk, o, kWave);
-            const int oe = __shfl_xor(be, o, kWave);
-            const float ov = __shfl_xor(bv, o, kWave);
-            if (oe != 0x7FFFFFFF && (be == 0x7FFFFFFF || ok_ > bk || (ok_ == bk && oe < be))) {
-                bk = ok_; be = oe; bv = ov;
-            }
-        }
-        sel_e[r] = be;
-        sel_v[r] = bv;
-        if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-    }
-    // renormalised softmax over the chosen logits (the full-softmax denominator cancels)
-    const float vmax = sel_v[0];
-    float p[kMaxTopK];
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-        p[r] = (r < k) ? expf(sel_v[r] - vmax) : 0.f;
-        psum += p[r];
-    }
-    const float inv = 1.0f / psum;
-    int mine = -1;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-        if (r >= k) break;
-        int rank = 0;
-#pragma unroll
-        for (int q = 0; q < kMaxTopK; ++q) rank += (q < k && sel_e[q] < sel_e[r]) ? 1 : 0;
-        if (lane == r) {
-            mine = sel_e[r];
-            ids_out[rank] = sel_e[r];
-            w_out[rank] = p[r] * inv;
-            if (ids_lds) ids_lds[rank] = sel_e[r];
-        }
-    }
-    return mine;
-}
 
 // ---------------------------------------------------------------------------
 // small-T router: one launch
@@ -121,51 +39,65 @@ __global__ __launch_bounds__(kSmallRouteThreads) void k_route_small(
     const int gw = blockIdx.x * (kSmallRouteThreads / kWave) + wave;
     const int nw = gridDim.x * (kSmallRouteThreads / kWave);
 
-    // phase 1: logits[t][e] for the experts of this wavefront
+    // phase 1: logits[t][e] for the experts of this wavefront; all of a lane's
+    // W_r and x loads for up to 2048 columns are issued before any is used
     for (int e = gw; e < E; e += nw) {
         float acc[TMAX];
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) acc[t] = 0.f;
         const float* wrow = Wr + (size_t)e * H;
-        for (int h = lane * 4; h < H; h += kWave * 4) {
-            const float4 wv = *reinterpret_cast<const float4*>(wrow + h);
+        for (int h0 = 0; h0 < H; h0 += kWave * 4 * 8) {
+            float4 wv[8];
+            u32x2 xv[8][TMAX];
 #pragma unroll
-            for (int t = 0; t < TMAX; ++t) {
-                if (t < T) {
-                    const u32x2 xv = *reinterpret_cast<const u32x2*>(x + (size_t)t * H + h);
-                    acc[t] = fmaf(bf16lo(xv.x), wv.x, acc[t]);
-                    acc[t] = fmaf(bf16hi(xv.x), wv.y, acc[t]);
-                    acc[t] = fmaf(bf16lo(xv.y), wv.z, acc[t]);
-                    acc[t] = fmaf(bf16hi(xv.y), wv.w, acc[t]);
-                }
+            for (int u = 0; u < 8; ++u) {
+                const int h = h0 + (u * kWave + lane) * 4;
+                const bool ok = h < H;
+                wv[u] = ok ? *reinterpret_cast<const float4*>(wrow + h) : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t)
+                    xv[u][t] = (ok && t < T) ? *reinterpret_cast<const u32x2*>(x + (size_t)t * H + h)
+                                             : u32x2{0u, 0u};
             }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t) {
+                    acc[t] = fmaf(bf16lo(xv[u][t].x), wv[u].x, acc[t]);
+                    acc[t] = fmaf(bf16hi(xv[u][t].x), wv[u].y, acc[t]);
+                    acc[t] = fmaf(bf16lo(xv[u][t].y), wv[u].z, acc[t]);
+                    acc[t] = fmaf(bf16hi(xv[u][t].y), wv[u].w, acc[t]);
+                }
         }
         const float bias = br ? br[e] : 0.f;
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
             if (t < T) {
-                const float s = wave_sum(acc[t]);
+                const float sum = wave_sum(acc[t]);
                 if (lane == 0)
-                    __hip_atomic_store(&logits[t * E + e], s + bias, __ATOMIC_RELAXED,
+                    __hip_atomic_store(&logits[t * E + e], sum + bias, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
 
-    // phase 2: the last workgroup to finish selects and groups
+    // phase 2: the last workgroup to finish selects and groups.  The logits are
+    // written and read with device-scope atomics, which bypass the per-XCD
+    // caches; each wavefront waits for its own stores to complete before the
+    // workgroup takes its ticket, so the workgroup drawing the last ticket sees
+    // every logit.  (A full device fence here would also write back the L2.)
     __shared__ int s_last;
     __shared__ int32_t s_ids[TMAX * kMaxTopK];
     __shared__ int32_t s_cnt[1024];
-    __threadfence();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL,
+        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == gridDim.x - 1);
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
 
     for (int t = wave; t < T; t += kSmallRouteThreads / kWave) {
         float vals[EPL];

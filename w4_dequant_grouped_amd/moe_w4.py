@@ -34,8 +34,9 @@ class moe_w4_weights(ctypes.Structure):
     _fields_ = [("gate", moe_w4_mat), ("up", moe_w4_mat), ("down", moe_w4_mat)]
 
 
-EXPORTS = ("moe_w4_workspace_bytes", "moe_w4_route", "moe_w4_forward", "moe_w4_route_timed",
-           "moe_w4_forward_timed", "moe_w4_status_string", "moe_w4_last_error")
+EXPORTS = ("moe_w4_workspace_bytes", "moe_w4_route", "moe_w4_forward", "moe_w4_block",
+           "moe_w4_route_timed", "moe_w4_forward_timed", "moe_w4_block_timed",
+           "moe_w4_status_string", "moe_w4_last_error")
 
 _lib = None
 
@@ -58,6 +59,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    ctypes.POINTER(moe_w4_weights), P, P, P, P, P, P,
                                    ctypes.c_size_t, P]
     lib.moe_w4_forward.restype = ctypes.c_int
+    W = ctypes.POINTER(moe_w4_weights)
+    lib.moe_w4_block.argtypes = [ctypes.POINTER(moe_w4_dims), P, P, P, W, W, P, P, P, P, P, P, P,
+                                 ctypes.c_size_t, P]
+    lib.moe_w4_block.restype = ctypes.c_int
+    lib.moe_w4_block_timed.argtypes = lib.moe_w4_block.argtypes + [P, ctypes.c_int, P]
+    lib.moe_w4_block_timed.restype = ctypes.c_int
     lib.moe_w4_route_timed.argtypes = lib.moe_w4_route.argtypes + [P, ctypes.c_int, P]
     lib.moe_w4_route_timed.restype = ctypes.c_int
     lib.moe_w4_forward_timed.argtypes = lib.moe_w4_forward.argtypes + [P, ctypes.c_int, P]
@@ -192,6 +199,41 @@ def moe_w4_forward(dims: moe_w4_dims, x: torch.Tensor, routed, shared, routing: 
     return out
 
 
+def _check_routing(routing: Routing) -> None:
+    for name in ("ids", "counts", "offsets", "perm"):
+        _dev(getattr(routing, name), torch.int32, name)
+    _dev(routing.weights, torch.float32, "weights")
+
+
+def moe_w4_block(dims: moe_w4_dims, x: torch.Tensor, router_w: torch.Tensor,
+                 router_b: Optional[torch.Tensor], routed_struct: moe_w4_weights,
+                 shared_struct: Optional[moe_w4_weights], routing: Routing, out: torch.Tensor,
+                 workspace: torch.Tensor, events=None) -> int:
+    """Route and forward in one library call.
+
+    With ``events`` (hipEvent handles) the call records them around each kernel
+    and returns the kernel count; otherwise returns 0."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(router_w, torch.float32, "router_w")
+    if router_b is not None:
+        _dev(router_b, torch.float32, "router_b")
+    _check_routing(routing)
+    _dev(out, torch.bfloat16, "out")
+    _dev(workspace, torch.uint8, "workspace")
+    lib = load_library()
+    args = (ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(router_b), ctypes.byref(routed_struct),
+            None if shared_struct is None else ctypes.byref(shared_struct), _ptr(routing.ids),
+            _ptr(routing.weights), _ptr(routing.counts), _ptr(routing.offsets), _ptr(routing.perm),
+            _ptr(out), _ptr(workspace), workspace.numel(), _stream())
+    if events is None:
+        _check(lib.moe_w4_block(*args), "moe_w4_block")
+        return 0
+    arr, cap = _events_arg(events)
+    n = ctypes.c_int(0)
+    _check(lib.moe_w4_block_timed(*args, arr, cap, ctypes.byref(n)), "moe_w4_block_timed")
+    return n.value
+
+
 def _events_arg(events):
     if events is None:
         return None, 0
@@ -243,10 +285,22 @@ class Block:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def __call__(self, x: torch.Tensor) -> torch.Tensor:
+        """Route + forward through the single-call entry point."""
+        moe_w4_block(self.dims, x, self.layer.router_w, self.layer.router_b, self.routed_struct,
+                     self.shared_struct, self.routing, self.out, self.workspace)
+        return self.out
+
+    def split(self, x: torch.Tensor) -> torch.Tensor:
+        """Route, then forward, as two separate library calls."""
         moe_w4_route(self.dims, x, self.layer.router_w, self.layer.router_b, self.routing, self.workspace)
         moe_w4_forward(self.dims, x, self.layer.routed, self.layer.shared, self.routing, self.out,
                        self.workspace, self.routed_struct, self.shared_struct)
         return self.out
+
+    def block_timed(self, x: torch.Tensor, events) -> int:
+        """One single-call block recording events around every kernel; returns the kernel count."""
+        return moe_w4_block(self.dims, x, self.layer.router_w, self.layer.router_b, self.routed_struct,
+                            self.shared_struct, self.routing, self.out, self.workspace, events)
 
     def timed(self, x: torch.Tensor, route_events, forward_events):
         """One call recording events around every kernel; returns (route kernels, forward kernels)."""
