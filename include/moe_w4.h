@@ -29,8 +29,8 @@
  *    Device faults surface at the caller's next synchronisation, as in HIP.
  *  - Workspace: `workspace` must hold at least moe_w4_workspace_bytes(dims)
  *    bytes, be 256-byte aligned, and be ZERO-FILLED before the first call that
- *    uses it.  Every call leaves its first 256 bytes (a control block) zero
- *    again.  route() and forward() for the same dims may share one workspace;
+ *    uses it.  Its first MOE_W4_CONTROL_BYTES bytes are a control block (ticket
+ *    and work-queue counters) that every call leaves zero again.  route() and forward() for the same dims may share one workspace;
  *    calls that may run concurrently need distinct workspaces.
  *
  * Weight layout (moe_w4_mat), for E matrices of shape [N][K]:
@@ -39,7 +39,7 @@
  *    scales  bf16   [E][N][K/G]   per (row, group of G consecutive k)
  *    biases  bf16   [E][N][K/G]
  *    dequantised weight  w[e][n][k] = code * scale[e][n][k/G] + bias[e][n][k/G]
- *  `codes` must be 16-byte aligned, `scales` and `biases` 2-byte aligned.
+ *  `codes` must be 16-byte aligned, `scales` and `biases` 4-byte aligned.
  *  `x`, `out` and `router_w` must be 16-byte aligned, int32/fp32 arrays 4-byte.
  *
  * Supported sizes (checked): 1 <= top_k <= 16, top_k <= E <= 1024, group == 64,
@@ -57,6 +57,9 @@ extern "C" {
 
 /* Largest T served by the decode (GEMV) path of moe_w4_forward(). */
 #define MOE_W4_DECODE_MAX_T 5
+
+/* Bytes at the start of the workspace used as the control block. */
+#define MOE_W4_CONTROL_BYTES 4096
 
 enum {
     MOE_W4_OK = 0,

@@ -62,7 +62,8 @@ def test_workspace_bytes(lib):
     # K-split partial logits + bf16 split of the router weight + h (T*k + T rows) + fp32 accumulator;
     # no term for expanded expert weights
     T, H, I, E, k = 2048, 2048, 512, 256, 8
-    expect_min = 4 * T * E * 4 + 3 * E * H * 2 + (T * k + T) * I * 2 + T * H * 4
+    expect_min = (B.MOE_W4_CONTROL_BYTES + 4 * T * E * 4 + 3 * E * H * 2 + (T * k + T) * I * 2
+                  + T * H * 4)
     assert expect_min <= big <= expect_min + 256 * 8
     assert big < E * I * H * 2 // 10      # far below one bf16 copy of the routed weights
     for bad in (_dims(group=32), _dims(H=300), _dims(I=100), _dims(top_k=0), _dims(top_k=17),
@@ -130,6 +131,7 @@ def test_forward_rejects_bad_arguments(lib):
     assert _forward(lib, _dims(), shared=_weights(biases=None)) == ERR_NULL
     assert _forward(lib, _dims(), routed=_weights(codes=FAKE + 8)) == ERR_ALIGN
     assert _forward(lib, _dims(), shared=_weights(scales=FAKE + 1)) == ERR_ALIGN
+    assert _forward(lib, _dims(), routed=_weights(biases=FAKE + 2)) == ERR_ALIGN
     assert _forward(lib, _dims(), out=FAKE + 2) == ERR_ALIGN
     assert _forward(lib, _dims(), x=FAKE + 8) == ERR_ALIGN
     d = _dims()

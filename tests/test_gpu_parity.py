@@ -153,7 +153,7 @@ def test_repeat_calls_and_workspace_reuse(full_layer):
     rs, os_ = run_block(layer, x1.cuda(), S(T=1, H=2048, I=512, E=256, top_k=8), workspace=ws)
     ref1 = O.route(x1, full_layer.router_w, None, 8)
     check_routing(rs, ref1, "T=1 after T=2048")
-    assert int(ws[:256].cpu().sum()) == 0
+    assert int(ws[:B.MOE_W4_CONTROL_BYTES].cpu().sum()) == 0
     r2, o2 = run_block(layer, xb.cuda(), big, workspace=ws)
     for a, b in zip(r1, (r2.ids, r2.counts, r2.offsets, r2.perm)):
         assert torch.equal(a, b)
@@ -222,4 +222,4 @@ def test_block_calls_leave_control_block_clear(full_layer):
         r, _ = run_block(layer, x.cuda(), shape, workspace=ws)
         if i % 8 == 0:
             check_routing(r, O.route(x, full_layer.router_w, None, 8), f"call {i}")
-    assert int(ws[:256].cpu().sum()) == 0
+    assert int(ws[:B.MOE_W4_CONTROL_BYTES].cpu().sum()) == 0

@@ -110,78 +110,130 @@ __device__ __forceinline__ TileCtx locate(int mt, const int* s_pre, int nseg, in
     return c;
 }
 
-// tile index -> (M-tile, N-tile): the NT N-tiles of one M-tile go to workgroups
-// with equal index mod 8 (one XCD)
+// Tiles are handed out dynamically from 8 queues in the control block.  Queue q
+// holds the M-tiles mt = q (mod 8), each followed by its NT N-tiles; tile index
+// i = q + 8 j of queue entry j maps to (M-tile, N-tile) below.  Workgroup b runs
+// on XCD b mod 8 (round-robin dispatch) and serves queue b mod 8 first, so the
+// N-tiles of one M-tile, which share its gathered activation rows, are normally
+// taken by workgroups of one XCD and find those rows in its L2.  A workgroup
+// whose queue is empty takes tiles from the others.
 __device__ __forceinline__ void tile_coords(int i, int NT, int& mt, int& nt) {
     mt = (i & 7) + 8 * (i / (8 * NT));
     nt = (i >> 3) % NT;
 }
 
-// ---------------------------------------------------------------------------
-// The K-loop of one tile, software-pipelined:
-//   A (kBM rows x kKC bf16 per chunk) is copied global -> LDS by the direct
-//   global_load_lds_dwordx4 path (no registers), double buffered, one barrier
-//   per chunk.  Each lane supplies its own source address, so the rows are
-//   gathered by token on the fly and the 16-byte chunks of a row are stored
-//   XOR-swizzled by row, which keeps the MFMA operand reads conflict-free.
-//   B (codes, 128 bits per lane per 16-row block, plus the group's scale and
-//   bias) goes straight to registers and is dequantised there.  The next
-//   chunk's A and B are in flight while the current chunk's MFMAs run.
-// ---------------------------------------------------------------------------
-constexpr int kARow = kKC * 2;               // bytes of one A row per chunk (256)
-constexpr int kABuf = kBM * kARow;           // bytes of one A buffer (32 KiB)
-constexpr int kStages = 4;                   // K-loop pipeline depth
-constexpr int kRowsPerWaveDma = kBM / kWaves;   // A rows copied by each wavefront
-constexpr int kDmaPerWave = kRowsPerWaveDma / 4;  // 4 rows (1 KiB) per DMA instruction
-
-template <int NMAT, int NBW>
-struct BRegs {
-    u32x4 c[NMAT][NBW];
-    uint32_t s[NMAT][NBW];      // bf16 scale bits (combined only at use, so that
-    uint32_t b[NMAT][NBW];      // issuing the loads never waits for them)
-};
-
-// Per-lane B addressing: element offsets of the lane's row within its matrix set.
-template <int NMAT, int NBW>
-struct BAddr {
-    const uint8_t* codes[NMAT];      // matrix base (wave-uniform)
-    const uint16_t* scales[NMAT];
-    const uint16_t* biases[NMAT];
-    uint32_t row[NBW];               // row index (expert * N + n) of each 16-row block
-    int K;
-    int lane;
-};
-
-// Loads of chunk kc; a dummy chunk (past the end of K) loads the first bytes of
-// each matrix in every lane, one cache line per instruction, so that the number
-// of loads per chunk never varies.
-template <int NMAT, int NBW>
-__device__ __forceinline__ void load_b_chunk(BRegs<NMAT, NBW>& r, const BAddr<NMAT, NBW>& a, int kc,
-                                             bool dummy) {
-    const int kq = a.K / kGroup;
-    const int g = kc / kGroup + ((a.lane >> 4) >> 1);         // lanes 32..63 use the odd group
-    const int cb = (kc >> 1) + (a.lane >> 4) * 16;
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-            const size_t row = a.row[nb];
-            const size_t co = dummy ? 0 : row * (size_t)(a.K / 2) + cb;
-            const size_t so = dummy ? 0 : row * kq + g;
-            r.c[m][nb] = load_u32x4(a.codes[m] + co);
-            r.s[m][nb] = a.scales[m][so];
-            r.b[m][nb] = a.biases[m][so];
-        }
+// Entries in queue q.
+__device__ __forceinline__ int queue_len(int q, int n_mt, int NT) {
+    return (n_mt > q) ? ((n_mt - q + 7) / 8) * NT : 0;
 }
 
-// 16 bytes per lane, global -> LDS, written at lds + 16 * lane (lds is the same for
-// the whole wavefront).  Issued through inline assembly so that the compiler's
-// wait insertion does not see it: it would otherwise wait for every in-flight
-// copy at each barrier, which serialises the pipeline.  The K-loop waits for the
-// copies explicitly with vmcnt; M0 is restored after use.
-__device__ __forceinline__ void dma16_to_lds(const void* src, void* lds) {
-    const uint32_t l = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+__device__ __forceinline__ uint32_t queue_take(uint32_t* ctl, int q) {
+    return __hip_atomic_fetch_add(ctl + kCtlQueue + q * kCtlQueueStride, 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Next tile index for this workgroup, or -1 when every queue is empty.  `q`
+// is the queue to try first and, on success, the queue the tile came from;
+// `empty` remembers the queues already found empty.
+__device__ __forceinline__ int grab_tile(uint32_t* ctl, int n_mt, int NT, int& q, uint32_t& empty) {
+    for (int d = 0; d < 8; ++d) {
+        const int qq = (q + d) & 7;
+        if (empty & (1u << qq)) continue;
+        const int lim = queue_len(qq, n_mt, NT);
+        if (lim > 0) {
+            const uint32_t j = queue_take(ctl, qq);
+            if ((int)j < lim) {
+                q = qq;
+                return qq + 8 * (int)j;
+            }
+        }
+        empty |= 1u << qq;
+    }
+    return -1;
+}
+
+// Tile scheduling state of a workgroup (meaningful in thread 0 only).  While a
+// tile is processed, the next entry of the current queue is already being
+// taken; its result is needed only when the tile is done.
+struct TileQueue {
+    int q;               // current queue
+    uint32_t empty;      // queues found empty
+    uint32_t taken;      // entry taken from queue q for the next tile
+    bool pending;
+    __device__ __forceinline__ void prefetch(uint32_t* ctl) {
+        pending = !(empty & (1u << q));
+        if (pending) taken = queue_take(ctl, q);
+    }
+    __device__ __forceinline__ int next(uint32_t* ctl, int n_mt, int NT) {
+        if (pending && (int)taken < queue_len(q, n_mt, NT)) return q + 8 * (int)taken;
+        if (pending) empty |= 1u << q;
+        return grab_tile(ctl, n_mt, NT, q, empty);
+    }
+};
+
+// The last workgroup to finish clears the queues for the next launch.
+__device__ __forceinline__ void release_queues(uint32_t* ctl) {
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(ctl + kCtlExit, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == gridDim.x - 1) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                __hip_atomic_store(ctl + kCtlQueue + q * kCtlQueueStride, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ctl + kCtlExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The K-loop of one tile, software-pipelined through LDS.
+//   Every operand byte of a K chunk -- the kBM activation rows (A), the
+//   wavefront's packed weight rows (B codes) and their group scale/bias words --
+//   is copied global -> LDS by the direct global_load_lds path, issued through
+//   inline assembly.  The loop therefore holds no load the compiler tracks: the
+//   only waits on the copies are the explicit vmcnt waits, which count exactly
+//   the copies issued after the chunk being consumed (a compiler-tracked load
+//   among untracked copies would make the compiler's own waits drain later
+//   chunks too, collapsing the pipeline).  kStages buffers form a ring: while
+//   chunk c is multiplied, chunks c+1 .. c+kStages-2 are in flight and chunk
+//   c+kStages-1 is being issued.  A rows are gathered by token on the fly and
+//   stored XOR-swizzled by row, which keeps the MFMA operand reads conflict-free.
+// ---------------------------------------------------------------------------
+constexpr int kARow = kKC * 2;                     // bytes of one A row per chunk (256)
+constexpr int kABuf = kBM * kARow;                 // A bytes per stage (32 KiB)
+constexpr int kBRowBytes = kKC / 2;                // packed codes of a weight row per chunk (64)
+constexpr int kBBlk = 16 * kBRowBytes;             // codes of one 16-row block (1 KiB)
+constexpr int kBlkPerWave = 2;                     // (matrix, 16-row block) pairs per wavefront
+constexpr int kBBuf = kWaves * kBlkPerWave * kBBlk;    // B code bytes per stage (16 KiB)
+constexpr int kSBWave = kWave * 4;                 // scale/bias words of a wavefront (256 B)
+constexpr int kSBBuf = kWaves * kSBWave;           // per stage (2 KiB)
+constexpr int kStageBytes = kABuf + kBBuf + kSBBuf;
+constexpr int kStages = 3;                         // 150 KiB of the 160 KiB LDS
+constexpr int kRowsPerWaveDma = kBM / kWaves;      // A rows copied by each wavefront
+constexpr int kDmaPerWave = kRowsPerWaveDma / 4;   // 4 rows (1 KiB) per A copy instruction
+constexpr int kLoadsPerChunk = kDmaPerWave + kBlkPerWave + 1;   // copies per wavefront per chunk
+
+// Per-wavefront B addressing (wave-uniform).
+template <int NMAT, int NBW>
+struct BAddr {
+    const uint8_t* codes[NMAT];      // matrix bases
+    const uint16_t* scales[NMAT];
+    const uint16_t* biases[NMAT];
+    uint32_t rowblk[NBW];            // first row (expert * N + n) of each 16-row block
+    int K;
+};
+
+// global -> LDS copies.  `lds` is the same for the whole wavefront; lane i
+// writes at lds + 16 i (dwordx4) or lds + 4 i (dword).  Issued through inline
+// assembly so that the compiler's wait insertion does not see them (it would
+// otherwise wait for every in-flight copy at each barrier); the K-loop waits for
+// them explicitly.  M0 is restored after use.
+__device__ __forceinline__ uint32_t lds_base(const void* lds) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+}
+__device__ __forceinline__ void dma16_to_lds(const void* src, const void* lds) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -190,7 +242,19 @@ __device__ __forceinline__ void dma16_to_lds(const void* src, void* lds) {
         "global_load_lds_dwordx4 %1, off\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(src), "s"(l)
+        : "v"(src), "s"(lds_base(lds))
+        : "memory");
+}
+__device__ __forceinline__ void dma4_to_lds(const void* src, const void* lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds_base(lds))
         : "memory");
 }
 
@@ -199,12 +263,13 @@ __device__ __forceinline__ void dma16_to_lds(const void* src, void* lds) {
 struct ASrc {
     const uint8_t* base;
     size_t row_bytes;
-    int rowidx[kDmaPerWave];   // row index of the lane's row in each DMA instruction
+    int rowidx[kDmaPerWave];   // row index of the lane's row in each copy instruction
 };
 
-// Issue the DMA of one A chunk: wavefront w copies rows [16w, 16w+16), four rows
-// (64 lanes x 16 bytes) per instruction.  Rows past the tile's valid rows re-read
-// its last valid row, so every address stays inside the operand.
+// Copy one A chunk: wavefront w copies rows [16w, 16w+16), four rows (64 lanes x
+// 16 bytes) per instruction.  Rows past the tile's valid rows re-read its last
+// valid row, so every address stays inside the operand.  A dummy chunk (past the
+// end of K) reads the operand's first bytes.
 __device__ __forceinline__ void issue_a_dma(uint8_t* s_buf, int wave, int lane, const ASrc& a,
                                             int kc_bytes, bool dummy) {
 #pragma unroll
@@ -218,6 +283,54 @@ __device__ __forceinline__ void issue_a_dma(uint8_t* s_buf, int wave, int lane, 
     }
 }
 
+// Copy the wavefront's B operands of chunk kc into its slices of the stage:
+//  * codes: one instruction per (matrix, 16-row block) pair p; lane L fills
+//    slot L&3 (16 bytes) of row r = L>>2 (64 B per row) with quarter
+//    (L&3) ^ ((r>>2)&3) of the row's 64 code bytes of the chunk.  The XOR
+//    spreads the 16 rows' reads of one quarter over all LDS banks;
+//  * scale/bias: one dword instruction; lane L copies the word holding the
+//    chunk's two groups (even group in the low half) of row L&15, from the
+//    scales (bit 4 of L clear) or biases, of pair p = L>>5.  The word is 4-byte
+//    aligned because K/64 is even and the arrays are 4-byte aligned.
+template <int NMAT, int NBW>
+__device__ __forceinline__ void issue_b_dma(uint8_t* s_b, uint8_t* s_sb, const BAddr<NMAT, NBW>& a,
+                                            int lane, int kc, bool dummy) {
+    static_assert(NMAT * NBW == kBlkPerWave, "B slice layout");
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const size_t row = a.rowblk[nb] + (lane >> 2);
+            const int quarter = (lane & 3) ^ ((lane >> 4) & 3);
+            const uint8_t* src = dummy ? a.codes[m]
+                                       : a.codes[m] + row * (size_t)(a.K / 2) + (kc >> 1) + quarter * 16;
+            dma16_to_lds(src, s_b + (m * NBW + nb) * kBBlk);
+        }
+    // per-lane choice of array and row by bit masks on the (wave-uniform) values,
+    // so that no array of the argument struct is indexed by a lane-varying value
+    const uint64_t second = 0ull - (uint64_t)(lane >> 5);          // pair 1: all ones
+    const uint64_t bias = 0ull - (uint64_t)((lane >> 4) & 1);       // biases: all ones
+    const uint64_t sc0 = (uint64_t)a.scales[0], sc1 = (uint64_t)a.scales[NMAT - 1];
+    const uint64_t bi0 = (uint64_t)a.biases[0], bi1 = (uint64_t)a.biases[NMAT - 1];
+    const uint64_t m2 = (NMAT == 2) ? second : 0ull;
+    const uint64_t sc = sc0 ^ ((sc0 ^ sc1) & m2), bi = bi0 ^ ((bi0 ^ bi1) & m2);
+    const uint64_t arr = sc ^ ((sc ^ bi) & bias);
+    const uint32_t r0 = a.rowblk[0], r1 = a.rowblk[NBW - 1];
+    const uint32_t rb = r0 ^ ((r0 ^ r1) & ((NBW == 2) ? (uint32_t)second : 0u));
+    const size_t row = rb + (lane & 15);
+    const uint64_t off = 2ull * (row * (size_t)(a.K / kGroup) + kc / kGroup);
+    const void* src = reinterpret_cast<const void*>(dummy ? sc0 : arr + off);
+    dma4_to_lds(src, s_sb);
+}
+
+__device__ __forceinline__ uint8_t* stage_a(uint8_t* s, int st) { return s + st * kStageBytes; }
+__device__ __forceinline__ uint8_t* stage_b(uint8_t* s, int st, int wave) {
+    return s + st * kStageBytes + kABuf + wave * kBlkPerWave * kBBlk;
+}
+__device__ __forceinline__ uint8_t* stage_sb(uint8_t* s, int st, int wave) {
+    return s + st * kStageBytes + kABuf + kBBuf + wave * kSBWave;
+}
+
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -228,17 +341,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 // One K chunk of MFMAs over MB valid 16-row blocks (compile-time, so each step
 // is branch-free and the A-fragment reads of a step are issued together).
 template <int NMAT, int NBW, int MB>
-__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, int lane, const BRegs<NMAT, NBW>& br,
-                                          f32x4 (&acc)[MB][NMAT][NBW]) {
+__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const uint8_t* s_b, const uint8_t* s_sb,
+                                          int lane, f32x4 (&acc)[MB][NMAT][NBW]) {
     const int arow = lane & 15;
     const int agrp = (lane >> 4) * 4;      // logical 16-byte chunk of the lane's 32 k values
     const uint32_t magic = 0x64006400u;
+    const uint32_t* sb = reinterpret_cast<const uint32_t*>(s_sb);
+    const int half = (lane >> 5) * 16;     // lanes 32..63 take the chunk's odd group
     DqConst q[NMAT][NBW];
+    u32x4 codes[NMAT][NBW];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-            q[m][nb] = make_dq(bf16_to_f32(br.s[m][nb]), bf16_to_f32(br.b[m][nb]));
+        for (int nb = 0; nb < NBW; ++nb) {
+            const int p = m * NBW + nb;
+            const uint32_t sw = sb[p * 32 + arow], bw = sb[p * 32 + 16 + arow];
+            q[m][nb] = make_dq(bf16_to_f32((sw >> half) & 0xFFFFu), bf16_to_f32((bw >> half) & 0xFFFFu));
+            codes[m][nb] = *reinterpret_cast<const u32x4*>(
+                s_b + p * kBBlk + arow * kBRowBytes + (((lane >> 4) ^ (arow >> 2)) & 3) * 16);
+        }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int col = ((agrp + j) ^ arow) * 16;
@@ -251,8 +372,8 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, int lane, const BR
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
-                const uint32_t d = (j == 0) ? br.c[m][nb].x : (j == 1) ? br.c[m][nb].y
-                                 : (j == 2) ? br.c[m][nb].z : br.c[m][nb].w;
+                const uint32_t d = (j == 0) ? codes[m][nb].x : (j == 1) ? codes[m][nb].y
+                                 : (j == 2) ? codes[m][nb].z : codes[m][nb].w;
                 b[m][nb] = dequant8_mix(d, q[m][nb], magic);
             }
 #pragma unroll
@@ -266,52 +387,54 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, int lane, const BR
     }
 }
 
-// Issue the loads of one K chunk: the A DMA first, then B to registers.  The
-// order matters for the vmcnt accounting in tile_kloop.
+// Issue the copies of one K chunk into stage st: the wavefront's A rows (only if
+// any of its 16 rows is in the tile's MB row blocks), then B codes, then
+// scale/bias -- a fixed count per wavefront, dummy or not.
 template <int NMAT, int NBW>
-__device__ __forceinline__ void issue_chunk(BRegs<NMAT, NBW>& br, const BAddr<NMAT, NBW>& ba,
-                                            uint8_t* s_stage, int wave, int lane, const ASrc& src,
-                                            int kc, bool dummy) {
-    issue_a_dma(s_stage, wave, lane, src, 2 * kc, dummy);
-    load_b_chunk(br, ba, kc, dummy);
+__device__ __forceinline__ void issue_chunk(uint8_t* s_stage, int st, int wave, int lane,
+                                            const ASrc& src, const BAddr<NMAT, NBW>& ba, int kc,
+                                            bool dummy, bool has_a) {
+    if (has_a) issue_a_dma(stage_a(s_stage, st), wave, lane, src, 2 * kc, dummy);
+    issue_b_dma(stage_b(s_stage, st, wave), stage_sb(s_stage, st, wave), ba, lane, kc, dummy);
 }
 
-// Vector-memory instructions one issue_chunk emits per wavefront.
-template <int NMAT, int NBW>
-constexpr int kLoadsPerChunk = kDmaPerWave + 3 * NMAT * NBW;
-
-// K-loop with a D-stage ring: chunk c lives in LDS stage c % D and register set
-// c % D; chunks c+1 .. c+D-2 are in flight while chunk c is multiplied.  Every
-// iteration issues exactly one chunk (a dummy one past the end of K), so the
-// number of loads queued behind chunk c is always the same: its own B loads and
-// D-2 whole chunks.  Loads complete in order, so waiting until at most that many
-// are outstanding means chunk c has landed.
-template <int NMAT, int NBW, int D, int MB>
-__device__ __forceinline__ void tile_kloop(uint8_t* s_a, int K, int wave, int lane,
+// K-loop over the ring.  Every iteration issues exactly one chunk (a dummy one
+// past the end of K), so the copies queued behind chunk c at its wait are always
+// the kStages-2 whole chunks issued after it.  Copies complete in order, so
+// waiting until at most that many are outstanding means this wavefront's part of
+// chunk c has landed; the barrier then makes every wavefront's part visible and
+// frees the stage read in the previous iteration.
+template <int NMAT, int NBW, int MB>
+__device__ __forceinline__ void tile_kloop(uint8_t* s_stage, int K, int wave, int lane,
                                            const ASrc& src, const BAddr<NMAT, NBW>& ba,
                                            f32x4 (&acc)[MB][NMAT][NBW]) {
-    static_assert(D >= 2 && D <= 4, "pipeline depth");
-    constexpr int kBehind = 3 * NMAT * NBW + (D - 2) * kLoadsPerChunk<NMAT, NBW>;
+    constexpr int D = kStages;
+    static_assert(D >= 2, "pipeline depth");
+    constexpr int kBehind = (D - 2) * kLoadsPerChunk;                    // waves copying A rows
+    constexpr int kBehindNoA = (D - 2) * (kLoadsPerChunk - kDmaPerWave);  // waves that do not
     static_assert(kBehind < 64, "pipeline too deep for vmcnt");
+    const bool has_a = wave < MB;          // wave w copies rows [16 w, 16 w + 16)
     const int nch = K / kKC;
-    BRegs<NMAT, NBW> br[D];
 #pragma unroll
     for (int st = 0; st < D - 1; ++st)
-        issue_chunk(br[st], ba, s_a + st * kABuf, wave, lane, src, st * kKC, st >= nch);
+        issue_chunk(s_stage, st, wave, lane, src, ba, st * kKC, st >= nch, has_a);
     const int nit = (nch + D - 1) / D * D;
     for (int base = 0; base < nit; base += D) {
 #pragma unroll
         for (int st = 0; st < D; ++st) {
             const int c = base + st;
-            wait_vmcnt<kBehind>();
+            if (has_a) wait_vmcnt<kBehind>();
+            else wait_vmcnt<kBehindNoA>();
             __syncthreads();       // chunk c visible to all; chunk c-1's stage is free
             const int nxt = (st + D - 1) % D;
-            issue_chunk(br[nxt], ba, s_a + nxt * kABuf, wave, lane, src, (c + D - 1) * kKC,
-                        c + D - 1 >= nch);
-            if (c < nch) mma_chunk<NMAT, NBW, MB>(s_a + st * kABuf, lane, br[st], acc);
+            issue_chunk(s_stage, nxt, wave, lane, src, ba, (c + D - 1) * kKC, c + D - 1 >= nch,
+                        has_a);
+            if (c < nch)
+                mma_chunk<NMAT, NBW, MB>(stage_a(s_stage, st), stage_b(s_stage, st, wave),
+                                         stage_sb(s_stage, st, wave), lane, acc);
         }
     }
-    wait_vmcnt<0>();               // drain the dummy loads
+    wait_vmcnt<0>();               // drain the dummy copies
     __syncthreads();               // all stages free for the next tile
 }
 
@@ -319,7 +442,7 @@ __device__ __forceinline__ void tile_kloop(uint8_t* s_a, int K, int wave, int la
 // Per-tile bodies, specialised on the number MB of valid 16-row blocks
 // ---------------------------------------------------------------------------
 template <int NBW, int MB>
-__device__ __forceinline__ void gateup_tile(uint8_t* s_a, int H, int I, int wave, int lane,
+__device__ __forceinline__ void gateup_tile(uint8_t* s_stage, int H, int I, int wave, int lane,
                                             const ASrc& src, const BAddr<2, NBW>& ba, int rows,
                                             int rowbase, int nbase, uint16_t* __restrict__ h) {
     f32x4 acc[MB][2][NBW];
@@ -329,7 +452,7 @@ __device__ __forceinline__ void gateup_tile(uint8_t* s_a, int H, int I, int wave
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) acc[mb][m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    tile_kloop<2, NBW, kStages, MB>(s_a, H, wave, lane, src, ba, acc);
+    tile_kloop<2, NBW, MB>(s_stage, H, wave, lane, src, ba, acc);
     // epilogue: h = silu(gate) * up, bf16, expert-sorted rows
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -348,7 +471,7 @@ __device__ __forceinline__ void gateup_tile(uint8_t* s_a, int H, int I, int wave
 }
 
 template <int NBW, int MB>
-__device__ __forceinline__ void down_tile(uint8_t* s_a, int H, int I, int wave, int lane,
+__device__ __forceinline__ void down_tile(uint8_t* s_stage, int H, int I, int wave, int lane,
                                           const ASrc& src, const BAddr<1, NBW>& ba, int rows,
                                           int nbase, const int* s_tok, const float* s_w,
                                           float* __restrict__ accum) {
@@ -357,7 +480,7 @@ __device__ __forceinline__ void down_tile(uint8_t* s_a, int H, int I, int wave, 
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) acc[mb][0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    tile_kloop<1, NBW, kStages, MB>(s_a, I, wave, lane, src, ba, acc);
+    tile_kloop<1, NBW, MB>(s_stage, I, wave, lane, src, ba, acc);
     // epilogue: routing-weighted add into the token's fp32 accumulator row
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -380,11 +503,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
     const uint16_t* __restrict__ x, int T, int H, int I, int E, int k,
     W4Set routed, W4Set shared, int has_shared,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-    uint16_t* __restrict__ h, float* __restrict__ acc_zero, long acc_elems) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_a[kStages * kABuf];
+    uint16_t* __restrict__ h, float* __restrict__ acc_zero, long acc_elems, uint32_t* ctl) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages * kStageBytes];
     __shared__ int s_pre[kMaxSeg + 1];
     __shared__ int s_tmp[kThreads];
     __shared__ int s_tok[kBM];
+    __shared__ int s_next;
 
     // clear the fp32 output accumulator for the down kernel
     for (long i = ((long)blockIdx.x * kThreads + threadIdx.x) * 4; i < acc_elems;
@@ -395,29 +519,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
     const int n_mt = build_mtile_prefix(offsets, E, T, k, has_shared, s_pre, s_tmp);
     constexpr int BN = kWaves * 16 * NBW;
     const int NT = I / BN;
-    const int total = ((n_mt + 7) / 8) * 8 * NT;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false};    // thread 0's scheduling state
 
-    for (int i = blockIdx.x; i < total; i += gridDim.x) {
+    if (threadIdx.x == 0) s_next = grab_tile(ctl, n_mt, NT, tq.q, tq.empty);
+    __syncthreads();
+    for (int i = s_next; i >= 0; i = s_next) {
         int mt, nt;
         tile_coords(i, NT, mt, nt);
-        if (mt >= n_mt) continue;
         const TileCtx c = locate(mt, s_pre, nseg, E, T, k, offsets);
         const W4Set& Wset = c.shared ? shared : routed;
         __syncthreads();                 // previous tile's readers are done
         for (int r = threadIdx.x; r < c.rows; r += kThreads)
             s_tok[r] = c.shared ? (c.m0 + r) : min(max(perm[c.hbase + c.m0 + r], 0), T * k - 1) / k;
         __syncthreads();
+        if (threadIdx.x == 0) tq.prefetch(ctl);
         const int nbase = nt * BN + wave * 16 * NBW;
 
         BAddr<2, NBW> ba;
         ba.codes[0] = Wset.gate.codes; ba.scales[0] = Wset.gate.scales; ba.biases[0] = Wset.gate.biases;
         ba.codes[1] = Wset.up.codes;   ba.scales[1] = Wset.up.scales;   ba.biases[1] = Wset.up.biases;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) ba.row[nb] = (uint32_t)(c.e * I + nbase + nb * 16 + (lane & 15));
+        for (int nb = 0; nb < NBW; ++nb) ba.rowblk[nb] = (uint32_t)(c.e * I + nbase + nb * 16);
         ba.K = H;
-        ba.lane = lane;
         ASrc src;
         src.base = reinterpret_cast<const uint8_t*>(x);
         src.row_bytes = (size_t)H * 2;
@@ -427,16 +552,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
 
         const int rowbase = c.hbase + c.m0;
         switch ((c.rows + 15) >> 4) {
-            case 1: gateup_tile<NBW, 1>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 2: gateup_tile<NBW, 2>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 3: gateup_tile<NBW, 3>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 4: gateup_tile<NBW, 4>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 5: gateup_tile<NBW, 5>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 6: gateup_tile<NBW, 6>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 7: gateup_tile<NBW, 7>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            default: gateup_tile<NBW, 8>(s_a, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 1: gateup_tile<NBW, 1>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 2: gateup_tile<NBW, 2>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 3: gateup_tile<NBW, 3>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 4: gateup_tile<NBW, 4>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 5: gateup_tile<NBW, 5>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 6: gateup_tile<NBW, 6>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 7: gateup_tile<NBW, 7>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            default: gateup_tile<NBW, 8>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
         }
+        if (threadIdx.x == 0) s_next = tq.next(ctl, n_mt, NT);
+        __syncthreads();
     }
+    release_queues(ctl);
 }
 
 // ---------------------------------------------------------------------------
@@ -446,25 +574,28 @@ template <int NBW>
 __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
     int T, int H, int I, int E, int k, W4Set routed, W4Set shared, int has_shared,
     const float* __restrict__ topk_w, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm, const uint16_t* __restrict__ h, float* __restrict__ accum) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_a[kStages * kABuf];
+    const int32_t* __restrict__ perm, const uint16_t* __restrict__ h, float* __restrict__ accum,
+    uint32_t* ctl) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages * kStageBytes];
     __shared__ int s_pre[kMaxSeg + 1];
     __shared__ int s_tmp[kThreads];
     __shared__ int s_tok[kBM];
     __shared__ float s_w[kBM];
+    __shared__ int s_next;
 
     const int nseg = E + (has_shared ? 1 : 0);
     const int n_mt = build_mtile_prefix(offsets, E, T, k, has_shared, s_pre, s_tmp);
     constexpr int BN = kWaves * 16 * NBW;
     const int NT = H / BN;
-    const int total = ((n_mt + 7) / 8) * 8 * NT;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false};    // thread 0's scheduling state
 
-    for (int i = blockIdx.x; i < total; i += gridDim.x) {
+    if (threadIdx.x == 0) s_next = grab_tile(ctl, n_mt, NT, tq.q, tq.empty);
+    __syncthreads();
+    for (int i = s_next; i >= 0; i = s_next) {
         int mt, nt;
         tile_coords(i, NT, mt, nt);
-        if (mt >= n_mt) continue;
         const TileCtx c = locate(mt, s_pre, nseg, E, T, k, offsets);
         const W4Set& Wset = c.shared ? shared : routed;
         __syncthreads();
@@ -476,13 +607,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
                 s_w[r] = topk_w[f];
             }
         }
+        __syncthreads();
+        if (threadIdx.x == 0) tq.prefetch(ctl);
         const int nbase = nt * BN + wave * 16 * NBW;
         BAddr<1, NBW> ba;
         ba.codes[0] = Wset.down.codes; ba.scales[0] = Wset.down.scales; ba.biases[0] = Wset.down.biases;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) ba.row[nb] = (uint32_t)(c.e * H + nbase + nb * 16 + (lane & 15));
+        for (int nb = 0; nb < NBW; ++nb) ba.rowblk[nb] = (uint32_t)(c.e * H + nbase + nb * 16);
         ba.K = I;
-        ba.lane = lane;
         ASrc src;
         src.base = reinterpret_cast<const uint8_t*>(h + (size_t)(c.hbase + c.m0) * I);
         src.row_bytes = (size_t)I * 2;
@@ -491,16 +623,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
             src.rowidx[q] = min(wave * kRowsPerWaveDma + q * 4 + (lane >> 4), c.rows - 1);
 
         switch ((c.rows + 15) >> 4) {
-            case 1: down_tile<NBW, 1>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 2: down_tile<NBW, 2>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 3: down_tile<NBW, 3>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 4: down_tile<NBW, 4>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 5: down_tile<NBW, 5>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 6: down_tile<NBW, 6>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 7: down_tile<NBW, 7>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            default: down_tile<NBW, 8>(s_a, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 1: down_tile<NBW, 1>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 2: down_tile<NBW, 2>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 3: down_tile<NBW, 3>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 4: down_tile<NBW, 4>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 5: down_tile<NBW, 5>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 6: down_tile<NBW, 6>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 7: down_tile<NBW, 7>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            default: down_tile<NBW, 8>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
         }
+        if (threadIdx.x == 0) s_next = tq.next(ctl, n_mt, NT);
+        __syncthreads();
     }
+    release_queues(ctl);
 }
 
 __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ acc,
@@ -542,14 +677,14 @@ hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTi
     tm.before();
     hipLaunchKernelGGL(k_grouped_gateup<NBW_GU>, dim3(g_gu), dim3(kThreads), 0, st, a.x, a.T,
                        a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.offsets, a.perm,
-                       a.ws_h, a.ws_acc, acc_elems);
+                       a.ws_h, a.ws_acc, acc_elems, a.ctl);
     tm.after();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
     hipLaunchKernelGGL(k_grouped_down<NBW_DN>, dim3(g_dn), dim3(kThreads), 0, st, a.T, a.H, a.I,
                        a.E, a.k, a.routed, a.shared, a.has_shared, a.topk_w, a.offsets, a.perm,
-                       a.ws_h, a.ws_acc);
+                       a.ws_h, a.ws_acc, a.ctl);
     tm.after();
     err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -47,7 +47,14 @@ struct ForwardArgs {
     uint16_t* out;           // [T][H] bf16
     uint16_t* ws_h;          // [T*k + T][I] bf16: expert-sorted rows, then shared rows
     float* ws_acc;           // [T][H] fp32 (grouped path)
+    uint32_t* ctl;           // workspace control block (zero between calls)
 };
+
+// Control block words (the block is kCtlWords words, zero between calls).
+constexpr int kCtlTicket = 0;            // one-launch router: arrival ticket
+constexpr int kCtlQueue = 32;            // grouped GEMMs: 8 per-XCD tile queues, 128 B apart
+constexpr int kCtlQueueStride = 32;
+constexpr int kCtlExit = kCtlQueue + 8 * kCtlQueueStride;   // grouped GEMMs: exit ticket
 
 // Optional per-kernel timing: events[2i] / events[2i+1] are recorded on the launch
 // stream before / after the i-th kernel of a call (while capacity allows).

@@ -14,7 +14,7 @@ namespace {
 thread_local std::string g_last_error;
 
 constexpr size_t kAlign = 256;
-constexpr size_t kCtrlBytes = 256;
+constexpr size_t kCtrlBytes = MOE_W4_CONTROL_BYTES;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -62,7 +62,7 @@ int launch_status(hipError_t err) {
 
 bool mat_ok(const moe_w4_mat& m, int* status) {
     if (!m.codes || !m.scales || !m.biases) { *status = MOE_W4_ERR_NULL; return false; }
-    if (!aligned(m.codes, 16) || !aligned(m.scales, 2) || !aligned(m.biases, 2)) {
+    if (!aligned(m.codes, 16) || !aligned(m.scales, 4) || !aligned(m.biases, 4)) {
         *status = MOE_W4_ERR_ALIGN;
         return false;
     }
@@ -174,6 +174,7 @@ hipError_t run_forward(const moe_w4_dims* dims, const void* x, const moe_w4_weig
     a.out = static_cast<uint16_t*>(out);
     a.ws_h = reinterpret_cast<uint16_t*>(ws + L.h);
     a.ws_acc = reinterpret_cast<float*>(ws + L.acc);
+    a.ctl = reinterpret_cast<uint32_t*>(ws);
     return (a.T <= MOE_W4_DECODE_MAX_T) ? moe_w4::launch_forward_decode(a, stream, tm)
                                         : moe_w4::launch_forward_grouped(a, stream, tm);
 }

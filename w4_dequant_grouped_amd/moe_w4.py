@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_w4.so")
 
 MOE_W4_DECODE_MAX_T = 5
+MOE_W4_CONTROL_BYTES = 4096
 
 
 class moe_w4_dims(ctypes.Structure):
