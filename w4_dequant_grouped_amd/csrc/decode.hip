@@ -23,6 +23,7 @@
 #include "device.h"
 #include "gemv.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe_w4 {
 
@@ -126,6 +127,68 @@ __device__ __forceinline__ Slot find_slot(const int32_t* __restrict__ offsets, i
 constexpr int kGuRowsPerWave = 4;
 constexpr int kGuRowsPerBlock = 4 * kGuRowsPerWave;
 
+// Rows n0 .. n0+3 of gate and up of expert e, for the cnt token rows tok[0..cnt):
+// h[hrow0 + i][n0 + r] = silu(gate . x) * (up . x), bf16.  One wavefront.
+template <int TMAX>
+__device__ __forceinline__ void gateup_rows(const uint16_t* __restrict__ x, int H, int I,
+                                            const W4& G, const W4& U, int e, int n0, int cnt,
+                                            const int (&tok)[TMAX], int hrow0,
+                                            uint16_t* __restrict__ h, int lane) {
+    const int ngroups = H / kGroup;
+    const int nchunks = H / 32;
+    float ag[kGuRowsPerWave][TMAX], au[kGuRowsPerWave][TMAX];
+#pragma unroll
+    for (int r = 0; r < kGuRowsPerWave; ++r)
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) { ag[r][i] = 0.f; au[r][i] = 0.f; }
+
+    for (int c = lane; c < nchunks; c += kWave) {
+        u32x4 cg[kGuRowsPerWave], cu[kGuRowsPerWave];
+        uint32_t sg[kGuRowsPerWave], bg[kGuRowsPerWave], su[kGuRowsPerWave], bu[kGuRowsPerWave];
+        u32x4 xv[TMAX][4];
+#pragma unroll
+        for (int r = 0; r < kGuRowsPerWave; ++r) {
+            const size_t row = (size_t)e * I + (n0 + r);
+            cg[r] = load_u32x4(G.codes + row * (H / 2) + c * 16);
+            cu[r] = load_u32x4(U.codes + row * (H / 2) + c * 16);
+            const size_t gi = row * ngroups + (c >> 1);
+            sg[r] = G.scales[gi];
+            bg[r] = G.biases[gi];
+            su[r] = U.scales[gi];
+            bu[r] = U.biases[gi];
+        }
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i)
+            if (i < cnt) load64(x + (size_t)tok[i] * H + c * 32, xv[i]);
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) {
+            if (i >= cnt) break;
+            uint32_t xi[16];
+            float xs;
+            interleave32(xv[i], xi, xs);
+#pragma unroll
+            for (int r = 0; r < kGuRowsPerWave; ++r) {
+                const float s0 = bf16_to_f32(sg[r]), s1 = bf16_to_f32(su[r]);
+                const float pg = dot32_magic(cg[r], xi);
+                const float pu = dot32_magic(cu[r], xi);
+                ag[r][i] += fmaf(s0, pg, (bf16_to_f32(bg[r]) - 128.0f * s0) * xs);
+                au[r][i] += fmaf(s1, pu, (bf16_to_f32(bu[r]) - 128.0f * s1) * xs);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TMAX; ++i) {
+        if (i >= cnt) break;
+        const int hrow = hrow0 + i;
+#pragma unroll
+        for (int r = 0; r < kGuRowsPerWave; ++r) {
+            const float g = wave_sum(ag[r][i]);
+            const float u = wave_sum(au[r][i]);
+            if (lane == r) h[(size_t)hrow * I + n0 + r] = (uint16_t)f32_to_bf16(silu(g) * u);
+        }
+    }
+}
+
 template <int TMAX>
 __global__ __launch_bounds__(256) void k_decode_gateup(
     const uint16_t* __restrict__ x, int T, int H, int I, int E, int k,
@@ -160,61 +223,8 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
         if (TMAX > 1 && i < sl.cnt)
             tok[i] = is_shared ? i : min(max(perm[sl.off + i], 0), T * k - 1) / k;
     }
-
     const int n0 = blockIdx.y * kGuRowsPerBlock + wave * kGuRowsPerWave;
-    const int ngroups = H / kGroup;
-    const int nchunks = H / 32;
-    float ag[kGuRowsPerWave][TMAX], au[kGuRowsPerWave][TMAX];
-#pragma unroll
-    for (int r = 0; r < kGuRowsPerWave; ++r)
-#pragma unroll
-        for (int i = 0; i < TMAX; ++i) { ag[r][i] = 0.f; au[r][i] = 0.f; }
-
-    for (int c = lane; c < nchunks; c += kWave) {
-        u32x4 cg[kGuRowsPerWave], cu[kGuRowsPerWave];
-        uint32_t sg[kGuRowsPerWave], bg[kGuRowsPerWave], su[kGuRowsPerWave], bu[kGuRowsPerWave];
-        u32x4 xv[TMAX][4];
-#pragma unroll
-        for (int r = 0; r < kGuRowsPerWave; ++r) {
-            const size_t row = (size_t)e * I + (n0 + r);
-            cg[r] = load_u32x4(G.codes + row * (H / 2) + c * 16);
-            cu[r] = load_u32x4(U.codes + row * (H / 2) + c * 16);
-            const size_t gi = row * ngroups + (c >> 1);
-            sg[r] = G.scales[gi];
-            bg[r] = G.biases[gi];
-            su[r] = U.scales[gi];
-            bu[r] = U.biases[gi];
-        }
-#pragma unroll
-        for (int i = 0; i < TMAX; ++i)
-            if (i < sl.cnt) load64(x + (size_t)tok[i] * H + c * 32, xv[i]);
-#pragma unroll
-        for (int i = 0; i < TMAX; ++i) {
-            if (i >= sl.cnt) break;
-            uint32_t xi[16];
-            float xs;
-            interleave32(xv[i], xi, xs);
-#pragma unroll
-            for (int r = 0; r < kGuRowsPerWave; ++r) {
-                const float s0 = bf16_to_f32(sg[r]), s1 = bf16_to_f32(su[r]);
-                const float pg = dot32_magic(cg[r], xi);
-                const float pu = dot32_magic(cu[r], xi);
-                ag[r][i] += fmaf(s0, pg, (bf16_to_f32(bg[r]) - 128.0f * s0) * xs);
-                au[r][i] += fmaf(s1, pu, (bf16_to_f32(bu[r]) - 128.0f * s1) * xs);
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < TMAX; ++i) {
-        if (i >= sl.cnt) break;
-        const int hrow = sl.off + i;
-#pragma unroll
-        for (int r = 0; r < kGuRowsPerWave; ++r) {
-            const float g = wave_sum(ag[r][i]);
-            const float u = wave_sum(au[r][i]);
-            if (lane == r) h[(size_t)hrow * I + n0 + r] = (uint16_t)f32_to_bf16(silu(g) * u);
-        }
-    }
+    gateup_rows<TMAX>(x, H, I, G, U, e, n0, sl.cnt, tok, sl.off, h, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -223,6 +233,8 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
 constexpr int kDnRowsPerWave = 2;
 constexpr int kDnRowsPerBlock = 4 * kDnRowsPerWave;
 constexpr int kDnUnroll = 3;     // (slot, chunk) items per lane whose loads are issued together
+constexpr int kDnLdsRows = 48;   // h staged in LDS when T*k + T <= 48 rows of I <= 512
+constexpr int kDnLdsI = 512;
 
 template <int TMAX>
 __global__ __launch_bounds__(256) void k_decode_down(
@@ -232,11 +244,22 @@ __global__ __launch_bounds__(256) void k_decode_down(
     uint16_t* __restrict__ out) {
     __shared__ Slot s_slots[kMaxSlots];
     __shared__ int s_n;
+    __shared__ __attribute__((aligned(16))) uint16_t s_h[kDnLdsRows * kDnLdsI];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    // h is dense (rows 0 .. T*k + T - 1): stage it in LDS while wavefront 0 reads
+    // the routing, so that no h read waits behind the weight reads later
+    const int hrows = T * k + T;
+    const bool h_in_lds = hrows <= kDnLdsRows && I <= kDnLdsI;
+    if (h_in_lds) {
+        const int n16 = hrows * I / 8;
+        for (int i = threadIdx.x; i < n16; i += blockDim.x)
+            reinterpret_cast<u32x4*>(s_h)[i] = reinterpret_cast<const u32x4*>(h)[i];
+    }
     if (wave == 0) build_slots(offsets, E, T, k, has_shared, s_slots, &s_n, lane);
     __syncthreads();
     const int nslots = s_n;
+
     const int n0 = blockIdx.x * kDnRowsPerBlock + wave * kDnRowsPerWave;
     const int cpr = I / 32;            // 32-code chunks per down row
     const int ngroups = I / kGroup;
@@ -283,7 +306,13 @@ __global__ __launch_bounds__(256) void k_decode_down(
                 if (is_shared) { t = i; w = 1.0f; }
                 else { const int f = min(max(perm[hrow], 0), T * k - 1); t = f / k; w = topk_w[f]; }
                 u32x4 hv[4];
-                load64(h + (size_t)hrow * I + cc[u] * 32, hv);
+                if (h_in_lds) {
+                    const u32x4* q = reinterpret_cast<const u32x4*>(s_h + (size_t)hrow * I + cc[u] * 32);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) hv[b] = q[b];
+                } else {
+                    load64(h + (size_t)hrow * I + cc[u] * 32, hv);
+                }
                 uint32_t xi[16];
                 float hs;
                 interleave32(hv, xi, hs);
@@ -324,6 +353,218 @@ static hipError_t decode_t(const ForwardArgs& a, hipStream_t st, KernelTimer& tm
                        a.perm, a.ws_h, a.out);
     tm.after();
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Route + forward of decode rows in three launches (moe_w4_block)
+// ---------------------------------------------------------------------------
+// Launch 1: router logits (a wavefront per expert) and the shared expert's
+//   gate/up -- both need only x, so their bytes stream together.
+// Launch 2: every workgroup reads the T x E logits and repeats the (cheap)
+//   top-k and grouping in LDS; workgroup (0, 0) writes the routing outputs.
+//   Workgroup (s, y) then runs rows 16y .. 16y+15 of gate/up of the s-th
+//   selected expert (ascending id).  There is no "last workgroup" hand-off
+//   inside the router: the kernel boundary is the only grid-wide dependency
+//   between the logits and the expert weights.
+// Launch 3: k_decode_down over the shared expert and the selected experts.
+
+template <int TMAX>
+__global__ __launch_bounds__(256) void k_decode_logits_shared(DecodeBlockArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int T = a.T, H = a.H, E = a.E;
+    const int nlog = (E + 3) / 4;
+    if ((int)blockIdx.x < nlog) {
+        const int e = blockIdx.x * 4 + wave;
+        if (e >= E) return;
+        float acc[TMAX];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) acc[t] = 0.f;
+        const float* wrow = a.Wr + (size_t)e * H;
+        for (int h0 = 0; h0 < H; h0 += kWave * 4 * 8) {
+            float4 wv[8];
+            u32x2 xv[8][TMAX];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int hh = h0 + (u * kWave + lane) * 4;
+                const bool ok = hh < H;
+                wv[u] = ok ? *reinterpret_cast<const float4*>(wrow + hh) : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t)
+                    xv[u][t] = (ok && t < T) ? *reinterpret_cast<const u32x2*>(a.x + (size_t)t * H + hh)
+                                             : u32x2{0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t) {
+                    acc[t] = fmaf(bf16lo(xv[u][t].x), wv[u].x, acc[t]);
+                    acc[t] = fmaf(bf16hi(xv[u][t].x), wv[u].y, acc[t]);
+                    acc[t] = fmaf(bf16lo(xv[u][t].y), wv[u].z, acc[t]);
+                    acc[t] = fmaf(bf16hi(xv[u][t].y), wv[u].w, acc[t]);
+                }
+        }
+        const float bias = a.br ? a.br[e] : 0.f;
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if (t >= T) break;
+            const float sum = wave_sum(acc[t]);
+            if (lane == 0) a.logits[t * E + e] = sum + bias;
+        }
+    } else {
+        int tok[TMAX];
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) tok[i] = i;
+        const int n0 = (blockIdx.x - nlog) * kGuRowsPerBlock + wave * kGuRowsPerWave;
+        gateup_rows<TMAX>(a.x, H, a.I, a.shared.gate, a.shared.up, 0, n0, T, tok, T * a.k, a.h, lane);
+    }
+}
+
+template <int TMAX, int EPL>
+__global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) {
+    constexpr int N = TMAX * kMaxTopK;            // (token, slot) entries at most
+    constexpr int EPW = (N + kWave - 1) / kWave;  // entries per lane in the grouping
+    __shared__ int32_t s_ids[N];
+    __shared__ float s_w[N];
+    __shared__ int s_ptok[N], s_pflat[N];
+    __shared__ int s_u[N], s_uoff[N], s_ucnt[N];
+    __shared__ int s_nu;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int T = a.T, E = a.E, k = a.k;
+    const int n = T * k;
+
+    // top-k of every token: wavefront t
+    for (int t = wave; t < T; t += 4) {
+        float vals[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + kWave * j;
+            vals[j] = (e < E) ? a.logits[t * E + e] : -INFINITY;
+        }
+        wave_topk_select<EPL>(vals, E, k, lane, s_ids + t * k, s_w + t * k);
+    }
+    __syncthreads();
+    // grouping by wavefront 0, in registers: entry i = lane + 64 j; its position
+    // in (expert, token) order is #{entries of lower experts} + #{entries of the
+    // same expert from earlier tokens}; the first entry of each expert also gets
+    // the expert's rank among the selected experts
+    if (wave == 0) {
+        int ee[EPW], below[EPW], before[EPW], cnt[EPW], rank[EPW];
+#pragma unroll
+        for (int j = 0; j < EPW; ++j) {
+            const int i = lane + kWave * j;
+            ee[j] = (i < n) ? s_ids[i] : 0x7FFFFFFF;
+            below[j] = before[j] = cnt[j] = rank[j] = 0;
+        }
+        for (int q = 0; q < n; ++q) {
+            const int eq = __builtin_amdgcn_readlane(ee[0], q & (kWave - 1));
+            const int eq1 = (EPW > 1) ? __builtin_amdgcn_readlane(ee[EPW - 1], q & (kWave - 1)) : eq;
+            const int e_q = (q < kWave) ? eq : eq1;
+            const int tq = q / k;
+#pragma unroll
+            for (int j = 0; j < EPW; ++j) {
+                const int t = (lane + kWave * j) / k;
+                below[j] += (e_q < ee[j]) ? 1 : 0;
+                before[j] += (e_q == ee[j] && tq < t) ? 1 : 0;
+                cnt[j] += (e_q == ee[j]) ? 1 : 0;
+            }
+        }
+        bool first[EPW];
+#pragma unroll
+        for (int j = 0; j < EPW; ++j) first[j] = (lane + kWave * j < n) && before[j] == 0;
+        for (int q = 0; q < n; ++q) {
+            const int src = q & (kWave - 1);
+            const bool hi = q >= kWave;
+            const int fq = hi ? __builtin_amdgcn_readlane((int)first[EPW - 1], src)
+                              : __builtin_amdgcn_readlane((int)first[0], src);
+            const int e_q = hi ? __builtin_amdgcn_readlane(ee[EPW - 1], src)
+                               : __builtin_amdgcn_readlane(ee[0], src);
+#pragma unroll
+            for (int j = 0; j < EPW; ++j) rank[j] += (fq && e_q < ee[j]) ? 1 : 0;
+        }
+        int nu = 0;
+#pragma unroll
+        for (int j = 0; j < EPW; ++j) {
+            const int i = lane + kWave * j;
+            if (i < n) {
+                const int p = below[j] + before[j];
+                s_ptok[p] = i / k;
+                s_pflat[p] = i;
+                if (first[j]) {
+                    s_u[rank[j]] = ee[j];
+                    s_uoff[rank[j]] = p;
+                    s_ucnt[rank[j]] = cnt[j];
+                }
+            }
+            nu += __builtin_popcountll(__builtin_amdgcn_ballot_w64(first[j]));
+        }
+        if (lane == 0) s_nu = nu;
+    }
+    __syncthreads();
+    const int nu = s_nu;
+    if (blockIdx.x == 0 && blockIdx.y == 0) {     // the routing outputs of the call
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            a.ids[i] = s_ids[i];
+            a.tw[i] = s_w[i];
+            a.perm[i] = s_pflat[i];
+        }
+        for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+            int off = 0, cnt = 0;
+            for (int u = 0; u < nu; ++u) {
+                off += (s_u[u] < e) ? s_ucnt[u] : 0;
+                cnt = (s_u[u] == e) ? s_ucnt[u] : cnt;
+            }
+            a.offsets[e] = off;
+            if (e < E) a.counts[e] = cnt;
+        }
+    }
+    const int slot = blockIdx.x;
+    if (slot >= nu) return;
+    const int cnt = min(s_ucnt[slot], T);
+    int tok[TMAX];
+#pragma unroll
+    for (int i = 0; i < TMAX; ++i) tok[i] = s_ptok[s_uoff[slot] + min(i, cnt - 1)];
+    const int n0 = blockIdx.y * kGuRowsPerBlock + wave * kGuRowsPerWave;
+    gateup_rows<TMAX>(a.x, a.H, a.I, a.routed.gate, a.routed.up, s_u[slot], n0, cnt, tok,
+                      s_uoff[slot], a.h, lane);
+}
+
+template <int TMAX, int EPL>
+static hipError_t block_decode_t(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm) {
+    const int nlog = (a.E + 3) / 4;
+    const int nsh = a.has_shared ? a.I / kGuRowsPerBlock : 0;
+    tm.before();
+    hipLaunchKernelGGL(k_decode_logits_shared<TMAX>, dim3(nlog + nsh), dim3(256), 0, st, a);
+    tm.after();
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    tm.before();
+    hipLaunchKernelGGL((k_decode_route_gateup<TMAX, EPL>), dim3(min(a.E, a.T * a.k), a.I / kGuRowsPerBlock),
+                       dim3(256), 0, st, a);
+    tm.after();
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    tm.before();
+    hipLaunchKernelGGL(k_decode_down<TMAX>, dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T,
+                       a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.tw, a.offsets,
+                       a.perm, a.h, a.out);
+    tm.after();
+    return hipGetLastError();
+}
+
+template <int TMAX>
+static hipError_t block_decode_e(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm) {
+    if (a.E <= 256) return block_decode_t<TMAX, 4>(a, st, tm);
+    if (a.E <= 512) return block_decode_t<TMAX, 8>(a, st, tm);
+    return block_decode_t<TMAX, 16>(a, st, tm);
+}
+
+hipError_t launch_block_decode(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm) {
+    if (a.T <= 1) return block_decode_e<1>(a, st, tm);
+    if (a.T <= 2) return block_decode_e<2>(a, st, tm);
+    if (a.T <= 4) return block_decode_e<4>(a, st, tm);
+    return block_decode_e<8>(a, st, tm);
 }
 
 hipError_t launch_forward_decode(const ForwardArgs& a, hipStream_t st, KernelTimer& tm) {

@@ -56,6 +56,24 @@ constexpr int kCtlQueue = 32;            // grouped GEMMs: 8 per-XCD tile queues
 constexpr int kCtlQueueStride = 32;
 constexpr int kCtlExit = kCtlQueue + 8 * kCtlQueueStride;   // grouped GEMMs: exit ticket
 
+struct DecodeBlockArgs {     // route + forward of decode rows (T <= kDecodeMaxT)
+    const uint16_t* x;
+    const float* Wr;
+    const float* br;
+    int T, H, I, E, k;
+    W4Set routed;
+    W4Set shared;
+    int has_shared;
+    int32_t* ids;            // routing outputs, as moe_w4_route writes them
+    float* tw;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    uint16_t* out;           // [T][H] bf16
+    float* logits;           // [T][E] workspace
+    uint16_t* h;             // [T*k + T][I] bf16 workspace
+};
+
 // Optional per-kernel timing: events[2i] / events[2i+1] are recorded on the launch
 // stream before / after the i-th kernel of a call (while capacity allows).
 struct KernelTimer {
@@ -76,5 +94,6 @@ hipError_t launch_route_small(const RouteArgs& a, hipStream_t st, KernelTimer& t
 hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_forward_decode(const ForwardArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTimer& tm);
+hipError_t launch_block_decode(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm);
 
 }  // namespace moe_w4

@@ -257,6 +257,33 @@ int moe_w4_block_timed(const moe_w4_dims* dims, const void* x, const float* rout
     if (st != MOE_W4_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     moe_w4::KernelTimer tm = make_timer(events, capacity, stream);
+    if (dims->T <= MOE_W4_DECODE_MAX_T) {
+        const Layout L = layout(dims);
+        uint8_t* ws = static_cast<uint8_t*>(workspace);
+        moe_w4::DecodeBlockArgs a;
+        a.x = static_cast<const uint16_t*>(x);
+        a.Wr = router_w;
+        a.br = router_b;
+        a.T = dims->T;
+        a.H = dims->H;
+        a.I = dims->I;
+        a.E = dims->E;
+        a.k = dims->top_k;
+        a.routed = to_set(routed);
+        a.has_shared = shared ? 1 : 0;
+        a.shared = shared ? to_set(shared) : a.routed;
+        a.ids = topk_ids;
+        a.tw = topk_w;
+        a.counts = expert_counts;
+        a.offsets = expert_offsets;
+        a.perm = perm;
+        a.out = static_cast<uint16_t*>(out);
+        a.logits = reinterpret_cast<float*>(ws + L.logits);
+        a.h = reinterpret_cast<uint16_t*>(ws + L.h);
+        const hipError_t err = moe_w4::launch_block_decode(a, stream, tm);
+        if (n_kernels) *n_kernels = tm.count;
+        return launch_status(err);
+    }
     hipError_t err = run_route(dims, x, router_w, router_b, topk_ids, topk_w, expert_counts,
                                expert_offsets, perm, workspace, stream, tm);
     if (err == hipSuccess)

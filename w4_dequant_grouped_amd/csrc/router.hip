@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kSmallRouteThreads) void k_route_small(
                                                   __HIP_MEMORY_SCOPE_AGENT)
                               : -INFINITY;
         }
-        wave_topk<EPL>(vals, E, k, lane, ids + t * k, tw + t * k, s_ids + t * k);
+        wave_topk_select<EPL>(vals, E, k, lane, ids + t * k, tw + t * k, s_ids + t * k);
     }
     // grouping of the T*k (token, slot) entries
     for (int i = threadIdx.x; i < E; i += blockDim.x) s_cnt[i] = 0;
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ p
         }
         vals[j] = v;
     }
-    wave_topk<EPL>(vals, E, k, lane, ids + (size_t)t * k, tw + (size_t)t * k, nullptr);
+    wave_topk_select<EPL>(vals, E, k, lane, ids + (size_t)t * k, tw + (size_t)t * k);
 }
 
 // One workgroup per expert e.  Every token's ids are ascending, so
