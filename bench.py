@@ -36,9 +36,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MoE-layer tokens/sec + %HBM roofline (T=1) and %MFMA peak (T=2048)"
 
-ROUTE_SMALL = ["route_small"]
 ROUTE_LARGE = ["router_split", "router_logits", "router_topk", "router_group"]
-FWD_DECODE = ["decode_gateup", "decode_down"]
+BLOCK_DECODE = ["decode_logits_shared", "decode_route_gateup", "decode_down"]
 FWD_GROUPED = ["grouped_gateup", "grouped_down", "finalize"]
 
 
@@ -171,15 +170,20 @@ def run_decode(args, ev):
     xs = [[torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16) for _ in range(L)]
           for _ in range(nx)]
 
+    split = getattr(args, "entry", "block") == "split"
+
     def step(i=0):
         for l, blk in enumerate(blocks):
-            blk(xs[i % nx][l])
+            if split:
+                blk.split(xs[i % nx][l])
+            else:
+                blk(xs[i % nx][l])
 
     elapsed = time_steps(step, args.steps, args.warmup)
     ms_per_step = 1e3 * elapsed / args.steps
     value = L * T * args.steps / elapsed
 
-    names = ROUTE_SMALL + FWD_DECODE
+    names = BLOCK_DECODE
     kt = kernel_times(blocks, xs, min(args.steps, 10), ev, names,
                       lambda blk, x, e: blk.block_timed(x, e))
     # algorithmic bytes per launch from the routing each layer produced
@@ -190,10 +194,12 @@ def run_decode(args, ev):
     n_act = sum(active) / len(active)
     routing_bytes = T * k * 8 + (2 * E + 1 + T * k) * 4
     layer_bytes = E * H * 4 + (n_act + 1) * (2 * gu_b + dn_b) + 2 * T * H * 2 + routing_bytes
+    # per kernel: every byte it must read or write once (weights, activations,
+    # logits, h rows, routing)
     alg = {
-        "route_small": E * H * 4 + T * H * 2 + routing_bytes,
-        "decode_gateup": (n_act + 1) * 2 * gu_b + T * H * 2 + (T * k + T) * I * 2,
-        "decode_down": (n_act + 1) * dn_b + (T * k + T) * I * 2 + T * H * 2,
+        "decode_logits_shared": E * H * 4 + T * H * 2 + 2 * gu_b + T * E * 4 + T * I * 2,
+        "decode_route_gateup": T * E * 4 + n_act * 2 * gu_b + T * H * 2 + T * k * I * 2 + routing_bytes,
+        "decode_down": (n_act + 1) * dn_b + (T * k + T) * I * 2 + T * k * 8 + T * H * 2,
     }
     dom = max(names, key=lambda n: kt[n])
     achieved = alg[dom] / (kt[dom] * 1e-6) / 1e9
@@ -284,6 +290,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=int, default=1, help="decode rows per layer-call (1..5)")
+    ap.add_argument("--entry", choices=("block", "split"), default="block",
+                    help="decode through moe_w4_block (default) or moe_w4_route + moe_w4_forward "
+                         "(throughput only; kernel timings always use moe_w4_block)")
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")

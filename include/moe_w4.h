@@ -156,9 +156,16 @@ int moe_w4_forward(const moe_w4_dims* dims, const void* x,
 /*
  * moe_w4_route() followed by moe_w4_forward() in one call, with the same
  * arguments, outputs and errors as the pair: every argument is validated before
- * anything is enqueued, and both stages are enqueued on `hip_stream` in order.
- * The routing outputs are written as by moe_w4_route() (callers that do not
- * need them still pass the buffers: the forward stage reads them).
+ * anything is enqueued.  The routing outputs are written as moe_w4_route()
+ * writes them.  For T <= 2 the work is scheduled as three kernels instead of the
+ * pair's: (1) router logits together with the shared expert's gate/up, which
+ * need only x; (2) top-k and grouping repeated by every workgroup from the
+ * logits, followed by the selected experts' gate/up; (3) down and the weighted
+ * combine.  Splitting the decode step so that independent reads stream together
+ * and no single workgroup serialises the routing follows the pages' emphasis on
+ * the hand-off between decode stages ("Perplexity's Lily brings fast local AI
+ * to Apple silicon Macs", section "Where the Engine Gains Speed").  For larger
+ * T it enqueues route then forward.
  */
 int moe_w4_block(const moe_w4_dims* dims, const void* x,
                  const float* router_w, const float* router_b,

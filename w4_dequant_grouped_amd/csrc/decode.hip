@@ -98,6 +98,22 @@ __device__ __forceinline__ void build_slots(const int32_t* __restrict__ offsets,
     if (lane == 0) *s_n = min(base + a.total, kMaxSlots);
 }
 
+// Slot list from a table written by the routing kernel: [0] = n, then (expert,
+// first h row, rows) for each selected expert in ascending id.  One round trip.
+__device__ __forceinline__ void read_slot_table(const int32_t* __restrict__ table, int T, int k,
+                                                int has_shared, Slot* s_slots, int* s_n, int lane) {
+    const int base = has_shared ? 1 : 0;
+    const int n = min(max(table[0], 0), min(T * k, kMaxSlots - base));
+    if (has_shared && lane == 0) s_slots[0] = Slot{-1, T * k, T};
+    for (int i = lane; i < n; i += kWave) {
+        const int e = table[1 + 3 * i];
+        const int off = min(max(table[2 + 3 * i], 0), T * k);
+        const int cnt = min(max(table[3 + 3 * i], 0), min(T, T * k - off));
+        s_slots[base + i] = Slot{e, off, cnt};
+    }
+    if (lane == 0) *s_n = base + n;
+}
+
 // The idx-th non-empty expert (ascending id), found by one wavefront;
 // Slot{-2, 0, 0} if there are fewer.
 __device__ __forceinline__ Slot find_slot(const int32_t* __restrict__ offsets, int E, int T, int k,
@@ -124,30 +140,35 @@ __device__ __forceinline__ Slot find_slot(const int32_t* __restrict__ offsets, i
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU
 // ---------------------------------------------------------------------------
-constexpr int kGuRowsPerWave = 4;
-constexpr int kGuRowsPerBlock = 4 * kGuRowsPerWave;
+// Weight rows per wavefront: 4 for up to two token rows, 2 beyond (the x rows
+// and accumulators of every token stay in registers).
+template <int TMAX>
+constexpr int gu_rows_per_wave() { return TMAX <= 2 ? 4 : 2; }
+template <int TMAX>
+constexpr int gu_rows_per_block() { return 4 * gu_rows_per_wave<TMAX>(); }
 
-// Rows n0 .. n0+3 of gate and up of expert e, for the cnt token rows tok[0..cnt):
+// Rows n0 .. n0+R-1 of gate and up of expert e, for the cnt token rows tok[0..cnt):
 // h[hrow0 + i][n0 + r] = silu(gate . x) * (up . x), bf16.  One wavefront.
 template <int TMAX>
 __device__ __forceinline__ void gateup_rows(const uint16_t* __restrict__ x, int H, int I,
                                             const W4& G, const W4& U, int e, int n0, int cnt,
                                             const int (&tok)[TMAX], int hrow0,
                                             uint16_t* __restrict__ h, int lane) {
+    constexpr int R = gu_rows_per_wave<TMAX>();
     const int ngroups = H / kGroup;
     const int nchunks = H / 32;
-    float ag[kGuRowsPerWave][TMAX], au[kGuRowsPerWave][TMAX];
+    float ag[R][TMAX], au[R][TMAX];
 #pragma unroll
-    for (int r = 0; r < kGuRowsPerWave; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < TMAX; ++i) { ag[r][i] = 0.f; au[r][i] = 0.f; }
 
     for (int c = lane; c < nchunks; c += kWave) {
-        u32x4 cg[kGuRowsPerWave], cu[kGuRowsPerWave];
-        uint32_t sg[kGuRowsPerWave], bg[kGuRowsPerWave], su[kGuRowsPerWave], bu[kGuRowsPerWave];
+        u32x4 cg[R], cu[R];
+        uint32_t sg[R], bg[R], su[R], bu[R];
         u32x4 xv[TMAX][4];
 #pragma unroll
-        for (int r = 0; r < kGuRowsPerWave; ++r) {
+        for (int r = 0; r < R; ++r) {
             const size_t row = (size_t)e * I + (n0 + r);
             cg[r] = load_u32x4(G.codes + row * (H / 2) + c * 16);
             cu[r] = load_u32x4(U.codes + row * (H / 2) + c * 16);
@@ -167,7 +188,7 @@ __device__ __forceinline__ void gateup_rows(const uint16_t* __restrict__ x, int 
             float xs;
             interleave32(xv[i], xi, xs);
 #pragma unroll
-            for (int r = 0; r < kGuRowsPerWave; ++r) {
+            for (int r = 0; r < R; ++r) {
                 const float s0 = bf16_to_f32(sg[r]), s1 = bf16_to_f32(su[r]);
                 const float pg = dot32_magic(cg[r], xi);
                 const float pu = dot32_magic(cu[r], xi);
@@ -181,7 +202,7 @@ __device__ __forceinline__ void gateup_rows(const uint16_t* __restrict__ x, int 
         if (i >= cnt) break;
         const int hrow = hrow0 + i;
 #pragma unroll
-        for (int r = 0; r < kGuRowsPerWave; ++r) {
+        for (int r = 0; r < R; ++r) {
             const float g = wave_sum(ag[r][i]);
             const float u = wave_sum(au[r][i]);
             if (lane == r) h[(size_t)hrow * I + n0 + r] = (uint16_t)f32_to_bf16(silu(g) * u);
@@ -223,7 +244,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
         if (TMAX > 1 && i < sl.cnt)
             tok[i] = is_shared ? i : min(max(perm[sl.off + i], 0), T * k - 1) / k;
     }
-    const int n0 = blockIdx.y * kGuRowsPerBlock + wave * kGuRowsPerWave;
+    const int n0 = blockIdx.y * gu_rows_per_block<TMAX>() + wave * gu_rows_per_wave<TMAX>();
     gateup_rows<TMAX>(x, H, I, G, U, e, n0, sl.cnt, tok, sl.off, h, lane);
 }
 
@@ -241,7 +262,7 @@ __global__ __launch_bounds__(256) void k_decode_down(
     int T, int H, int I, int E, int k, W4Set routed, W4Set shared, int has_shared,
     const float* __restrict__ topk_w, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const uint16_t* __restrict__ h,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, const int32_t* __restrict__ slot_table) {
     __shared__ Slot s_slots[kMaxSlots];
     __shared__ int s_n;
     __shared__ __attribute__((aligned(16))) uint16_t s_h[kDnLdsRows * kDnLdsI];
@@ -256,7 +277,10 @@ __global__ __launch_bounds__(256) void k_decode_down(
         for (int i = threadIdx.x; i < n16; i += blockDim.x)
             reinterpret_cast<u32x4*>(s_h)[i] = reinterpret_cast<const u32x4*>(h)[i];
     }
-    if (wave == 0) build_slots(offsets, E, T, k, has_shared, s_slots, &s_n, lane);
+    if (wave == 0) {
+        if (slot_table) read_slot_table(slot_table, T, k, has_shared, s_slots, &s_n, lane);
+        else build_slots(offsets, E, T, k, has_shared, s_slots, &s_n, lane);
+    }
     __syncthreads();
     const int nslots = s_n;
 
@@ -340,7 +364,7 @@ __global__ __launch_bounds__(256) void k_decode_down(
 template <int TMAX>
 static hipError_t decode_t(const ForwardArgs& a, hipStream_t st, KernelTimer& tm) {
     const int max_slots = min(a.E, a.T * a.k) + (a.has_shared ? 1 : 0);
-    dim3 g1(max_slots, a.I / kGuRowsPerBlock);
+    dim3 g1(max_slots, a.I / gu_rows_per_block<TMAX>());
     tm.before();
     hipLaunchKernelGGL(k_decode_gateup<TMAX>, g1, dim3(256), 0, st, a.x, a.T, a.H, a.I, a.E, a.k,
                        a.routed, a.shared, a.has_shared, a.offsets, a.perm, a.ws_h);
@@ -350,7 +374,7 @@ static hipError_t decode_t(const ForwardArgs& a, hipStream_t st, KernelTimer& tm
     tm.before();
     hipLaunchKernelGGL(k_decode_down<TMAX>, dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T,
                        a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.topk_w, a.offsets,
-                       a.perm, a.ws_h, a.out);
+                       a.perm, a.ws_h, a.out, nullptr);
     tm.after();
     return hipGetLastError();
 }
@@ -415,7 +439,7 @@ __global__ __launch_bounds__(256) void k_decode_logits_shared(DecodeBlockArgs a)
         int tok[TMAX];
 #pragma unroll
         for (int i = 0; i < TMAX; ++i) tok[i] = i;
-        const int n0 = (blockIdx.x - nlog) * kGuRowsPerBlock + wave * kGuRowsPerWave;
+        const int n0 = (blockIdx.x - nlog) * gu_rows_per_block<TMAX>() + wave * gu_rows_per_wave<TMAX>();
         gateup_rows<TMAX>(a.x, H, a.I, a.shared.gate, a.shared.up, 0, n0, T, tok, T * a.k, a.h, lane);
     }
 }
@@ -423,16 +447,19 @@ __global__ __launch_bounds__(256) void k_decode_logits_shared(DecodeBlockArgs a)
 template <int TMAX, int EPL>
 __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) {
     constexpr int N = TMAX * kMaxTopK;            // (token, slot) entries at most
-    constexpr int EPW = (N + kWave - 1) / kWave;  // entries per lane in the grouping
     __shared__ int32_t s_ids[N];
     __shared__ float s_w[N];
-    __shared__ int s_ptok[N], s_pflat[N];
+    __shared__ uint64_t s_mask[TMAX][EPL];        // chosen experts of each token
+    __shared__ int s_ptok[N];
     __shared__ int s_u[N], s_uoff[N], s_ucnt[N];
     __shared__ int s_nu;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int T = a.T, E = a.E, k = a.k;
-    const int n = T * k;
+    // the workgroup past the last slot column writes the routing outputs and
+    // runs no expert rows (its other rows have nothing to do)
+    const bool writer = blockIdx.x == gridDim.x - 1;
+    if (writer && blockIdx.y != 0) return;
 
     // top-k of every token: wavefront t
     for (int t = wave; t < T; t += 4) {
@@ -442,90 +469,88 @@ __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) 
             const int e = lane + kWave * j;
             vals[j] = (e < E) ? a.logits[t * E + e] : -INFINITY;
         }
-        wave_topk_select<EPL>(vals, E, k, lane, s_ids + t * k, s_w + t * k);
+        wave_topk_select<EPL>(vals, E, k, lane, writer ? a.ids + t * k : s_ids + t * k,
+                              writer ? a.tw + t * k : s_w + t * k, nullptr, &s_mask[t][0]);
     }
     __syncthreads();
-    // grouping by wavefront 0, in registers: entry i = lane + 64 j; its position
-    // in (expert, token) order is #{entries of lower experts} + #{entries of the
-    // same expert from earlier tokens}; the first entry of each expert also gets
-    // the expert's rank among the selected experts
+    // grouping by wavefront 0 from the selection masks: lane l handles experts
+    // e = l + 64 j.  Entries of lower experts = popcounts of the masks below e;
+    // entries of e from earlier tokens = mask bits of e in those tokens; the
+    // rank of e among the selected experts = popcounts of the union below e;
+    // e's slot within a token = that token's popcounts below e.
     if (wave == 0) {
-        int ee[EPW], below[EPW], before[EPW], cnt[EPW], rank[EPW];
+        // all masks in registers (one LDS round trip), zero past T
+        uint64_t mk[TMAX][EPL];
+        int pre[TMAX][EPL];              // token t's chosen experts below 64 j
 #pragma unroll
-        for (int j = 0; j < EPW; ++j) {
-            const int i = lane + kWave * j;
-            ee[j] = (i < n) ? s_ids[i] : 0x7FFFFFFF;
-            below[j] = before[j] = cnt[j] = rank[j] = 0;
-        }
-        for (int q = 0; q < n; ++q) {
-            const int eq = __builtin_amdgcn_readlane(ee[0], q & (kWave - 1));
-            const int eq1 = (EPW > 1) ? __builtin_amdgcn_readlane(ee[EPW - 1], q & (kWave - 1)) : eq;
-            const int e_q = (q < kWave) ? eq : eq1;
-            const int tq = q / k;
+        for (int t = 0; t < TMAX; ++t) {
+            int run = 0;
 #pragma unroll
-            for (int j = 0; j < EPW; ++j) {
-                const int t = (lane + kWave * j) / k;
-                below[j] += (e_q < ee[j]) ? 1 : 0;
-                before[j] += (e_q == ee[j] && tq < t) ? 1 : 0;
-                cnt[j] += (e_q == ee[j]) ? 1 : 0;
+            for (int j = 0; j < EPL; ++j) {
+                mk[t][j] = (t < T) ? s_mask[t][j] : 0ull;
+                pre[t][j] = run;
+                run += __builtin_popcountll(mk[t][j]);
             }
-        }
-        bool first[EPW];
-#pragma unroll
-        for (int j = 0; j < EPW; ++j) first[j] = (lane + kWave * j < n) && before[j] == 0;
-        for (int q = 0; q < n; ++q) {
-            const int src = q & (kWave - 1);
-            const bool hi = q >= kWave;
-            const int fq = hi ? __builtin_amdgcn_readlane((int)first[EPW - 1], src)
-                              : __builtin_amdgcn_readlane((int)first[0], src);
-            const int e_q = hi ? __builtin_amdgcn_readlane(ee[EPW - 1], src)
-                               : __builtin_amdgcn_readlane(ee[0], src);
-#pragma unroll
-            for (int j = 0; j < EPW; ++j) rank[j] += (fq && e_q < ee[j]) ? 1 : 0;
         }
         int nu = 0;
+        int below_j = 0;                 // entries of experts < 64 j
 #pragma unroll
-        for (int j = 0; j < EPW; ++j) {
-            const int i = lane + kWave * j;
-            if (i < n) {
-                const int p = below[j] + before[j];
-                s_ptok[p] = i / k;
-                s_pflat[p] = i;
-                if (first[j]) {
-                    s_u[rank[j]] = ee[j];
-                    s_uoff[rank[j]] = p;
-                    s_ucnt[rank[j]] = cnt[j];
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + kWave * j;
+            uint64_t un = 0ull;
+            int below = below_j, cnt = 0, tot_j = 0;
+#pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+                un |= mk[t][j];
+                below += bits_below(mk[t][j]);
+                cnt += (int)((mk[t][j] >> lane) & 1ull);
+                tot_j += __builtin_popcountll(mk[t][j]);
+            }
+            if (writer && e < E) {
+                a.offsets[e] = below;
+                a.counts[e] = cnt;
+            }
+            if (cnt > 0) {
+                const int rank = nu + bits_below(un);
+                s_u[rank] = e;
+                s_uoff[rank] = below;
+                s_ucnt[rank] = cnt;
+                int before = 0;
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t) {
+                    if ((mk[t][j] >> lane) & 1ull) {
+                        const int p = below + before;
+                        s_ptok[p] = t;
+                        if (writer) a.perm[p] = t * k + pre[t][j] + bits_below(mk[t][j]);
+                        ++before;
+                    }
                 }
             }
-            nu += __builtin_popcountll(__builtin_amdgcn_ballot_w64(first[j]));
+            below_j += tot_j;
+            nu += __builtin_popcountll(un);
         }
+        if (writer && lane == 0) a.offsets[E] = T * k;
         if (lane == 0) s_nu = nu;
     }
     __syncthreads();
-    const int nu = s_nu;
-    if (blockIdx.x == 0 && blockIdx.y == 0) {     // the routing outputs of the call
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            a.ids[i] = s_ids[i];
-            a.tw[i] = s_w[i];
-            a.perm[i] = s_pflat[i];
+    if (writer) {                     // slot table for the down kernel
+        const int nu = s_nu;
+        for (int i = threadIdx.x; i < nu; i += blockDim.x) {
+            a.slots[1 + 3 * i] = s_u[i];
+            a.slots[2 + 3 * i] = s_uoff[i];
+            a.slots[3 + 3 * i] = s_ucnt[i];
         }
-        for (int e = threadIdx.x; e <= E; e += blockDim.x) {
-            int off = 0, cnt = 0;
-            for (int u = 0; u < nu; ++u) {
-                off += (s_u[u] < e) ? s_ucnt[u] : 0;
-                cnt = (s_u[u] == e) ? s_ucnt[u] : cnt;
-            }
-            a.offsets[e] = off;
-            if (e < E) a.counts[e] = cnt;
-        }
+        if (threadIdx.x == 0) a.slots[0] = nu;
+        return;
     }
+    const int nu = s_nu;
     const int slot = blockIdx.x;
     if (slot >= nu) return;
     const int cnt = min(s_ucnt[slot], T);
     int tok[TMAX];
 #pragma unroll
     for (int i = 0; i < TMAX; ++i) tok[i] = s_ptok[s_uoff[slot] + min(i, cnt - 1)];
-    const int n0 = blockIdx.y * kGuRowsPerBlock + wave * kGuRowsPerWave;
+    const int n0 = blockIdx.y * gu_rows_per_block<TMAX>() + wave * gu_rows_per_wave<TMAX>();
     gateup_rows<TMAX>(a.x, a.H, a.I, a.routed.gate, a.routed.up, s_u[slot], n0, cnt, tok,
                       s_uoff[slot], a.h, lane);
 }
@@ -533,22 +558,22 @@ __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) 
 template <int TMAX, int EPL>
 static hipError_t block_decode_t(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm) {
     const int nlog = (a.E + 3) / 4;
-    const int nsh = a.has_shared ? a.I / kGuRowsPerBlock : 0;
+    const int nsh = a.has_shared ? a.I / gu_rows_per_block<TMAX>() : 0;
     tm.before();
     hipLaunchKernelGGL(k_decode_logits_shared<TMAX>, dim3(nlog + nsh), dim3(256), 0, st, a);
     tm.after();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL((k_decode_route_gateup<TMAX, EPL>), dim3(min(a.E, a.T * a.k), a.I / kGuRowsPerBlock),
-                       dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_decode_route_gateup<TMAX, EPL>),
+                       dim3(min(a.E, a.T * a.k) + 1, a.I / gu_rows_per_block<TMAX>()), dim3(256), 0, st, a);
     tm.after();
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
     hipLaunchKernelGGL(k_decode_down<TMAX>, dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T,
                        a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.tw, a.offsets,
-                       a.perm, a.h, a.out);
+                       a.perm, a.h, a.out, a.slots);
     tm.after();
     return hipGetLastError();
 }
@@ -561,17 +586,23 @@ static hipError_t block_decode_e(const DecodeBlockArgs& a, hipStream_t st, Kerne
 }
 
 hipError_t launch_block_decode(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm) {
-    if (a.T <= 1) return block_decode_e<1>(a, st, tm);
-    if (a.T <= 2) return block_decode_e<2>(a, st, tm);
-    if (a.T <= 4) return block_decode_e<4>(a, st, tm);
-    return block_decode_e<8>(a, st, tm);
+    static_assert(kBlockDecodeMaxT == 2, "instantiations below");
+    switch (a.T) {
+        case 1: return block_decode_e<1>(a, st, tm);
+        case 2: return block_decode_e<2>(a, st, tm);
+        default: return hipErrorInvalidValue;     // the host serves larger T by route + forward
+    }
 }
 
 hipError_t launch_forward_decode(const ForwardArgs& a, hipStream_t st, KernelTimer& tm) {
-    if (a.T <= 1) return decode_t<1>(a, st, tm);
-    if (a.T <= 2) return decode_t<2>(a, st, tm);
-    if (a.T <= 4) return decode_t<4>(a, st, tm);
-    return decode_t<8>(a, st, tm);
+    switch (a.T) {
+        case 1: return decode_t<1>(a, st, tm);
+        case 2: return decode_t<2>(a, st, tm);
+        case 3: return decode_t<3>(a, st, tm);
+        case 4: return decode_t<4>(a, st, tm);
+        case 5: return decode_t<5>(a, st, tm);
+        default: return decode_t<8>(a, st, tm);
+    }
 }
 
 }  // namespace moe_w4

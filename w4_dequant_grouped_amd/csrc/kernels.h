@@ -9,6 +9,10 @@ namespace moe_w4 {
 
 constexpr int kSmallRouteMaxT = 8;   // largest T the one-launch router serves
 constexpr int kDecodeMaxT = 8;       // largest T the GEMV kernels are built for
+// Largest T for which moe_w4_block runs the three-launch decode schedule (every
+// routing workgroup repeats the top-k of all T rows, which stops paying off as
+// the selected experts -- and workgroups -- multiply); above it, route + forward.
+constexpr int kBlockDecodeMaxT = 2;
 
 struct W4 {                  // E matrices [N][K], packed as in moe_w4.h
     const uint8_t* codes;
@@ -72,6 +76,7 @@ struct DecodeBlockArgs {     // route + forward of decode rows (T <= kDecodeMaxT
     uint16_t* out;           // [T][H] bf16
     float* logits;           // [T][E] workspace
     uint16_t* h;             // [T*k + T][I] bf16 workspace
+    int32_t* slots;          // [1 + 3 T k] workspace: selected experts for the down kernel
 };
 
 // Optional per-kernel timing: events[2i] / events[2i+1] are recorded on the launch

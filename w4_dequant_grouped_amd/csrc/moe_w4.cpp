@@ -257,7 +257,7 @@ int moe_w4_block_timed(const moe_w4_dims* dims, const void* x, const float* rout
     if (st != MOE_W4_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     moe_w4::KernelTimer tm = make_timer(events, capacity, stream);
-    if (dims->T <= MOE_W4_DECODE_MAX_T) {
+    if (dims->T <= moe_w4::kBlockDecodeMaxT) {
         const Layout L = layout(dims);
         uint8_t* ws = static_cast<uint8_t*>(workspace);
         moe_w4::DecodeBlockArgs a;
@@ -280,6 +280,8 @@ int moe_w4_block_timed(const moe_w4_dims* dims, const void* x, const float* rout
         a.out = static_cast<uint16_t*>(out);
         a.logits = reinterpret_cast<float*>(ws + L.logits);
         a.h = reinterpret_cast<uint16_t*>(ws + L.h);
+        // the decode path has no fp32 accumulator: its region holds the slot table
+        a.slots = reinterpret_cast<int32_t*>(ws + L.acc);
         const hipError_t err = moe_w4::launch_block_decode(a, stream, tm);
         if (n_kernels) *n_kernels = tm.count;
         return launch_status(err);

@@ -36,12 +36,14 @@ __device__ __forceinline__ int bits_below(uint64_t mask) {
 // bitwise binary search on the order keys finds the k-th largest key theta (32
 // steps of one compare and one ballot count each); the entries above theta and
 // the lowest-id entries equal to theta are chosen, and every chosen entry's rank
-// in ascending expert order comes from the ballot masks.
+// in ascending expert order comes from the ballot masks, which are also
+// returned in masks_out[j] (bit l: expert 64 j + l chosen) when given.
 template <int EPL>
 __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E, int k, int lane,
                                                  int32_t* __restrict__ ids_out,
                                                  float* __restrict__ w_out,
-                                                 int32_t* ids_lds = nullptr) {
+                                                 int32_t* ids_lds = nullptr,
+                                                 uint64_t* masks_out = nullptr) {
     uint32_t key[EPL];
 #pragma unroll
     for (int j = 0; j < EPL; ++j) key[j] = (lane + kWave * j < E) ? order_key(vals[j]) : 0u;
@@ -93,6 +95,7 @@ __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E
             w_out[rank] = p[j] * inv;
             if (ids_lds) ids_lds[rank] = lane + kWave * j;
         }
+        if (masks_out && lane == 0) masks_out[j] = m;   // chosen experts 64 j .. 64 j + 63
         before += __builtin_popcountll(m);
     }
 }
