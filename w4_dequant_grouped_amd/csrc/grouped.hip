@@ -100,13 +100,15 @@ __device__ __forceinline__ TileCtx locate(int mt, const int* s_pre, int nseg, in
         const int mid = (lo + hi + 1) >> 1;
         if (s_pre[mid] <= mt) lo = mid; else hi = mid - 1;
     }
+    // every lane holds the same values: keep them in scalar registers
+    lo = (int)__builtin_amdgcn_readfirstlane(lo);
     TileCtx c;
     c.seg = lo;
     c.shared = (lo >= E);
     c.e = c.shared ? 0 : lo;
-    c.m0 = (mt - s_pre[lo]) * kBM;
-    c.rows = min(kBM, seg_count(offsets, lo, E, T, k) - c.m0);
-    c.hbase = seg_first(offsets, lo, E, T, k);
+    c.m0 = (int)__builtin_amdgcn_readfirstlane((mt - s_pre[lo]) * kBM);
+    c.rows = (int)__builtin_amdgcn_readfirstlane(min(kBM, seg_count(offsets, lo, E, T, k) - c.m0));
+    c.hbase = (int)__builtin_amdgcn_readfirstlane(seg_first(offsets, lo, E, T, k));
     return c;
 }
 
@@ -214,38 +216,48 @@ constexpr int kRowsPerWaveDma = kBM / kWaves;      // A rows copied by each wave
 constexpr int kDmaPerWave = kRowsPerWaveDma / 4;   // 4 rows (1 KiB) per A copy instruction
 constexpr int kLoadsPerChunk = kDmaPerWave + kBlkPerWave + 1;   // copies per wavefront per chunk
 
-// Per-wavefront B addressing (wave-uniform).
+// Per-tile copy addressing.  The bases are wave-uniform (SGPRs, advanced per
+// chunk with scalar adds); the lane offsets are computed once per tile, so a
+// copy costs no vector arithmetic except the scale/bias address (+4 B a chunk).
 template <int NMAT, int NBW>
-struct BAddr {
-    const uint8_t* codes[NMAT];      // matrix bases
-    const uint16_t* scales[NMAT];
-    const uint16_t* biases[NMAT];
-    uint32_t rowblk[NBW];            // first row (expert * N + n) of each 16-row block
+struct TileSrc {
+    uint64_t a_base;                 // A operand (x for gate/up, the segment's h rows for down)
+    uint32_t a_off[kDmaPerWave];     // lane's byte offset of its row piece in each A copy
+    uint64_t b_base[NMAT][NBW];      // codes of the first row of each (matrix, 16-row block)
+    uint32_t b_off;                  // lane's byte offset within a block's chunk
+    uint64_t sb_addr;                // lane's scale/bias word of chunk 0
     int K;
 };
+
+__device__ __forceinline__ uint32_t uniform32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    return ((uint64_t)uniform32((uint32_t)(v >> 32)) << 32) | uniform32((uint32_t)v);
+}
 
 // global -> LDS copies.  `lds` is the same for the whole wavefront; lane i
 // writes at lds + 16 i (dwordx4) or lds + 4 i (dword).  Issued through inline
 // assembly so that the compiler's wait insertion does not see them (it would
 // otherwise wait for every in-flight copy at each barrier); the K-loop waits for
 // them explicitly.  M0 is restored after use.
-__device__ __forceinline__ uint32_t lds_base(const void* lds) {
-    return __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+// LDS byte address (wave-uniform) of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* shared_obj) {
+    return uniform32((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)shared_obj);
 }
-__device__ __forceinline__ void dma16_to_lds(const void* src, const void* lds) {
+// 16 bytes per lane from sbase + voff (sbase wave-uniform) to LDS address lds + 16 lane
+__device__ __forceinline__ void dma16_to_lds(uint64_t sbase, uint32_t voff, uint32_t lds) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(src), "s"(lds_base(lds))
+        : "v"(voff), "s"(uniform64(sbase)), "s"(uniform32(lds))
         : "memory");
 }
-__device__ __forceinline__ void dma4_to_lds(const void* src, const void* lds) {
+// 4 bytes per lane from a per-lane address to LDS address lds + 4 lane
+__device__ __forceinline__ void dma4_to_lds(const void* src, uint32_t lds) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -254,81 +266,89 @@ __device__ __forceinline__ void dma4_to_lds(const void* src, const void* lds) {
         "global_load_lds_dword %1, off\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(src), "s"(lds_base(lds))
+        : "v"(src), "s"(uniform32(lds))
         : "memory");
 }
 
-// A rows of a tile: row r starts at base + rowidx(r) * row_bytes, where rowidx is
-// the token (gathered rows) or the consecutive h row.
-struct ASrc {
-    const uint8_t* base;
-    size_t row_bytes;
-    int rowidx[kDmaPerWave];   // row index of the lane's row in each copy instruction
-};
+// Offsets of a stage's parts from the start of the stage ring.
+__device__ __forceinline__ uint32_t off_a(int st) { return (uint32_t)(st * kStageBytes); }
+__device__ __forceinline__ uint32_t off_b(int st, int wave) {
+    return (uint32_t)(st * kStageBytes + kABuf + wave * kBlkPerWave * kBBlk);
+}
+__device__ __forceinline__ uint32_t off_sb(int st, int wave) {
+    return (uint32_t)(st * kStageBytes + kABuf + kBBuf + wave * kSBWave);
+}
 
-// Copy one A chunk: wavefront w copies rows [16w, 16w+16), four rows (64 lanes x
-// 16 bytes) per instruction.  Rows past the tile's valid rows re-read its last
-// valid row, so every address stays inside the operand.  A dummy chunk (past the
-// end of K) reads the operand's first bytes.
-__device__ __forceinline__ void issue_a_dma(uint8_t* s_buf, int wave, int lane, const ASrc& a,
-                                            int kc_bytes, bool dummy) {
+// Lane offsets of the A copies: wavefront w copies rows [16w, 16w+16), four rows
+// (64 lanes x 16 bytes) per instruction; the lane's row is lrow and its 16-byte
+// piece is stored XOR-swizzled by row.  row_of(lrow) gives the source row index
+// (clamped by the caller to the tile's rows, so every address stays inside the
+// operand).
+template <typename RowOf>
+__device__ __forceinline__ void a_offsets(uint32_t (&off)[kDmaPerWave], int wave, int lane,
+                                          uint32_t row_bytes, RowOf row_of) {
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-        const int r0 = wave * kRowsPerWaveDma + i * 4;
-        const int lrow = r0 + (lane >> 4);
+        const int lrow = wave * kRowsPerWaveDma + i * 4 + (lane >> 4);
         const int logical = (lane & 15) ^ (lrow & 15);
-        const uint8_t* src = dummy ? a.base
-                                   : a.base + (size_t)a.rowidx[i] * a.row_bytes + kc_bytes + logical * 16;
-        dma16_to_lds(src, s_buf + r0 * kARow);
+        off[i] = (uint32_t)row_of(lrow) * row_bytes + (uint32_t)logical * 16u;
     }
 }
 
-// Copy the wavefront's B operands of chunk kc into its slices of the stage:
-//  * codes: one instruction per (matrix, 16-row block) pair p; lane L fills
-//    slot L&3 (16 bytes) of row r = L>>2 (64 B per row) with quarter
-//    (L&3) ^ ((r>>2)&3) of the row's 64 code bytes of the chunk.  The XOR
-//    spreads the 16 rows' reads of one quarter over all LDS banks;
-//  * scale/bias: one dword instruction; lane L copies the word holding the
-//    chunk's two groups (even group in the low half) of row L&15, from the
-//    scales (bit 4 of L clear) or biases, of pair p = L>>5.  The word is 4-byte
-//    aligned because K/64 is even and the arrays are 4-byte aligned.
+// B addressing of a tile:
+//  * codes: one copy per (matrix, 16-row block) pair p; lane L fills slot L&3
+//    (16 bytes) of row r = L>>2 (64 B per row) with quarter (L&3) ^ ((r>>2)&3)
+//    of the row's 64 code bytes of the chunk; the XOR spreads the 16 rows'
+//    reads of one quarter over the LDS banks;
+//  * scale/bias: one dword copy; lane L copies the word holding the chunk's two
+//    groups (even group in the low half) of row L&15, from the scales (bit 4 of
+//    L clear) or biases, of pair p = L>>5.  The word is 4-byte aligned because
+//    K/64 is even and the arrays are 4-byte aligned.
 template <int NMAT, int NBW>
-__device__ __forceinline__ void issue_b_dma(uint8_t* s_b, uint8_t* s_sb, const BAddr<NMAT, NBW>& a,
-                                            int lane, int kc, bool dummy) {
+__device__ __forceinline__ void b_addressing(TileSrc<NMAT, NBW>& t, const W4 (&mat)[NMAT],
+                                             const uint32_t (&rowblk)[NBW], int K, int lane) {
     static_assert(NMAT * NBW == kBlkPerWave, "B slice layout");
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-            const size_t row = a.rowblk[nb] + (lane >> 2);
-            const int quarter = (lane & 3) ^ ((lane >> 4) & 3);
-            const uint8_t* src = dummy ? a.codes[m]
-                                       : a.codes[m] + row * (size_t)(a.K / 2) + (kc >> 1) + quarter * 16;
-            dma16_to_lds(src, s_b + (m * NBW + nb) * kBBlk);
-        }
-    // per-lane choice of array and row by bit masks on the (wave-uniform) values,
-    // so that no array of the argument struct is indexed by a lane-varying value
+        for (int nb = 0; nb < NBW; ++nb)
+            t.b_base[m][nb] = uniform64((uint64_t)mat[m].codes + (uint64_t)rowblk[nb] * (uint64_t)(K / 2));
+    t.b_off = (uint32_t)(lane >> 2) * (uint32_t)(K / 2) + (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+    // per-lane choice of array and row by bit masks on the wave-uniform values, so
+    // that no array of a struct is indexed by a lane-varying value
     const uint64_t second = 0ull - (uint64_t)(lane >> 5);          // pair 1: all ones
     const uint64_t bias = 0ull - (uint64_t)((lane >> 4) & 1);       // biases: all ones
-    const uint64_t sc0 = (uint64_t)a.scales[0], sc1 = (uint64_t)a.scales[NMAT - 1];
-    const uint64_t bi0 = (uint64_t)a.biases[0], bi1 = (uint64_t)a.biases[NMAT - 1];
+    const uint64_t sc0 = (uint64_t)mat[0].scales, sc1 = (uint64_t)mat[NMAT - 1].scales;
+    const uint64_t bi0 = (uint64_t)mat[0].biases, bi1 = (uint64_t)mat[NMAT - 1].biases;
     const uint64_t m2 = (NMAT == 2) ? second : 0ull;
     const uint64_t sc = sc0 ^ ((sc0 ^ sc1) & m2), bi = bi0 ^ ((bi0 ^ bi1) & m2);
     const uint64_t arr = sc ^ ((sc ^ bi) & bias);
-    const uint32_t r0 = a.rowblk[0], r1 = a.rowblk[NBW - 1];
+    const uint32_t r0 = rowblk[0], r1 = rowblk[NBW - 1];
     const uint32_t rb = r0 ^ ((r0 ^ r1) & ((NBW == 2) ? (uint32_t)second : 0u));
-    const size_t row = rb + (lane & 15);
-    const uint64_t off = 2ull * (row * (size_t)(a.K / kGroup) + kc / kGroup);
-    const void* src = reinterpret_cast<const void*>(dummy ? sc0 : arr + off);
-    dma4_to_lds(src, s_sb);
+    t.sb_addr = arr + 2ull * ((uint64_t)(rb + (lane & 15)) * (uint64_t)(K / kGroup));
+    t.K = K;
 }
 
-__device__ __forceinline__ uint8_t* stage_a(uint8_t* s, int st) { return s + st * kStageBytes; }
-__device__ __forceinline__ uint8_t* stage_b(uint8_t* s, int st, int wave) {
-    return s + st * kStageBytes + kABuf + wave * kBlkPerWave * kBBlk;
-}
-__device__ __forceinline__ uint8_t* stage_sb(uint8_t* s, int st, int wave) {
-    return s + st * kStageBytes + kABuf + kBBuf + wave * kSBWave;
+// Copies of chunk c into stage c mod kStages: the wavefront's A rows (only if
+// any of its 16 rows is in the tile's row blocks), then B codes, then
+// scale/bias -- a fixed count per wavefront.
+template <int NMAT, int NBW>
+__device__ __forceinline__ void issue_chunk(uint32_t ring, int wave, const TileSrc<NMAT, NBW>& t,
+                                            int c, bool has_a) {
+    const int st = c % kStages;
+    if (has_a) {
+        const uint64_t ab = t.a_base + (uint64_t)c * (kKC * 2);
+#pragma unroll
+        for (int i = 0; i < kDmaPerWave; ++i)
+            dma16_to_lds(ab, t.a_off[i], ring + off_a(st) + (wave * kRowsPerWaveDma + i * 4) * kARow);
+    }
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+            dma16_to_lds(t.b_base[m][nb] + (uint64_t)c * (kKC / 2), t.b_off,
+                         ring + off_b(st, wave) + (m * NBW + nb) * kBBlk);
+    dma4_to_lds(reinterpret_cast<const void*>(t.sb_addr + (uint64_t)c * 4u), ring + off_sb(st, wave));
 }
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained).
@@ -336,6 +356,15 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until this wavefront's copies of a chunk have landed, given how many whole
+// chunks it has issued after it (copies complete in order).
+__device__ __forceinline__ void wait_chunk(int after, bool has_a) {
+    static_assert(kStages == 3, "at most one chunk is issued after the one consumed");
+    if (after <= 0) wait_vmcnt<0>();
+    else if (has_a) wait_vmcnt<kLoadsPerChunk>();
+    else wait_vmcnt<kLoadsPerChunk - kDmaPerWave>();
 }
 
 // One K chunk of MFMAs over MB valid 16-row blocks (compile-time, so each step
@@ -387,63 +416,37 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const uint8_t* s_b
     }
 }
 
-// Issue the copies of one K chunk into stage st: the wavefront's A rows (only if
-// any of its 16 rows is in the tile's MB row blocks), then B codes, then
-// scale/bias -- a fixed count per wavefront, dummy or not.
-template <int NMAT, int NBW>
-__device__ __forceinline__ void issue_chunk(uint8_t* s_stage, int st, int wave, int lane,
-                                            const ASrc& src, const BAddr<NMAT, NBW>& ba, int kc,
-                                            bool dummy, bool has_a) {
-    if (has_a) issue_a_dma(stage_a(s_stage, st), wave, lane, src, 2 * kc, dummy);
-    issue_b_dma(stage_b(s_stage, st, wave), stage_sb(s_stage, st, wave), ba, lane, kc, dummy);
-}
-
-// K-loop over the ring.  Every iteration issues exactly one chunk (a dummy one
-// past the end of K), so the copies queued behind chunk c at its wait are always
-// the kStages-2 whole chunks issued after it.  Copies complete in order, so
-// waiting until at most that many are outstanding means this wavefront's part of
-// chunk c has landed; the barrier then makes every wavefront's part visible and
-// frees the stage read in the previous iteration.
+// K-loop over the ring.  Iteration c waits for chunk c (the copies issued after it
+// are those of the at most kStages-2 later chunks already in flight), then a
+// barrier makes every wavefront's part visible and frees the stage read in
+// iteration c-1, which receives chunk c+kStages-1.  Nothing is copied past the
+// end of K.
 template <int NMAT, int NBW, int MB>
-__device__ __forceinline__ void tile_kloop(uint8_t* s_stage, int K, int wave, int lane,
-                                           const ASrc& src, const BAddr<NMAT, NBW>& ba,
+__device__ __forceinline__ void tile_kloop(uint8_t* s_stage, int wave, int lane,
+                                           const TileSrc<NMAT, NBW>& t,
                                            f32x4 (&acc)[MB][NMAT][NBW]) {
     constexpr int D = kStages;
-    static_assert(D >= 2, "pipeline depth");
-    constexpr int kBehind = (D - 2) * kLoadsPerChunk;                    // waves copying A rows
-    constexpr int kBehindNoA = (D - 2) * (kLoadsPerChunk - kDmaPerWave);  // waves that do not
-    static_assert(kBehind < 64, "pipeline too deep for vmcnt");
     const bool has_a = wave < MB;          // wave w copies rows [16 w, 16 w + 16)
-    const int nch = K / kKC;
-#pragma unroll
-    for (int st = 0; st < D - 1; ++st)
-        issue_chunk(s_stage, st, wave, lane, src, ba, st * kKC, st >= nch, has_a);
-    const int nit = (nch + D - 1) / D * D;
-    for (int base = 0; base < nit; base += D) {
-#pragma unroll
-        for (int st = 0; st < D; ++st) {
-            const int c = base + st;
-            if (has_a) wait_vmcnt<kBehind>();
-            else wait_vmcnt<kBehindNoA>();
-            __syncthreads();       // chunk c visible to all; chunk c-1's stage is free
-            const int nxt = (st + D - 1) % D;
-            issue_chunk(s_stage, nxt, wave, lane, src, ba, (c + D - 1) * kKC, c + D - 1 >= nch,
-                        has_a);
-            if (c < nch)
-                mma_chunk<NMAT, NBW, MB>(stage_a(s_stage, st), stage_b(s_stage, st, wave),
-                                         stage_sb(s_stage, st, wave), lane, acc);
-        }
+    const int nch = t.K / kKC;
+    const uint32_t ring = lds_addr(s_stage);
+    for (int c = 0; c < D - 1 && c < nch; ++c) issue_chunk(ring, wave, t, c, has_a);
+    for (int c = 0; c < nch; ++c) {
+        wait_chunk(min(D - 2, nch - 1 - c), has_a);
+        __syncthreads();       // chunk c visible to all; the stage of chunk c-1 is free
+        if (c + D - 1 < nch) issue_chunk(ring, wave, t, c + D - 1, has_a);
+        const int st = c % D;
+        mma_chunk<NMAT, NBW, MB>(s_stage + off_a(st), s_stage + off_b(st, wave),
+                                 s_stage + off_sb(st, wave), lane, acc);
     }
-    wait_vmcnt<0>();               // drain the dummy copies
-    __syncthreads();               // all stages free for the next tile
+    __syncthreads();           // all stages free for the next tile
 }
 
 // ---------------------------------------------------------------------------
 // Per-tile bodies, specialised on the number MB of valid 16-row blocks
 // ---------------------------------------------------------------------------
 template <int NBW, int MB>
-__device__ __forceinline__ void gateup_tile(uint8_t* s_stage, int H, int I, int wave, int lane,
-                                            const ASrc& src, const BAddr<2, NBW>& ba, int rows,
+__device__ __forceinline__ void gateup_tile(uint8_t* s_stage, int I, int wave, int lane,
+                                            const TileSrc<2, NBW>& ts, int rows,
                                             int rowbase, int nbase, uint16_t* __restrict__ h) {
     f32x4 acc[MB][2][NBW];
 #pragma unroll
@@ -452,7 +455,7 @@ __device__ __forceinline__ void gateup_tile(uint8_t* s_stage, int H, int I, int 
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) acc[mb][m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    tile_kloop<2, NBW, MB>(s_stage, H, wave, lane, src, ba, acc);
+    tile_kloop<2, NBW, MB>(s_stage, wave, lane, ts, acc);
     // epilogue: h = silu(gate) * up, bf16, expert-sorted rows
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -471,8 +474,8 @@ __device__ __forceinline__ void gateup_tile(uint8_t* s_stage, int H, int I, int 
 }
 
 template <int NBW, int MB>
-__device__ __forceinline__ void down_tile(uint8_t* s_stage, int H, int I, int wave, int lane,
-                                          const ASrc& src, const BAddr<1, NBW>& ba, int rows,
+__device__ __forceinline__ void down_tile(uint8_t* s_stage, int H, int wave, int lane,
+                                          const TileSrc<1, NBW>& ts, int rows,
                                           int nbase, const int* s_tok, const float* s_w,
                                           float* __restrict__ accum) {
     f32x4 acc[MB][1][NBW];
@@ -480,7 +483,7 @@ __device__ __forceinline__ void down_tile(uint8_t* s_stage, int H, int I, int wa
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) acc[mb][0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    tile_kloop<1, NBW, MB>(s_stage, I, wave, lane, src, ba, acc);
+    tile_kloop<1, NBW, MB>(s_stage, wave, lane, ts, acc);
     // epilogue: routing-weighted add into the token's fp32 accumulator row
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -520,12 +523,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
     constexpr int BN = kWaves * 16 * NBW;
     const int NT = I / BN;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = (int)uniform32(threadIdx.x / kWave);
     TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false};    // thread 0's scheduling state
 
     if (threadIdx.x == 0) s_next = grab_tile(ctl, n_mt, NT, tq.q, tq.empty);
     __syncthreads();
-    for (int i = s_next; i >= 0; i = s_next) {
+    for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
         int mt, nt;
         tile_coords(i, NT, mt, nt);
         const TileCtx c = locate(mt, s_pre, nseg, E, T, k, offsets);
@@ -537,29 +540,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
         if (threadIdx.x == 0) tq.prefetch(ctl);
         const int nbase = nt * BN + wave * 16 * NBW;
 
-        BAddr<2, NBW> ba;
-        ba.codes[0] = Wset.gate.codes; ba.scales[0] = Wset.gate.scales; ba.biases[0] = Wset.gate.biases;
-        ba.codes[1] = Wset.up.codes;   ba.scales[1] = Wset.up.scales;   ba.biases[1] = Wset.up.biases;
+        TileSrc<2, NBW> ts;
+        ts.a_base = uniform64((uint64_t)x);
+        const int last = c.rows - 1;
+        a_offsets(ts.a_off, wave, lane, (uint32_t)H * 2u, [&](int r) { return s_tok[min(r, last)]; });
+        const W4 mats[2] = {Wset.gate, Wset.up};
+        uint32_t rowblk[NBW];
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) ba.rowblk[nb] = (uint32_t)(c.e * I + nbase + nb * 16);
-        ba.K = H;
-        ASrc src;
-        src.base = reinterpret_cast<const uint8_t*>(x);
-        src.row_bytes = (size_t)H * 2;
-#pragma unroll
-        for (int q = 0; q < kDmaPerWave; ++q)
-            src.rowidx[q] = s_tok[min(wave * kRowsPerWaveDma + q * 4 + (lane >> 4), c.rows - 1)];
+        for (int nb = 0; nb < NBW; ++nb) rowblk[nb] = uniform32((uint32_t)(c.e * I + nbase + nb * 16));
+        b_addressing(ts, mats, rowblk, H, lane);
 
         const int rowbase = c.hbase + c.m0;
         switch ((c.rows + 15) >> 4) {
-            case 1: gateup_tile<NBW, 1>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 2: gateup_tile<NBW, 2>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 3: gateup_tile<NBW, 3>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 4: gateup_tile<NBW, 4>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 5: gateup_tile<NBW, 5>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 6: gateup_tile<NBW, 6>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            case 7: gateup_tile<NBW, 7>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
-            default: gateup_tile<NBW, 8>(s_stage, H, I, wave, lane, src, ba, c.rows, rowbase, nbase, h); break;
+            case 1: gateup_tile<NBW, 1>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
+            case 2: gateup_tile<NBW, 2>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
+            case 3: gateup_tile<NBW, 3>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
+            case 4: gateup_tile<NBW, 4>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
+            case 5: gateup_tile<NBW, 5>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
+            case 6: gateup_tile<NBW, 6>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
+            case 7: gateup_tile<NBW, 7>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
+            default: gateup_tile<NBW, 8>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
         }
         if (threadIdx.x == 0) s_next = tq.next(ctl, n_mt, NT);
         __syncthreads();
@@ -588,12 +588,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
     constexpr int BN = kWaves * 16 * NBW;
     const int NT = H / BN;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = (int)uniform32(threadIdx.x / kWave);
     TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false};    // thread 0's scheduling state
 
     if (threadIdx.x == 0) s_next = grab_tile(ctl, n_mt, NT, tq.q, tq.empty);
     __syncthreads();
-    for (int i = s_next; i >= 0; i = s_next) {
+    for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
         int mt, nt;
         tile_coords(i, NT, mt, nt);
         const TileCtx c = locate(mt, s_pre, nseg, E, T, k, offsets);
@@ -610,27 +610,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
         __syncthreads();
         if (threadIdx.x == 0) tq.prefetch(ctl);
         const int nbase = nt * BN + wave * 16 * NBW;
-        BAddr<1, NBW> ba;
-        ba.codes[0] = Wset.down.codes; ba.scales[0] = Wset.down.scales; ba.biases[0] = Wset.down.biases;
+        TileSrc<1, NBW> ts;
+        ts.a_base = uniform64((uint64_t)(h + (size_t)(c.hbase + c.m0) * I));
+        const int last = c.rows - 1;
+        a_offsets(ts.a_off, wave, lane, (uint32_t)I * 2u, [&](int r) { return min(r, last); });
+        const W4 mats[1] = {Wset.down};
+        uint32_t rowblk[NBW];
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) ba.rowblk[nb] = (uint32_t)(c.e * H + nbase + nb * 16);
-        ba.K = I;
-        ASrc src;
-        src.base = reinterpret_cast<const uint8_t*>(h + (size_t)(c.hbase + c.m0) * I);
-        src.row_bytes = (size_t)I * 2;
-#pragma unroll
-        for (int q = 0; q < kDmaPerWave; ++q)
-            src.rowidx[q] = min(wave * kRowsPerWaveDma + q * 4 + (lane >> 4), c.rows - 1);
+        for (int nb = 0; nb < NBW; ++nb) rowblk[nb] = uniform32((uint32_t)(c.e * H + nbase + nb * 16));
+        b_addressing(ts, mats, rowblk, I, lane);
 
         switch ((c.rows + 15) >> 4) {
-            case 1: down_tile<NBW, 1>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 2: down_tile<NBW, 2>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 3: down_tile<NBW, 3>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 4: down_tile<NBW, 4>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 5: down_tile<NBW, 5>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 6: down_tile<NBW, 6>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            case 7: down_tile<NBW, 7>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
-            default: down_tile<NBW, 8>(s_stage, H, I, wave, lane, src, ba, c.rows, nbase, s_tok, s_w, accum); break;
+            case 1: down_tile<NBW, 1>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
+            case 2: down_tile<NBW, 2>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
+            case 3: down_tile<NBW, 3>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
+            case 4: down_tile<NBW, 4>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
+            case 5: down_tile<NBW, 5>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
+            case 6: down_tile<NBW, 6>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
+            case 7: down_tile<NBW, 7>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
+            default: down_tile<NBW, 8>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
         }
         if (threadIdx.x == 0) s_next = tq.next(ctl, n_mt, NT);
         __syncthreads();
