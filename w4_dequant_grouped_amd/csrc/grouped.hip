@@ -8,27 +8,25 @@
 //
 // Kernels (one stream, no host round trip; the tile list is derived on the device
 // from the routing offsets):
-//   k_grouped_gateup  per tile (segment, 128-row M-tile, N-tile of I): the rows'
-//                     activations are gathered by token into LDS, the gate and up
-//                     codes are loaded 128 bits per lane straight into registers,
-//                     dequantised (w = c * s + b, fp32 FMA, RNE to bf16) into the
-//                     MFMA B operand and multiplied on v_mfma_f32_16x16x32_bf16
-//                     with fp32 accumulation; the epilogue applies SwiGLU and
-//                     writes h (bf16) in expert-sorted row order.  It also clears
-//                     the fp32 output accumulator.
+//   k_grouped_gateup  per tile (segment, 64-row M-tile, 64-column N-tile of I):
+//                     the rows' activations (gathered by token), the gate and up
+//                     codes and their scale/bias words are copied into LDS; each
+//                     wavefront dequantises its 16 weight rows (w = c * s + b,
+//                     fp32, RNE to bf16) into the MFMA B operand and multiplies on
+//                     v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the
+//                     epilogue applies SwiGLU and writes h (bf16) in expert-sorted
+//                     row order.  It also clears the fp32 output accumulator.
 //   k_grouped_down    same K-loop over h (rows contiguous per expert), epilogue
 //                     scales each row by its routing weight and adds it into the
 //                     token's fp32 accumulator row (atomic add).
 //   k_finalize        accumulator -> bf16 output (round to nearest even).
 // A segment is a routed expert's rows (offsets[e]..offsets[e+1], tokens via the
 // permutation) or the shared expert's rows (all tokens, weight 1).  Persistent
-// workgroups walk the tile list; consecutive N-tiles of one M-tile are given to
-// workgroups on the same XCD (workgroup b runs on XCD b mod 8) so the gathered
-// activations are fetched into that XCD's L2 once.
+// 4-wavefront workgroups, two per CU, take tiles from per-XCD queues.
 //
 // MFMA operand layout used (16x16x32, wave64): lane l supplies A row l%16 and B
 // column l%16, each with 8 k values for the k-slot group l/16; D element
-// (4*(l/16)+i, l%16) is accumulator i of lane l.  A lane loads 32 consecutive
+// (4*(l/16)+i, l%16) is accumulator i of lane l.  A lane holds 32 consecutive
 // codes of one weight row (k = 32*(l/16) .. +32 of a 128-wide K chunk); MFMA step
 // j consumes its 8 codes 8j..8j+7, and the A operand is read from LDS at the same
 // logical k, so both operands agree on the k order.
@@ -37,11 +35,12 @@
 
 namespace moe_w4 {
 
-constexpr int kBM = 128;               // rows per M-tile
+constexpr int kBM = 64;                // rows per M-tile
 constexpr int kMB = kBM / 16;          // 16-row MFMA blocks per M-tile
+static_assert(kMB == 4, "the per-tile dispatch below covers 1..4 row blocks");
 constexpr int kKC = 128;               // K per chunk (4 MFMA steps of 32)
 constexpr int kMaxSeg = 1025;
-constexpr int kWaves = 8;                // wavefronts per workgroup
+constexpr int kWaves = 4;                // wavefronts per workgroup (two workgroups per CU)
 constexpr int kThreads = kWaves * 64;
 
 struct TileCtx {
@@ -203,15 +202,15 @@ __device__ __forceinline__ void release_queues(uint32_t* ctl) {
 //   stored XOR-swizzled by row, which keeps the MFMA operand reads conflict-free.
 // ---------------------------------------------------------------------------
 constexpr int kARow = kKC * 2;                     // bytes of one A row per chunk (256)
-constexpr int kABuf = kBM * kARow;                 // A bytes per stage (32 KiB)
+constexpr int kABuf = kBM * kARow;                 // A bytes per stage (16 KiB)
 constexpr int kBRowBytes = kKC / 2;                // packed codes of a weight row per chunk (64)
 constexpr int kBBlk = 16 * kBRowBytes;             // codes of one 16-row block (1 KiB)
 constexpr int kBlkPerWave = 2;                     // (matrix, 16-row block) pairs per wavefront
-constexpr int kBBuf = kWaves * kBlkPerWave * kBBlk;    // B code bytes per stage (16 KiB)
+constexpr int kBBuf = kWaves * kBlkPerWave * kBBlk;    // B code bytes per stage (8 KiB)
 constexpr int kSBWave = kWave * 4;                 // scale/bias words of a wavefront (256 B)
-constexpr int kSBBuf = kWaves * kSBWave;           // per stage (2 KiB)
+constexpr int kSBBuf = kWaves * kSBWave;           // per stage (1 KiB)
 constexpr int kStageBytes = kABuf + kBBuf + kSBBuf;
-constexpr int kStages = 3;                         // 150 KiB of the 160 KiB LDS
+constexpr int kStages = 3;                         // 75 KiB: two workgroups share a CU's 160 KiB
 constexpr int kRowsPerWaveDma = kBM / kWaves;      // A rows copied by each wavefront
 constexpr int kDmaPerWave = kRowsPerWaveDma / 4;   // 4 rows (1 KiB) per A copy instruction
 constexpr int kLoadsPerChunk = kDmaPerWave + kBlkPerWave + 1;   // copies per wavefront per chunk
@@ -361,8 +360,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Wait until this wavefront's copies of a chunk have landed, given how many whole
 // chunks it has issued after it (copies complete in order).
 __device__ __forceinline__ void wait_chunk(int after, bool has_a) {
-    static_assert(kStages == 3, "at most one chunk is issued after the one consumed");
-    if (after <= 0) wait_vmcnt<0>();
+    static_assert(kStages == 2 || kStages == 3, "at most one chunk is issued after the one consumed");
+    if (kStages == 2 || after <= 0) wait_vmcnt<0>();
     else if (has_a) wait_vmcnt<kLoadsPerChunk>();
     else wait_vmcnt<kLoadsPerChunk - kDmaPerWave>();
 }
@@ -509,7 +508,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
     uint16_t* __restrict__ h, float* __restrict__ acc_zero, long acc_elems, uint32_t* ctl) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages * kStageBytes];
     __shared__ int s_pre[kMaxSeg + 1];
-    __shared__ int s_tmp[kThreads];
     __shared__ int s_tok[kBM];
     __shared__ int s_next;
 
@@ -519,7 +517,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
         *reinterpret_cast<float4*>(acc_zero + i) = float4{0.f, 0.f, 0.f, 0.f};
 
     const int nseg = E + (has_shared ? 1 : 0);
-    const int n_mt = build_mtile_prefix(offsets, E, T, k, has_shared, s_pre, s_tmp);
+    const int n_mt = build_mtile_prefix(offsets, E, T, k, has_shared, s_pre,
+                                        reinterpret_cast<int*>(s_stage));   // scan scratch in the ring
     constexpr int BN = kWaves * 16 * NBW;
     const int NT = I / BN;
     const int lane = threadIdx.x & (kWave - 1);
@@ -556,10 +555,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
             case 2: gateup_tile<NBW, 2>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
             case 3: gateup_tile<NBW, 3>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
             case 4: gateup_tile<NBW, 4>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
-            case 5: gateup_tile<NBW, 5>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
-            case 6: gateup_tile<NBW, 6>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
-            case 7: gateup_tile<NBW, 7>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
-            default: gateup_tile<NBW, 8>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
+            default: gateup_tile<NBW, kMB>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
         }
         if (threadIdx.x == 0) s_next = tq.next(ctl, n_mt, NT);
         __syncthreads();
@@ -578,13 +574,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
     uint32_t* ctl) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages * kStageBytes];
     __shared__ int s_pre[kMaxSeg + 1];
-    __shared__ int s_tmp[kThreads];
     __shared__ int s_tok[kBM];
     __shared__ float s_w[kBM];
     __shared__ int s_next;
 
     const int nseg = E + (has_shared ? 1 : 0);
-    const int n_mt = build_mtile_prefix(offsets, E, T, k, has_shared, s_pre, s_tmp);
+    const int n_mt = build_mtile_prefix(offsets, E, T, k, has_shared, s_pre,
+                                        reinterpret_cast<int*>(s_stage));   // scan scratch in the ring
     constexpr int BN = kWaves * 16 * NBW;
     const int NT = H / BN;
     const int lane = threadIdx.x & (kWave - 1);
@@ -625,10 +621,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
             case 2: down_tile<NBW, 2>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
             case 3: down_tile<NBW, 3>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
             case 4: down_tile<NBW, 4>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
-            case 5: down_tile<NBW, 5>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
-            case 6: down_tile<NBW, 6>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
-            case 7: down_tile<NBW, 7>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
-            default: down_tile<NBW, 8>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
+            default: down_tile<NBW, kMB>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
         }
         if (threadIdx.x == 0) s_next = tq.next(ctl, n_mt, NT);
         __syncthreads();
@@ -665,7 +658,7 @@ hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTi
     const int nseg = a.E + (a.has_shared ? 1 : 0);
     // upper bound of M-tiles: every routed row tile-padded, plus one partial per segment
     const long mt_bound = ((long)a.T * a.k) / kBM + nseg + (a.has_shared ? a.T / kBM + 1 : 0);
-    const int slots = cu_count();          // one 8-wave workgroup per CU
+    const int slots = 2 * cu_count();      // two 4-wave workgroups per CU
     const long gu_tiles = mt_bound * (a.I / (kWaves * 16 * NBW_GU)) + 8;
     const long dn_tiles = mt_bound * (a.H / (kWaves * 16 * NBW_DN)) + 8;
     const int g_gu = (int)(((gu_tiles < slots ? gu_tiles : slots) + 7) / 8 * 8);
