@@ -8,6 +8,7 @@
 namespace moe_w4 {
 
 constexpr int kSmallRouteMaxT = 8;   // largest T the one-launch router serves
+constexpr int kRouterKSplit = 8;     // partial logit planes of the tiled router (T > kSmallRouteMaxT)
 constexpr int kDecodeMaxT = 8;       // largest T the GEMV kernels are built for
 // Largest T for which moe_w4_block runs the three-launch decode schedule (every
 // routing workgroup repeats the top-k of all T rows, which stops paying off as

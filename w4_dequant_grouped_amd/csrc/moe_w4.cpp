@@ -40,8 +40,8 @@ Layout layout(const moe_w4_dims* d) {
     Layout L;
     const size_t T = (size_t)d->T, E = (size_t)d->E;
     size_t off = kCtrlBytes;
-    L.logits = off;   // small T: [T][E] logits; large T: 4 K-split partial planes
-    off = align_up(off + T * E * sizeof(float) * (d->T > moe_w4::kSmallRouteMaxT ? 4 : 1));
+    L.logits = off;   // small T: [T][E] logits; large T: K-split partial planes
+    off = align_up(off + T * E * sizeof(float) * (d->T > moe_w4::kSmallRouteMaxT ? moe_w4::kRouterKSplit : 1));
     L.planes = off;
     if (d->T > moe_w4::kSmallRouteMaxT) off = align_up(off + 3 * E * (size_t)d->H * 2);
     L.h = off;

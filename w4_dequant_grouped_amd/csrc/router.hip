@@ -188,66 +188,88 @@ __global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ 
     }
 }
 
-// Partial logits over one quarter of H for a tile of 64 tokens x 64 experts:
-// wavefront w owns tokens 16w..16w+15 and all 64 experts (four 16-expert blocks,
-// three planes each).  MFMA 16x16x32 bf16 operands come straight from global
-// memory: lane l holds row (token or expert) l%16 and the 8 consecutive k at
-// 8*(l/16) of each 32-k step.  The K split gives four times the wavefronts;
-// the top-k kernel adds the partials in a fixed order.
-constexpr int kLgTok = 64;
-constexpr int kLgExp = 64;
-constexpr int kLgSplit = 4;      // K split (partial logit planes)
-constexpr int kLgUnroll = 2;     // K steps whose loads are issued together (H/kLgSplit % 64 == 0)
+// Partial logits over one eighth of H (kRouterKSplit) for a tile of 256 tokens x
+// 64 experts: wavefront w owns tokens 64w..64w+63 (four 16-token MFMA row blocks)
+// and all 64 experts (four 16-expert blocks, three planes each), so every step's
+// 16 operand loads feed 48 MFMAs.  MFMA 16x16x32 bf16 operands come straight from
+// global memory (the four wavefronts share the weight fragments through L1):
+// lane l holds row (token or expert) l%16 and the 8 consecutive k at 8*(l/16)
+// of each 32-k step.  The next step's operands are loaded while the current
+// step's MFMAs run.  The top-k kernel adds the partials in a fixed order.
+constexpr int kLgTokW = 64;                  // tokens per wavefront
+constexpr int kLgTok = 4 * kLgTokW;          // tokens per workgroup
+constexpr int kLgExp = 64;                   // experts per workgroup
+
+struct LgFrag {
+    bf16x8 a[4];
+    bf16x8 b[4][3];
+};
+
+__device__ __forceinline__ void lg_load(LgFrag& f, const uint16_t* const (&xa)[4],
+                                        const uint16_t* const (&wb)[4], size_t plane, int k) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) f.a[mb] = *reinterpret_cast<const bf16x8*>(xa[mb] + k);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+            f.b[nb][p] = *reinterpret_cast<const bf16x8*>(wb[nb] + p * plane + k);
+}
 
 __global__ __launch_bounds__(256) void k_router_logits_mfma(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes, int T, int H, int E,
     float* __restrict__ partial) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int t0 = blockIdx.y * kLgTok + wave * 16;
+    const int t0 = blockIdx.y * kLgTok + wave * kLgTokW;
+    if (t0 >= T) return;                       // whole wavefront past T (no barriers below)
     const int e0 = blockIdx.x * kLgExp;
-    const int ks = H / kLgSplit;
+    const int ks = H / kRouterKSplit;          // a multiple of 32 (H % 256 == 0)
     const int kbeg = blockIdx.z * ks;
     const size_t plane = (size_t)E * H;
-    const int trow = min(t0 + (lane & 15), T - 1);           // rows past T re-read row T-1
-    const uint16_t* xa = x + (size_t)trow * H + kbeg + (lane >> 4) * 8;
+    const uint16_t* xa[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int trow = min(t0 + mb * 16 + (lane & 15), T - 1);     // rows past T re-read row T-1
+        xa[mb] = x + (size_t)trow * H + kbeg + (lane >> 4) * 8;
+    }
     const uint16_t* wb[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
         wb[nb] = planes + (size_t)min(e0 + nb * 16 + (lane & 15), E - 1) * H + kbeg + (lane >> 4) * 8;
-    f32x4 acc[4];
+    f32x4 acc[4][4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kc = 0; kc < ks; kc += 32 * kLgUnroll) {
-        bf16x8 a[kLgUnroll], b[kLgUnroll][4][3];
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int u = 0; u < kLgUnroll; ++u) {
-            a[u] = *reinterpret_cast<const bf16x8*>(xa + kc + 32 * u);
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    LgFrag cur;
+    lg_load(cur, xa, wb, plane, 0);
+    for (int kc = 0; kc < ks; kc += 32) {
+        LgFrag nxt;
+        if (kc + 32 < ks) lg_load(nxt, xa, wb, plane, kc + 32);
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+        for (int p = 0; p < 3; ++p)
 #pragma unroll
-                for (int p = 0; p < 3; ++p)
-                    b[u][nb][p] = *reinterpret_cast<const bf16x8*>(wb[nb] + p * plane + kc + 32 * u);
-        }
-#pragma unroll
-        for (int u = 0; u < kLgUnroll; ++u)
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
+            for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][nb][p], acc[nb], 0, 0, 0);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[mb], cur.b[nb][p],
+                                                                         acc[mb][nb], 0, 0, 0);
+        cur = nxt;
     }
     float* out = partial + (size_t)blockIdx.z * T * E;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int e = e0 + nb * 16 + (lane & 15);
-        if (e >= E) continue;
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = t0 + (lane >> 4) * 4 + q;
-            if (t < T) out[(size_t)t * E + e] = acc[nb][q];
+        for (int nb = 0; nb < 4; ++nb) {
+            const int e = e0 + nb * 16 + (lane & 15);
+            if (e >= E) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = t0 + mb * 16 + (lane >> 4) * 4 + q;
+                if (t < T) out[(size_t)t * E + e] = acc[mb][nb][q];
+            }
         }
-    }
 }
 
 // One wavefront per token: logits = bias + the K-split partials (fixed order),
@@ -266,10 +288,11 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ p
         const int e = lane + kWave * j;
         float v = -INFINITY;
         if (e < E) {
-            float p[kLgSplit];
+            static_assert(kRouterKSplit == 8, "summation order below");
+            float p[kRouterKSplit];
 #pragma unroll
-            for (int q = 0; q < kLgSplit; ++q) p[q] = partial[((size_t)q * T + t) * E + e];
-            v = (p[0] + p[1]) + (p[2] + p[3]);
+            for (int q = 0; q < kRouterKSplit; ++q) p[q] = partial[((size_t)q * T + t) * E + e];
+            v = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
             if (br) v += br[e];
         }
         vals[j] = v;
@@ -281,63 +304,98 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ p
 //   offsets[e] = sum over tokens of #{j : ids[t][j] < e}
 // and the expert's segment lists, in token order, the tokens whose ids contain
 // e.  Each workgroup reads all ids (T*k ints, L2-resident) and needs nothing
-// from the others: no histogram, no atomics.
-__global__ __launch_bounds__(256) void k_router_group(const int32_t* __restrict__ ids, int T, int E,
-                                                      int k, int32_t* __restrict__ counts,
-                                                      int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ perm) {
-    __shared__ int s_below[256];
-    __shared__ int s_hits[256];
+// from the others: no histogram, no atomics.  Thread tid owns a contiguous run
+// of the flattened (t, j) entries, read kGroupBatch x 4 at a time with every
+// load of a batch issued together (once to count, once more, from L2, to write
+// its part of the permutation).
+constexpr int kGroupThreads = 256;
+constexpr int kGroupBatch = 16;          // int4 loads per thread issued together
+
+__device__ __forceinline__ void group_load(const int32_t* __restrict__ ids, int n, int q,
+                                           int4& w) {
+    const int i = 4 * q;
+    if (i + 3 < n) {
+        w = *reinterpret_cast<const int4*>(ids + i);
+    } else {
+        w.x = (i < n) ? ids[i] : 0x7FFFFFFF;
+        w.y = (i + 1 < n) ? ids[i + 1] : 0x7FFFFFFF;
+        w.z = (i + 2 < n) ? ids[i + 2] : 0x7FFFFFFF;
+        w.w = (i + 3 < n) ? ids[i + 3] : 0x7FFFFFFF;
+    }
+}
+
+__global__ __launch_bounds__(kGroupThreads) void k_router_group(const int32_t* __restrict__ ids,
+                                                                int T, int E, int k,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ perm) {
+    __shared__ int s_below[kGroupThreads / kWave];
+    __shared__ int s_hits[kGroupThreads / kWave];
     const int e = blockIdx.x;
     const int tid = threadIdx.x;
-    // contiguous run of the flattened (t, j) entries per thread, 4 at a time
     const int n = T * k;
     const int n4 = (n + 3) / 4;
-    const int per4 = (n4 + 255) / 256;
+    const int per4 = (n4 + kGroupThreads - 1) / kGroupThreads;
     const int q0 = min(tid * per4, n4), q1 = min(q0 + per4, n4);
     int below = 0, hits = 0;
-    for (int q = q0; q < q1; ++q) {
-        const int i = 4 * q;
-        int v[4];
-        if (i + 3 < n) {
-            const int4 w = *reinterpret_cast<const int4*>(ids + i);
-            v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
-        } else {
+    for (int qb = q0; qb < q1; qb += kGroupBatch) {
+        int4 w[kGroupBatch];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = (i + u < n) ? ids[i + u] : 0x7FFFFFFF;
+        for (int u = 0; u < kGroupBatch; ++u) {
+            w[u] = int4{0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
+            if (qb + u < q1) group_load(ids, n, qb + u, w[u]);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            below += (v[u] < e) ? 1 : 0;
-            hits += (v[u] == e) ? 1 : 0;
+        for (int u = 0; u < kGroupBatch; ++u) {
+            const bool ok = qb + u < q1;
+            below += ok ? (w[u].x < e) + (w[u].y < e) + (w[u].z < e) + (w[u].w < e) : 0;
+            hits += ok ? (w[u].x == e) + (w[u].y == e) + (w[u].z == e) + (w[u].w == e) : 0;
         }
     }
-    s_below[tid] = below;
-    s_hits[tid] = hits;
+    // inclusive scan of hits and sum of below: within the wavefront by shuffles,
+    // then across the kGroupThreads / 64 wavefronts
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    int incl = hits, bsum = below;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int vh = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += vh;
+        bsum += __shfl_xor(bsum, o, kWave);
+    }
+    if (lane == kWave - 1) s_hits[wave] = incl;
+    if (lane == 0) s_below[wave] = bsum;
     __syncthreads();
-    // inclusive scan of hits; sum of below
-    for (int o = 1; o < 256; o <<= 1) {
-        const int vh = (tid >= o) ? s_hits[tid - o] : 0;
-        const int vb = (tid >= o) ? s_below[tid - o] : 0;
-        __syncthreads();
-        s_hits[tid] += vh;
-        s_below[tid] += vb;
-        __syncthreads();
+    int hits_before = 0, base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupThreads / kWave; ++w) {
+        hits_before += (w < wave) ? s_hits[w] : 0;
+        total += s_hits[w];
+        base += s_below[w];
     }
-    const int base = s_below[255];
-    int pos = base + s_hits[tid] - hits;
-    if (tid == 255) {
+    int pos = base + hits_before + incl - hits;
+    if (tid == 0) {
         offsets[e] = base;
-        counts[e] = s_hits[255];
+        counts[e] = total;
         if (e == E - 1) offsets[E] = n;
     }
     if (hits == 0) return;
-    for (int q = q0; q < q1; ++q)
+    for (int qb = q0; qb < q1; qb += kGroupBatch) {
+        int4 w[kGroupBatch];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = 4 * q + u;
-            if (i < n && ids[i] == e) perm[pos++] = i;
+        for (int u = 0; u < kGroupBatch; ++u) {
+            w[u] = int4{0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
+            if (qb + u < q1) group_load(ids, n, qb + u, w[u]);
         }
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u) {
+            if (qb + u >= q1) continue;
+            const int i = 4 * (qb + u);
+            if (w[u].x == e) perm[pos++] = i;
+            if (w[u].y == e) perm[pos++] = i + 1;
+            if (w[u].z == e) perm[pos++] = i + 2;
+            if (w[u].w == e) perm[pos++] = i + 3;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -374,7 +432,7 @@ hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& t
     if (err != hipSuccess) return err;
     tm.before();
     hipLaunchKernelGGL(k_router_logits_mfma,
-                       dim3((a.E + kLgExp - 1) / kLgExp, (a.T + kLgTok - 1) / kLgTok, kLgSplit),
+                       dim3((a.E + kLgExp - 1) / kLgExp, (a.T + kLgTok - 1) / kLgTok, kRouterKSplit),
                        dim3(256), 0, st, a.x, a.ws_planes, a.T, a.H, a.E, a.ws_logits);
     tm.after();
     err = hipGetLastError();
@@ -393,7 +451,7 @@ hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& t
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL(k_router_group, dim3(a.E), dim3(256), 0, st, a.ids, a.T, a.E, a.k, a.counts,
+    hipLaunchKernelGGL(k_router_group, dim3(a.E), dim3(kGroupThreads), 0, st, a.ids, a.T, a.E, a.k, a.counts,
                        a.offsets, a.perm);
     tm.after();
     return hipGetLastError();
