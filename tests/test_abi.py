@@ -137,3 +137,11 @@ def test_forward_rejects_bad_arguments(lib):
     assert _forward(lib, _dims(), x=FAKE + 8) == ERR_ALIGN
     d = _dims()
     assert _forward(lib, d, ws_bytes=B.moe_w4_workspace_bytes(d) - 256) == ERR_WS
+
+
+def test_binding_constants_match_the_header():
+    text = open(os.path.join(ROOT, "include", "moe_w4.h")).read()
+    for name in ("MOE_W4_DECODE_MAX_T", "MOE_W4_CONTROL_BYTES"):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+        assert m, name
+        assert int(m.group(1)) == getattr(B, name), name

@@ -223,3 +223,36 @@ def test_block_calls_leave_control_block_clear(full_layer):
         if i % 8 == 0:
             check_routing(r, O.route(x, full_layer.router_w, None, 8), f"call {i}")
     assert int(ws[:B.MOE_W4_CONTROL_BYTES].cpu().sum()) == 0
+
+
+# --- the 40-layer stack's layer size, and exact ties ------------------------------------
+
+def test_stack_layer_T16384_sampled():
+    """One layer of the 40-layer stack workload (T=16384, Zipf router bias): routing
+    bit-exact against the oracle over all 16384 tokens, 12 sampled output rows."""
+    wl = synth.WORKLOADS["stack40"]
+    layer = synth.draw_layer(wl.shape, wl.seed)
+    _sampled_full(wl.shape, wl.seed, layer, "stack layer T=16384")
+
+
+@pytest.mark.parametrize("T", [1, 2, 16])
+def test_boundary_ties_go_to_the_lower_expert(T):
+    """Experts 5 and 9 have identical router rows and biases, so their logits tie
+    exactly; with experts 0 and 1 far above and the rest far below, the k=3 choice
+    must take 5 and leave 9 (one-launch router at T=1, 2; single-call block at
+    T=1, 2; tiled router at T=16)."""
+    shape = S(T=T, H=256, I=128, E=16, top_k=3)
+    layer = synth.draw_layer(shape, 80 + T)
+    layer.router_w[9] = layer.router_w[5]
+    bias = torch.full((16,), -40.0, dtype=torch.float32)
+    bias[0], bias[1], bias[5], bias[9] = 40.0, 30.0, 10.0, 10.0
+    layer.router_b = bias
+    x = synth.draw_x(T, 256, 80 + T)
+    ref = O.route(x, layer.router_w, layer.router_b, 3)
+    assert (ref.ids == np.array([0, 1, 5])).all()
+    lg = layer.to("cuda")
+    for split in (False, True):
+        r, out = run_block(lg, x.cuda(), shape, split=split)
+        check_routing(r, ref, f"ties T={T} {'split' if split else 'block'}")
+        y = O.forward_grouped(x, layer, ref, shape.group)
+        check_output(out, y, what=f"ties T={T}")
