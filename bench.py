@@ -52,6 +52,12 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(e, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
     def create(self, n):
         evs = []
@@ -127,12 +133,20 @@ def kernel_times(blocks, xs, steps, ev: HipEvents, names, timed):
     """Average duration per kernel name over `steps` passes over all blocks.
 
     ``timed(block, x, events)`` runs one block call recording an event pair
-    around each kernel and returns the kernel count."""
+    around each kernel and returns the kernel count.  Before each block call an
+    empty event pair is recorded on the same stream; its average span is the
+    cost the two event records add around a kernel, and is subtracted.
+    Returns (kernel_us, raw_kernel_us, empty_pair_us)."""
     import torch
     n = len(names)
-    events = []
+    stream = torch.cuda.current_stream().cuda_stream
+    events, empties = [], []
     for s in range(steps):
         for l, blk in enumerate(blocks):
+            z = ev.create(2)
+            ev.record(z[0], stream)
+            ev.record(z[1], stream)
+            empties.append(z)
             e = ev.create(2 * n)
             got = timed(blk, xs[s % len(xs)][l], e)
             assert got == n, (got, names)
@@ -143,7 +157,13 @@ def kernel_times(blocks, xs, steps, ev: HipEvents, names, timed):
         for i, name in enumerate(names):
             sums[name] += ev.elapsed_ms(e[2 * i], e[2 * i + 1])
         ev.destroy(e)
-    return {name: 1e3 * v / len(events) for name, v in sums.items()}   # microseconds per launch
+    empty = 0.0
+    for z in empties:
+        empty += ev.elapsed_ms(z[0], z[1])
+        ev.destroy(z)
+    empty_us = 1e3 * empty / len(empties)
+    raw = {name: 1e3 * v / len(events) for name, v in sums.items()}   # microseconds per launch
+    return {name: max(v - empty_us, 0.0) for name, v in raw.items()}, raw, empty_us
 
 
 def split_timed(nr):
@@ -184,8 +204,8 @@ def run_decode(args, ev):
     value = L * T * args.steps / elapsed
 
     names = BLOCK_DECODE
-    kt = kernel_times(blocks, xs, min(args.steps, 10), ev, names,
-                      lambda blk, x, e: blk.block_timed(x, e))
+    kt, kt_raw, pair_us = kernel_times(blocks, xs, min(args.steps, 10), ev, names,
+                                       lambda blk, x, e: blk.block_timed(x, e))
     # algorithmic bytes per launch from the routing each layer produced
     gu_b, dn_b = expert_bytes(H, I)
     active = []
@@ -209,6 +229,8 @@ def run_decode(args, ev):
         "traffic": traffic_from_profiles(dom, "decode"),
         "alg_bytes_per_launch": int(alg[dom]), "avg_launch_us": round(kt[dom], 3),
         "kernel_us": {n: round(v, 3) for n, v in kt.items()},
+        "kernel_us_event_pairs_raw": {n: round(v, 3) for n, v in kt_raw.items()},
+        "empty_event_pair_us": round(pair_us, 3),
         "layer_call_alg_bytes": int(layer_bytes),
         "layer_call_hbm_frac": round(layer_bytes / (ms_per_step / L * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "active_experts_per_call": n_act,
@@ -238,7 +260,8 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
 
     elapsed = time_steps(step, steps, warmup)
     per_call_ms = 1e3 * elapsed / (steps * L)
-    kt = kernel_times(blocks, xs, steps, ev, ROUTE_LARGE + FWD_GROUPED, split_timed(len(ROUTE_LARGE)))
+    kt, kt_raw, pair_us = kernel_times(blocks, xs, steps, ev, ROUTE_LARGE + FWD_GROUPED,
+                                       split_timed(len(ROUTE_LARGE)))
     rows = T * k + T
     flops = {"grouped_gateup": 2.0 * rows * H * 2 * I, "grouped_down": 2.0 * rows * I * H}
     dom = max(flops, key=lambda n: kt[n])
@@ -254,7 +277,9 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_from_profiles(dom, "prefill"),
                      "alg_flops_per_launch": flops[dom], "avg_launch_us": round(kt[dom], 3),
-                     "kernel_us": {n: round(v, 3) for n, v in kt.items()}},
+                     "kernel_us": {n: round(v, 3) for n, v in kt.items()},
+                     "kernel_us_event_pairs_raw": {n: round(v, 3) for n, v in kt_raw.items()},
+                     "empty_event_pair_us": round(pair_us, 3)},
     }
 
 

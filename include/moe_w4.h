@@ -145,6 +145,12 @@ int moe_w4_route(const moe_w4_dims* dims,
  * T <= MOE_W4_DECODE_MAX_T runs the decode path (one wavefront per weight row
  * streams each selected expert's bytes once); larger T runs the grouped MFMA
  * path.  Both accumulate in fp32; intermediate activations are rounded to bf16.
+ * The grouped path rounds each routed (token, slot) row's weighted expert output
+ * and the shared expert's output to bf16, then sums a token's rows in fp32 in
+ * slot order (shared last), so its result does not depend on scheduling.
+ * perm must be a permutation of 0 .. T*top_k-1 consistent with expert_offsets, as
+ * route() writes it: other values cannot make an access leave its buffer, but
+ * the output is then unspecified.
  * `topk_ids` is accepted for interface symmetry and may be NULL.
  */
 int moe_w4_forward(const moe_w4_dims* dims, const void* x,

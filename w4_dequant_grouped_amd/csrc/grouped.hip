@@ -15,14 +15,17 @@
 //                     fp32, RNE to bf16) into the MFMA B operand and multiplies on
 //                     v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the
 //                     epilogue applies SwiGLU and writes h (bf16) in expert-sorted
-//                     row order.  It also clears the fp32 output accumulator.
-//   k_grouped_down    same K-loop over h (rows contiguous per expert), epilogue
-//                     scales each row by its routing weight and adds it into the
-//                     token's fp32 accumulator row (atomic add).
-//   k_finalize        accumulator -> bf16 output (round to nearest even).
+//                     row order.
+//   k_grouped_down    same K-loop over h (rows contiguous per expert); the epilogue
+//                     scales each row by its routing weight and stores it (bf16) as
+//                     row t*k + j of a per-(token, slot) buffer, the shared expert's
+//                     row of token t as row T*k + t.  Plain stores: no atomics, and
+//                     every output row is owned by exactly one tile row.
+//   k_finalize        out[t] = sum of token t's k slot rows and its shared row, in
+//                     slot order, in fp32, rounded to bf16 (deterministic).
 // A segment is a routed expert's rows (offsets[e]..offsets[e+1], tokens via the
 // permutation) or the shared expert's rows (all tokens, weight 1).  Persistent
-// 4-wavefront workgroups, two per CU, take tiles from per-XCD queues.
+// 4-wavefront workgroups, three per CU, take tiles from per-XCD queues.
 //
 // MFMA operand layout used (16x16x32, wave64): lane l supplies A row l%16 and B
 // column l%16, each with 8 k values for the k-slot group l/16; D element
@@ -39,9 +42,9 @@ constexpr int kBM = 64;                // rows per M-tile
 constexpr int kMB = kBM / 16;          // 16-row MFMA blocks per M-tile
 static_assert(kMB == 4, "the per-tile dispatch below covers 1..4 row blocks");
 constexpr int kKC = 128;               // K per chunk (4 MFMA steps of 32)
-constexpr int kMaxSeg = 1025;
-constexpr int kWaves = 4;                // wavefronts per workgroup (two workgroups per CU)
+constexpr int kWaves = 4;                // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64;
+constexpr int kWgPerCu = 3;              // resident workgroups per CU (persistent grid size)
 
 struct TileCtx {
     int seg;        // segment index (E = shared)
@@ -210,7 +213,7 @@ constexpr int kBBuf = kWaves * kBlkPerWave * kBBlk;    // B code bytes per stage
 constexpr int kSBWave = kWave * 4;                 // scale/bias words of a wavefront (256 B)
 constexpr int kSBBuf = kWaves * kSBWave;           // per stage (1 KiB)
 constexpr int kStageBytes = kABuf + kBBuf + kSBBuf;
-constexpr int kStages = 3;                         // 75 KiB: two workgroups share a CU's 160 KiB
+constexpr int kStages = 2;                         // 50 KiB: three workgroups share a CU's 160 KiB
 constexpr int kRowsPerWaveDma = kBM / kWaves;      // A rows copied by each wavefront
 constexpr int kDmaPerWave = kRowsPerWaveDma / 4;   // 4 rows (1 KiB) per A copy instruction
 constexpr int kLoadsPerChunk = kDmaPerWave + kBlkPerWave + 1;   // copies per wavefront per chunk
@@ -443,6 +446,33 @@ __device__ __forceinline__ void tile_kloop(uint8_t* s_stage, int wave, int lane,
 // ---------------------------------------------------------------------------
 // Per-tile bodies, specialised on the number MB of valid 16-row blocks
 // ---------------------------------------------------------------------------
+// Stores one 16x16 result block as bf16 with one dword store per lane and row
+// pair: lane l holds column c = l%16 of rows 4*(l/16) + q; lanes l and l^1 swap
+// two values so that the even lane writes columns (c, c+1) of rows q = 0, 1 and
+// the odd lane columns (c-1, c) of rows q = 2, 3.  row_ptr(m) is the bf16 row
+// of tile row m (m < rows only); col0 is the block's first column (even).
+template <typename RowPtr>
+__device__ __forceinline__ void store_block_bf16(const float (&v)[4], int lane, int m0, int rows,
+                                                 int col0, RowPtr row_ptr) {
+    const bool odd = lane & 1;
+    const float s0 = odd ? v[0] : v[2], s1 = odd ? v[1] : v[3];
+    // quad_perm [1, 0, 3, 2]: value of lane l^1
+    const float r0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xF, 0xF, false));
+    const float r1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0xB1, 0xF, 0xF, false));
+    const int col = col0 + ((lane & 15) & ~1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = odd ? 2 + i : i;
+        const int m = m0 + (lane >> 4) * 4 + q;
+        const float own = odd ? (i ? v[3] : v[2]) : (i ? v[1] : v[0]);
+        const float other = i ? r1 : r0;
+        if (m < rows) {
+            const uint32_t pair = odd ? pack_bf16x2(other, own) : pack_bf16x2(own, other);
+            *reinterpret_cast<uint32_t*>(row_ptr(m) + col) = pair;
+        }
+    }
+}
+
 template <int NBW, int MB>
 __device__ __forceinline__ void gateup_tile(uint8_t* s_stage, int I, int wave, int lane,
                                             const TileSrc<2, NBW>& ts, int rows,
@@ -460,40 +490,38 @@ __device__ __forceinline__ void gateup_tile(uint8_t* s_stage, int I, int wave, i
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
-            const int n = nbase + nb * 16 + (lane & 15);
+            float v[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int m = mb * 16 + (lane >> 4) * 4 + q;
-                if (m < rows) {
-                    const float g = acc[mb][0][nb][q], u = acc[mb][1][nb][q];
-                    h[(size_t)(rowbase + m) * I + n] = (uint16_t)f32_to_bf16(silu(g) * u);
-                }
-            }
+            for (int q = 0; q < 4; ++q) v[q] = silu(acc[mb][0][nb][q]) * acc[mb][1][nb][q];
+            store_block_bf16(v, lane, mb * 16, rows, nbase + nb * 16,
+                             [&](int m) { return h + (size_t)(rowbase + m) * I; });
         }
 }
 
 template <int NBW, int MB>
 __device__ __forceinline__ void down_tile(uint8_t* s_stage, int H, int wave, int lane,
                                           const TileSrc<1, NBW>& ts, int rows,
-                                          int nbase, const int* s_tok, const float* s_w,
-                                          float* __restrict__ accum) {
+                                          int nbase, const int* s_dst, const float* s_w,
+                                          uint16_t* __restrict__ y) {
     f32x4 acc[MB][1][NBW];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) acc[mb][0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     tile_kloop<1, NBW, MB>(s_stage, wave, lane, ts, acc);
-    // epilogue: routing-weighted add into the token's fp32 accumulator row
+    // epilogue: the routing-weighted row, rounded to bf16, into its own row of y
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
-            const int n = nbase + nb * 16 + (lane & 15);
+            float v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int m = mb * 16 + (lane >> 4) * 4 + q;
-                if (m < rows) unsafeAtomicAdd(accum + (size_t)s_tok[m] * H + n, s_w[m] * acc[mb][0][nb][q]);
+                const int m = min(mb * 16 + (lane >> 4) * 4 + q, rows - 1);
+                v[q] = s_w[m] * acc[mb][0][nb][q];
             }
+            store_block_bf16(v, lane, mb * 16, rows, nbase + nb * 16,
+                             [&](int m) { return y + (size_t)s_dst[m] * H; });
         }
 }
 
@@ -501,20 +529,15 @@ __device__ __forceinline__ void down_tile(uint8_t* s_stage, int H, int wave, int
 // gate/up + SwiGLU
 // ---------------------------------------------------------------------------
 template <int NBW>
-__global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
+__global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
     const uint16_t* __restrict__ x, int T, int H, int I, int E, int k,
     W4Set routed, W4Set shared, int has_shared,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-    uint16_t* __restrict__ h, float* __restrict__ acc_zero, long acc_elems, uint32_t* ctl) {
+    uint16_t* __restrict__ h, uint32_t* ctl) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages * kStageBytes];
-    __shared__ int s_pre[kMaxSeg + 1];
+    extern __shared__ int s_pre[];       // M-tile prefix over the segments (nseg + 1 entries)
     __shared__ int s_tok[kBM];
     __shared__ int s_next;
-
-    // clear the fp32 output accumulator for the down kernel
-    for (long i = ((long)blockIdx.x * kThreads + threadIdx.x) * 4; i < acc_elems;
-         i += (long)gridDim.x * kThreads * 4)
-        *reinterpret_cast<float4*>(acc_zero + i) = float4{0.f, 0.f, 0.f, 0.f};
 
     const int nseg = E + (has_shared ? 1 : 0);
     const int n_mt = build_mtile_prefix(offsets, E, T, k, has_shared, s_pre,
@@ -567,14 +590,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gateup(
 // down + routing-weighted scatter-add
 // ---------------------------------------------------------------------------
 template <int NBW>
-__global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
+__global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
     int T, int H, int I, int E, int k, W4Set routed, W4Set shared, int has_shared,
     const float* __restrict__ topk_w, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm, const uint16_t* __restrict__ h, float* __restrict__ accum,
+    const int32_t* __restrict__ perm, const uint16_t* __restrict__ h, uint16_t* __restrict__ y,
     uint32_t* ctl) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages * kStageBytes];
-    __shared__ int s_pre[kMaxSeg + 1];
-    __shared__ int s_tok[kBM];
+    extern __shared__ int s_pre[];       // M-tile prefix over the segments (nseg + 1 entries)
+    __shared__ int s_dst[kBM];           // row of y each tile row goes to
     __shared__ float s_w[kBM];
     __shared__ int s_next;
 
@@ -596,10 +619,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
         const W4Set& Wset = c.shared ? shared : routed;
         __syncthreads();
         for (int r = threadIdx.x; r < c.rows; r += kThreads) {
-            if (c.shared) { s_tok[r] = c.m0 + r; s_w[r] = 1.0f; }
+            if (c.shared) { s_dst[r] = T * k + c.m0 + r; s_w[r] = 1.0f; }
             else {
                 const int f = min(max(perm[c.hbase + c.m0 + r], 0), T * k - 1);
-                s_tok[r] = f / k;
+                s_dst[r] = f;
                 s_w[r] = topk_w[f];
             }
         }
@@ -617,11 +640,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
         b_addressing(ts, mats, rowblk, I, lane);
 
         switch ((c.rows + 15) >> 4) {
-            case 1: down_tile<NBW, 1>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
-            case 2: down_tile<NBW, 2>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
-            case 3: down_tile<NBW, 3>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
-            case 4: down_tile<NBW, 4>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
-            default: down_tile<NBW, kMB>(s_stage, H, wave, lane, ts, c.rows, nbase, s_tok, s_w, accum); break;
+            case 1: down_tile<NBW, 1>(s_stage, H, wave, lane, ts, c.rows, nbase, s_dst, s_w, y); break;
+            case 2: down_tile<NBW, 2>(s_stage, H, wave, lane, ts, c.rows, nbase, s_dst, s_w, y); break;
+            case 3: down_tile<NBW, 3>(s_stage, H, wave, lane, ts, c.rows, nbase, s_dst, s_w, y); break;
+            case 4: down_tile<NBW, 4>(s_stage, H, wave, lane, ts, c.rows, nbase, s_dst, s_w, y); break;
+            default: down_tile<NBW, kMB>(s_stage, H, wave, lane, ts, c.rows, nbase, s_dst, s_w, y); break;
         }
         if (threadIdx.x == 0) s_next = tq.next(ctl, n_mt, NT);
         __syncthreads();
@@ -629,14 +652,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_down(
     release_queues(ctl);
 }
 
-__global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ acc,
-                                                  uint16_t* __restrict__ out, long n) {
-    for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (long)gridDim.x * 256 * 8) {
-        const float4 a = *reinterpret_cast<const float4*>(acc + i);
-        const float4 b = *reinterpret_cast<const float4*>(acc + i + 4);
-        u32x4 o = {pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                   pack_bf16x2(b.z, b.w)};
-        *reinterpret_cast<u32x4*>(out + i) = o;
+__device__ __forceinline__ void add_bf16x8(float (&acc)[8], const u32x4 v) {
+    acc[0] += bf16lo(v.x); acc[1] += bf16hi(v.x); acc[2] += bf16lo(v.y); acc[3] += bf16hi(v.y);
+    acc[4] += bf16lo(v.z); acc[5] += bf16hi(v.z); acc[6] += bf16lo(v.w); acc[7] += bf16hi(v.w);
+}
+
+// out[t][n] = bf16(sum_j y[t*k + j][n] + y[T*k + t][n]), eight columns per thread:
+// the k slot rows of a token are adjacent, so every read is a 16-byte load.
+__global__ __launch_bounds__(256) void k_finalize(const uint16_t* __restrict__ y,
+                                                  uint16_t* __restrict__ out, int T, int H, int k,
+                                                  int has_shared) {
+    const long n8 = (long)T * H / 8;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
+        const long t = i / (H / 8);
+        const int col = (int)(i - t * (H / 8)) * 8;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const uint16_t* row = y + (size_t)t * k * H + col;
+        for (int j = 0; j < k; ++j) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(row + (size_t)j * H);
+            add_bf16x8(acc, v);
+        }
+        if (has_shared) add_bf16x8(acc, *reinterpret_cast<const u32x4*>(y + ((size_t)T * k + t) * H + col));
+        u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                   pack_bf16x2(acc[6], acc[7])};
+        *reinterpret_cast<u32x4*>(out + (size_t)t * H + col) = o;
     }
 }
 
@@ -658,31 +697,31 @@ hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTi
     const int nseg = a.E + (a.has_shared ? 1 : 0);
     // upper bound of M-tiles: every routed row tile-padded, plus one partial per segment
     const long mt_bound = ((long)a.T * a.k) / kBM + nseg + (a.has_shared ? a.T / kBM + 1 : 0);
-    const int slots = 2 * cu_count();      // two 4-wave workgroups per CU
+    const int slots = kWgPerCu * cu_count();
+    const size_t pre_bytes = (size_t)(nseg + 1) * sizeof(int);
     const long gu_tiles = mt_bound * (a.I / (kWaves * 16 * NBW_GU)) + 8;
     const long dn_tiles = mt_bound * (a.H / (kWaves * 16 * NBW_DN)) + 8;
     const int g_gu = (int)(((gu_tiles < slots ? gu_tiles : slots) + 7) / 8 * 8);
     const int g_dn = (int)(((dn_tiles < slots ? dn_tiles : slots) + 7) / 8 * 8);
-    const long acc_elems = (long)a.T * a.H;
 
     tm.before();
-    hipLaunchKernelGGL(k_grouped_gateup<NBW_GU>, dim3(g_gu), dim3(kThreads), 0, st, a.x, a.T,
+    hipLaunchKernelGGL(k_grouped_gateup<NBW_GU>, dim3(g_gu), dim3(kThreads), pre_bytes, st, a.x, a.T,
                        a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.offsets, a.perm,
-                       a.ws_h, a.ws_acc, acc_elems, a.ctl);
+                       a.ws_h, a.ctl);
     tm.after();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL(k_grouped_down<NBW_DN>, dim3(g_dn), dim3(kThreads), 0, st, a.T, a.H, a.I,
+    hipLaunchKernelGGL(k_grouped_down<NBW_DN>, dim3(g_dn), dim3(kThreads), pre_bytes, st, a.T, a.H, a.I,
                        a.E, a.k, a.routed, a.shared, a.has_shared, a.topk_w, a.offsets, a.perm,
-                       a.ws_h, a.ws_acc, a.ctl);
+                       a.ws_h, a.ws_y, a.ctl);
     tm.after();
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const long nblk = (acc_elems / 8 + 255) / 256;
+    const long nblk = ((long)a.T * a.H / 8 + 255) / 256;
     tm.before();
-    hipLaunchKernelGGL(k_finalize, dim3((unsigned)(nblk < 2048 ? nblk : 2048)), dim3(256), 0, st,
-                       a.ws_acc, a.out, acc_elems);
+    hipLaunchKernelGGL(k_finalize, dim3((unsigned)(nblk < 4096 ? nblk : 4096)), dim3(256), 0, st,
+                       a.ws_y, a.out, a.T, a.H, a.k, a.has_shared);
     tm.after();
     return hipGetLastError();
 }

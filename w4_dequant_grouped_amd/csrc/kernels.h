@@ -51,7 +51,9 @@ struct ForwardArgs {
     const int32_t* perm;     // [T*k]
     uint16_t* out;           // [T][H] bf16
     uint16_t* ws_h;          // [T*k + T][I] bf16: expert-sorted rows, then shared rows
-    float* ws_acc;           // [T][H] fp32 (grouped path)
+    uint16_t* ws_y;          // [T*k + T][H] bf16 (grouped path): each routed (token, slot)
+                             // row's weighted expert output at row t*k + j, then the
+                             // shared expert's row of token t at row T*k + t
     uint32_t* ctl;           // workspace control block (zero between calls)
 };
 

@@ -19,7 +19,7 @@ constexpr size_t kCtrlBytes = MOE_W4_CONTROL_BYTES;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t logits, planes, h, acc, total;
+    size_t logits, planes, h, y, total;
 };
 
 bool dims_ok(const moe_w4_dims* d, int* status) {
@@ -46,8 +46,8 @@ Layout layout(const moe_w4_dims* d) {
     if (d->T > moe_w4::kSmallRouteMaxT) off = align_up(off + 3 * E * (size_t)d->H * 2);
     L.h = off;
     off = align_up(off + (T * (size_t)d->top_k + T) * (size_t)d->I * 2);
-    L.acc = off;
-    off = align_up(off + T * (size_t)d->H * sizeof(float));
+    L.y = off;        // grouped path: per-(token, slot) output rows; decode block: slot table
+    off = align_up(off + (T * (size_t)d->top_k + T) * (size_t)d->H * 2);
     L.total = off;
     return L;
 }
@@ -173,7 +173,7 @@ hipError_t run_forward(const moe_w4_dims* dims, const void* x, const moe_w4_weig
     a.perm = perm;
     a.out = static_cast<uint16_t*>(out);
     a.ws_h = reinterpret_cast<uint16_t*>(ws + L.h);
-    a.ws_acc = reinterpret_cast<float*>(ws + L.acc);
+    a.ws_y = reinterpret_cast<uint16_t*>(ws + L.y);
     a.ctl = reinterpret_cast<uint32_t*>(ws);
     return (a.T <= MOE_W4_DECODE_MAX_T) ? moe_w4::launch_forward_decode(a, stream, tm)
                                         : moe_w4::launch_forward_grouped(a, stream, tm);
@@ -281,7 +281,7 @@ int moe_w4_block_timed(const moe_w4_dims* dims, const void* x, const float* rout
         a.logits = reinterpret_cast<float*>(ws + L.logits);
         a.h = reinterpret_cast<uint16_t*>(ws + L.h);
         // the decode path has no fp32 accumulator: its region holds the slot table
-        a.slots = reinterpret_cast<int32_t*>(ws + L.acc);
+        a.slots = reinterpret_cast<int32_t*>(ws + L.y);
         const hipError_t err = moe_w4::launch_block_decode(a, stream, tm);
         if (n_kernels) *n_kernels = tm.count;
         return launch_status(err);
