@@ -195,14 +195,11 @@ __device__ __forceinline__ void release_queues(uint32_t* ctl) {
 //   Every operand byte of a K chunk -- the kBM activation rows (A), the
 //   wavefront's packed weight rows (B codes) and their group scale/bias words --
 //   is copied global -> LDS by the direct global_load_lds path, issued through
-//   inline assembly.  The loop therefore holds no load the compiler tracks: the
-//   only waits on the copies are the explicit vmcnt waits, which count exactly
-//   the copies issued after the chunk being consumed (a compiler-tracked load
-//   among untracked copies would make the compiler's own waits drain later
-//   chunks too, collapsing the pipeline).  kStages buffers form a ring: while
-//   chunk c is multiplied, chunks c+1 .. c+kStages-2 are in flight and chunk
-//   c+kStages-1 is being issued.  A rows are gathered by token on the fly and
-//   stored XOR-swizzled by row, which keeps the MFMA operand reads conflict-free.
+//   inline assembly, into one of two stages: while chunk c is multiplied from
+//   one stage, chunk c+1 is copied into the other.  The loop holds no load the
+//   compiler tracks, and its only waits on the copies are explicit.  A rows are
+//   gathered by token on the fly and stored XOR-swizzled by row, which keeps the
+//   MFMA operand reads conflict-free.
 // ---------------------------------------------------------------------------
 constexpr int kARow = kKC * 2;                     // bytes of one A row per chunk (256)
 constexpr int kABuf = kBM * kARow;                 // A bytes per stage (16 KiB)
@@ -216,7 +213,6 @@ constexpr int kStageBytes = kABuf + kBBuf + kSBBuf;
 constexpr int kStages = 2;                         // 50 KiB: three workgroups share a CU's 160 KiB
 constexpr int kRowsPerWaveDma = kBM / kWaves;      // A rows copied by each wavefront
 constexpr int kDmaPerWave = kRowsPerWaveDma / 4;   // 4 rows (1 KiB) per A copy instruction
-constexpr int kLoadsPerChunk = kDmaPerWave + kBlkPerWave + 1;   // copies per wavefront per chunk
 
 // Per-tile copy addressing.  The bases are wave-uniform (SGPRs, advanced per
 // chunk with scalar adds); the lane offsets are computed once per tile, so a
@@ -360,15 +356,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Wait until this wavefront's copies of a chunk have landed, given how many whole
-// chunks it has issued after it (copies complete in order).
-__device__ __forceinline__ void wait_chunk(int after, bool has_a) {
-    static_assert(kStages == 2 || kStages == 3, "at most one chunk is issued after the one consumed");
-    if (kStages == 2 || after <= 0) wait_vmcnt<0>();
-    else if (has_a) wait_vmcnt<kLoadsPerChunk>();
-    else wait_vmcnt<kLoadsPerChunk - kDmaPerWave>();
-}
-
 // One K chunk of MFMAs over MB valid 16-row blocks (compile-time, so each step
 // is branch-free and the A-fragment reads of a step are issued together).
 template <int NMAT, int NBW, int MB>
@@ -418,29 +405,36 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const uint8_t* s_b
     }
 }
 
-// K-loop over the ring.  Iteration c waits for chunk c (the copies issued after it
-// are those of the at most kStages-2 later chunks already in flight), then a
-// barrier makes every wavefront's part visible and frees the stage read in
-// iteration c-1, which receives chunk c+kStages-1.  Nothing is copied past the
-// end of K.
+// K-loop over the two-stage ring.  Iteration c waits for this wavefront's copies
+// (vmcnt 0), then a barrier makes every wavefront's part of chunk c visible and
+// frees the stage read in iteration c-1, which receives chunk c+1 while chunk c
+// is multiplied.  The loop is unrolled by two so that each stage's LDS offsets
+// are compile-time constants.  Nothing is copied past the end of K.
+template <int NMAT, int NBW, int MB, int ST>
+__device__ __forceinline__ void kloop_step(uint8_t* s_stage, uint32_t ring, int wave, int lane,
+                                           const TileSrc<NMAT, NBW>& t, int c, int nch, bool has_a,
+                                           f32x4 (&acc)[MB][NMAT][NBW]) {
+    wait_vmcnt<0>();
+    __syncthreads();           // chunk c visible to all; the other stage is free
+    if (c + 1 < nch) issue_chunk(ring, wave, t, c + 1, has_a);
+    mma_chunk<NMAT, NBW, MB>(s_stage + off_a(ST), s_stage + off_b(ST, wave), s_stage + off_sb(ST, wave),
+                             lane, acc);
+}
+
 template <int NMAT, int NBW, int MB>
 __device__ __forceinline__ void tile_kloop(uint8_t* s_stage, int wave, int lane,
                                            const TileSrc<NMAT, NBW>& t,
                                            f32x4 (&acc)[MB][NMAT][NBW]) {
-    constexpr int D = kStages;
+    static_assert(kStages == 2, "the loop below alternates two stages");
     const bool has_a = wave < MB;          // wave w copies rows [16 w, 16 w + 16)
     const int nch = t.K / kKC;
     const uint32_t ring = lds_addr(s_stage);
-    for (int c = 0; c < D - 1 && c < nch; ++c) issue_chunk(ring, wave, t, c, has_a);
-    for (int c = 0; c < nch; ++c) {
-        wait_chunk(min(D - 2, nch - 1 - c), has_a);
-        __syncthreads();       // chunk c visible to all; the stage of chunk c-1 is free
-        if (c + D - 1 < nch) issue_chunk(ring, wave, t, c + D - 1, has_a);
-        const int st = c % D;
-        mma_chunk<NMAT, NBW, MB>(s_stage + off_a(st), s_stage + off_b(st, wave),
-                                 s_stage + off_sb(st, wave), lane, acc);
+    issue_chunk(ring, wave, t, 0, has_a);
+    for (int c = 0; c < nch; c += 2) {
+        kloop_step<NMAT, NBW, MB, 0>(s_stage, ring, wave, lane, t, c, nch, has_a, acc);
+        if (c + 1 < nch) kloop_step<NMAT, NBW, MB, 1>(s_stage, ring, wave, lane, t, c + 1, nch, has_a, acc);
     }
-    __syncthreads();           // all stages free for the next tile
+    __syncthreads();           // both stages free for the next tile
 }
 
 // ---------------------------------------------------------------------------
