@@ -12,8 +12,9 @@ value = MoE-layer tokens per second = 40 * T * steps / elapsed.
 
 The same line carries:
   roofline      the dominant kernel's algorithmic bytes (or flops) per launch over
-                its average duration, timed with HIP events recorded around each
-                kernel on the launch stream in a second pass over the same steps
+                its average duration, timed with HIP events that the library passes
+                to each kernel's dispatch as start/stop events (hipExtLaunchKernelGGL)
+                in a second pass over the same steps
   cpu_baseline  the CPU oracle (float64 NumPy) timed on a bounded sample of the
                 same workload on this host
   prefill       the T=2048 Zipf-skewed prefill layer-call (8 layers rotated):
@@ -42,8 +43,8 @@ FWD_GROUPED = ["grouped_gateup", "grouped_down", "finalize"]
 
 
 # ---------------------------------------------------------------------------
-# HIP events through the runtime's C API (the library launches on the stream
-# passed to it; events recorded there bracket its kernels)
+# HIP events through the runtime's C API (the library dispatches each timed
+# kernel with one event pair as its start/stop events)
 # ---------------------------------------------------------------------------
 class HipEvents:
     def __init__(self):
@@ -52,12 +53,6 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-
-    def record(self, e, stream):
-        rc = self.hip.hipEventRecord(e, stream)
-        if rc != 0:
-            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
     def create(self, n):
         evs = []
@@ -132,21 +127,15 @@ def time_steps(step_fn, steps, warmup):
 def kernel_times(blocks, xs, steps, ev: HipEvents, names, timed):
     """Average duration per kernel name over `steps` passes over all blocks.
 
-    ``timed(block, x, events)`` runs one block call recording an event pair
-    around each kernel and returns the kernel count.  Before each block call an
-    empty event pair is recorded on the same stream; its average span is the
-    cost the two event records add around a kernel, and is subtracted.
-    Returns (kernel_us, raw_kernel_us, empty_pair_us)."""
+    ``timed(block, x, events)`` runs one block call with an event pair per kernel
+    and returns the kernel count.  The library dispatches each kernel with its
+    pair as start/stop events (hipExtLaunchKernelGGL), so a pair spans that
+    kernel's own execution, as rocprofv3's kernel trace does."""
     import torch
     n = len(names)
-    stream = torch.cuda.current_stream().cuda_stream
-    events, empties = [], []
+    events = []
     for s in range(steps):
         for l, blk in enumerate(blocks):
-            z = ev.create(2)
-            ev.record(z[0], stream)
-            ev.record(z[1], stream)
-            empties.append(z)
             e = ev.create(2 * n)
             got = timed(blk, xs[s % len(xs)][l], e)
             assert got == n, (got, names)
@@ -157,13 +146,7 @@ def kernel_times(blocks, xs, steps, ev: HipEvents, names, timed):
         for i, name in enumerate(names):
             sums[name] += ev.elapsed_ms(e[2 * i], e[2 * i + 1])
         ev.destroy(e)
-    empty = 0.0
-    for z in empties:
-        empty += ev.elapsed_ms(z[0], z[1])
-        ev.destroy(z)
-    empty_us = 1e3 * empty / len(empties)
-    raw = {name: 1e3 * v / len(events) for name, v in sums.items()}   # microseconds per launch
-    return {name: max(v - empty_us, 0.0) for name, v in raw.items()}, raw, empty_us
+    return {name: 1e3 * v / len(events) for name, v in sums.items()}   # microseconds per launch
 
 
 def split_timed(nr):
@@ -204,8 +187,8 @@ def run_decode(args, ev):
     value = L * T * args.steps / elapsed
 
     names = BLOCK_DECODE
-    kt, kt_raw, pair_us = kernel_times(blocks, xs, min(args.steps, 10), ev, names,
-                                       lambda blk, x, e: blk.block_timed(x, e))
+    kt = kernel_times(blocks, xs, min(args.steps, 10), ev, names,
+                      lambda blk, x, e: blk.block_timed(x, e))
     # algorithmic bytes per launch from the routing each layer produced
     gu_b, dn_b = expert_bytes(H, I)
     active = []
@@ -229,8 +212,6 @@ def run_decode(args, ev):
         "traffic": traffic_from_profiles(dom, "decode"),
         "alg_bytes_per_launch": int(alg[dom]), "avg_launch_us": round(kt[dom], 3),
         "kernel_us": {n: round(v, 3) for n, v in kt.items()},
-        "kernel_us_event_pairs_raw": {n: round(v, 3) for n, v in kt_raw.items()},
-        "empty_event_pair_us": round(pair_us, 3),
         "layer_call_alg_bytes": int(layer_bytes),
         "layer_call_hbm_frac": round(layer_bytes / (ms_per_step / L * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "active_experts_per_call": n_act,
@@ -260,8 +241,7 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
 
     elapsed = time_steps(step, steps, warmup)
     per_call_ms = 1e3 * elapsed / (steps * L)
-    kt, kt_raw, pair_us = kernel_times(blocks, xs, steps, ev, ROUTE_LARGE + FWD_GROUPED,
-                                       split_timed(len(ROUTE_LARGE)))
+    kt = kernel_times(blocks, xs, steps, ev, ROUTE_LARGE + FWD_GROUPED, split_timed(len(ROUTE_LARGE)))
     rows = T * k + T
     flops = {"grouped_gateup": 2.0 * rows * H * 2 * I, "grouped_down": 2.0 * rows * I * H}
     dom = max(flops, key=lambda n: kt[n])
@@ -277,9 +257,7 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_from_profiles(dom, "prefill"),
                      "alg_flops_per_launch": flops[dom], "avg_launch_us": round(kt[dom], 3),
-                     "kernel_us": {n: round(v, 3) for n, v in kt.items()},
-                     "kernel_us_event_pairs_raw": {n: round(v, 3) for n, v in kt_raw.items()},
-                     "empty_event_pair_us": round(pair_us, 3)},
+                     "kernel_us": {n: round(v, 3) for n, v in kt.items()}},
     }
 
 

@@ -182,11 +182,12 @@ int moe_w4_block(const moe_w4_dims* dims, const void* x,
 
 /*
  * The same calls with per-kernel timing.  When `events` is not NULL it holds
- * `capacity` hipEvent_t handles created by the caller; the call records
- * events[2i] on `hip_stream` just before, and events[2i+1] just after, the i-th
- * kernel it launches (while 2i+1 < capacity).  *n_kernels (if not NULL) receives
- * the number of kernels launched.  Everything else is as for moe_w4_route() and
- * moe_w4_forward().  Used to time each kernel with HIP events.
+ * `capacity` hipEvent_t handles created by the caller; the i-th kernel the call
+ * launches (while 2i+1 < capacity) is dispatched with events[2i] and
+ * events[2i+1] as its start and stop events (hipExtLaunchKernelGGL), so
+ * hipEventElapsedTime on the pair gives that kernel's own execution time.
+ * *n_kernels (if not NULL) receives the number of kernels launched.  Everything
+ * else is as for moe_w4_route() and moe_w4_forward().
  */
 int moe_w4_route_timed(const moe_w4_dims* dims,
                        const void* x, const float* router_w, const float* router_b,

@@ -366,13 +366,13 @@ static hipError_t decode_t(const ForwardArgs& a, hipStream_t st, KernelTimer& tm
     const int max_slots = min(a.E, a.T * a.k) + (a.has_shared ? 1 : 0);
     dim3 g1(max_slots, a.I / gu_rows_per_block<TMAX>());
     tm.before();
-    hipLaunchKernelGGL(k_decode_gateup<TMAX>, g1, dim3(256), 0, st, a.x, a.T, a.H, a.I, a.E, a.k,
+    tm.launch(k_decode_gateup<TMAX>, g1, dim3(256), 0, st, a.x, a.T, a.H, a.I, a.E, a.k,
                        a.routed, a.shared, a.has_shared, a.offsets, a.perm, a.ws_h);
     tm.after();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL(k_decode_down<TMAX>, dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T,
+    tm.launch(k_decode_down<TMAX>, dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T,
                        a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.topk_w, a.offsets,
                        a.perm, a.ws_h, a.out, nullptr);
     tm.after();
@@ -560,18 +560,18 @@ static hipError_t block_decode_t(const DecodeBlockArgs& a, hipStream_t st, Kerne
     const int nlog = (a.E + 3) / 4;
     const int nsh = a.has_shared ? a.I / gu_rows_per_block<TMAX>() : 0;
     tm.before();
-    hipLaunchKernelGGL(k_decode_logits_shared<TMAX>, dim3(nlog + nsh), dim3(256), 0, st, a);
+    tm.launch(k_decode_logits_shared<TMAX>, dim3(nlog + nsh), dim3(256), 0, st, a);
     tm.after();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL((k_decode_route_gateup<TMAX, EPL>),
+    tm.launch((k_decode_route_gateup<TMAX, EPL>),
                        dim3(min(a.E, a.T * a.k) + 1, a.I / gu_rows_per_block<TMAX>()), dim3(256), 0, st, a);
     tm.after();
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL(k_decode_down<TMAX>, dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T,
+    tm.launch(k_decode_down<TMAX>, dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T,
                        a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.tw, a.offsets,
                        a.perm, a.h, a.out, a.slots);
     tm.after();

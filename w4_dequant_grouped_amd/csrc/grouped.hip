@@ -699,14 +699,14 @@ hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTi
     const int g_dn = (int)(((dn_tiles < slots ? dn_tiles : slots) + 7) / 8 * 8);
 
     tm.before();
-    hipLaunchKernelGGL(k_grouped_gateup<NBW_GU>, dim3(g_gu), dim3(kThreads), pre_bytes, st, a.x, a.T,
+    tm.launch(k_grouped_gateup<NBW_GU>, dim3(g_gu), dim3(kThreads), pre_bytes, st, a.x, a.T,
                        a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.offsets, a.perm,
                        a.ws_h, a.ctl);
     tm.after();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL(k_grouped_down<NBW_DN>, dim3(g_dn), dim3(kThreads), pre_bytes, st, a.T, a.H, a.I,
+    tm.launch(k_grouped_down<NBW_DN>, dim3(g_dn), dim3(kThreads), pre_bytes, st, a.T, a.H, a.I,
                        a.E, a.k, a.routed, a.shared, a.has_shared, a.topk_w, a.offsets, a.perm,
                        a.ws_h, a.ws_y, a.ctl);
     tm.after();
@@ -714,7 +714,7 @@ hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTi
     if (err != hipSuccess) return err;
     const long nblk = ((long)a.T * a.H / 8 + 255) / 256;
     tm.before();
-    hipLaunchKernelGGL(k_finalize, dim3((unsigned)(nblk < 4096 ? nblk : 4096)), dim3(256), 0, st,
+    tm.launch(k_finalize, dim3((unsigned)(nblk < 4096 ? nblk : 4096)), dim3(256), 0, st,
                        a.ws_y, a.out, a.T, a.H, a.k, a.has_shared);
     tm.after();
     return hipGetLastError();

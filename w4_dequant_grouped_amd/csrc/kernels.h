@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -84,17 +85,29 @@ struct DecodeBlockArgs {     // route + forward of decode rows (T <= kDecodeMaxT
 
 // Optional per-kernel timing: events[2i] / events[2i+1] are recorded on the launch
 // stream before / after the i-th kernel of a call (while capacity allows).
+// Launches kernels and, when the caller supplies events, brackets each one with
+// an event pair.  The pair is handed to hipExtLaunchKernelGGL, so the events take
+// the dispatch's own begin and end timestamps (no separate event packets around
+// the kernel).  before() arms the next launch, after() closes the pair.
 struct KernelTimer {
     hipEvent_t* events = nullptr;
     int capacity = 0;
     int count = 0;
-    hipStream_t stream = nullptr;
-    void before() {
-        if (events && 2 * count + 1 < capacity) (void)hipEventRecord(events[2 * count], stream);
-    }
+    bool armed = false;
+    void before() { armed = true; }
     void after() {
-        if (events && 2 * count + 1 < capacity) (void)hipEventRecord(events[2 * count + 1], stream);
+        armed = false;
         ++count;
+    }
+    template <typename F, typename... Args>
+    void launch(F kernel, const dim3& grid, const dim3& block, uint32_t shmem, hipStream_t st,
+                Args... args) {
+        hipEvent_t start = nullptr, stop = nullptr;
+        if (armed && events && 2 * count + 1 < capacity) {
+            start = events[2 * count];
+            stop = events[2 * count + 1];
+        }
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, start, stop, 0u, args...);
     }
 };
 

@@ -114,11 +114,10 @@ int check_forward(const moe_w4_dims* dims, const void* x, const moe_w4_weights* 
     return MOE_W4_OK;
 }
 
-moe_w4::KernelTimer make_timer(void** events, int capacity, hipStream_t stream) {
+moe_w4::KernelTimer make_timer(void** events, int capacity) {
     moe_w4::KernelTimer tm;
     tm.events = reinterpret_cast<hipEvent_t*>(events);
     tm.capacity = events ? capacity : 0;
-    tm.stream = stream;
     return tm;
 }
 
@@ -194,7 +193,7 @@ int moe_w4_route_timed(const moe_w4_dims* dims, const void* x, const float* rout
                      perm, workspace, workspace_bytes);
     if (st != MOE_W4_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    moe_w4::KernelTimer tm = make_timer(events, capacity, stream);
+    moe_w4::KernelTimer tm = make_timer(events, capacity);
     const hipError_t err = run_route(dims, x, router_w, router_b, topk_ids, topk_w, expert_counts,
                                      expert_offsets, perm, workspace, stream, tm);
     if (n_kernels) *n_kernels = tm.count;
@@ -224,7 +223,7 @@ int moe_w4_forward_timed(const moe_w4_dims* dims, const void* x, const moe_w4_we
                        workspace_bytes);
     if (st != MOE_W4_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    moe_w4::KernelTimer tm = make_timer(events, capacity, stream);
+    moe_w4::KernelTimer tm = make_timer(events, capacity);
     const hipError_t err = run_forward(dims, x, routed, shared, topk_w, expert_offsets, perm, out,
                                        workspace, stream, tm);
     if (n_kernels) *n_kernels = tm.count;
@@ -256,7 +255,7 @@ int moe_w4_block_timed(const moe_w4_dims* dims, const void* x, const float* rout
                        workspace_bytes);
     if (st != MOE_W4_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    moe_w4::KernelTimer tm = make_timer(events, capacity, stream);
+    moe_w4::KernelTimer tm = make_timer(events, capacity);
     if (dims->T <= moe_w4::kBlockDecodeMaxT) {
         const Layout L = layout(dims);
         uint8_t* ws = static_cast<uint8_t*>(workspace);

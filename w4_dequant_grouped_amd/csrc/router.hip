@@ -402,22 +402,22 @@ __global__ __launch_bounds__(kGroupThreads) void k_router_group(const int32_t* _
 // launchers
 // ---------------------------------------------------------------------------
 template <int EPL>
-static void route_small_epl(const RouteArgs& a, hipStream_t st) {
+static void route_small_epl(const RouteArgs& a, hipStream_t st, KernelTimer& tm) {
     if (a.T <= 1)
-        hipLaunchKernelGGL((k_route_small<1, EPL>), dim3(kSmallRouteBlocks), dim3(kSmallRouteThreads),
+        tm.launch((k_route_small<1, EPL>), dim3(kSmallRouteBlocks), dim3(kSmallRouteThreads),
                            0, st, a.x, a.Wr, a.br, a.T, a.H, a.E, a.k, a.ids, a.w, a.counts,
                            a.offsets, a.perm, a.ws_logits, a.ws_ticket);
     else
-        hipLaunchKernelGGL((k_route_small<kSmallRouteMaxT, EPL>), dim3(kSmallRouteBlocks),
+        tm.launch((k_route_small<kSmallRouteMaxT, EPL>), dim3(kSmallRouteBlocks),
                            dim3(kSmallRouteThreads), 0, st, a.x, a.Wr, a.br, a.T, a.H, a.E, a.k,
                            a.ids, a.w, a.counts, a.offsets, a.perm, a.ws_logits, a.ws_ticket);
 }
 
 hipError_t launch_route_small(const RouteArgs& a, hipStream_t st, KernelTimer& tm) {
     tm.before();
-    if (a.E <= 256) route_small_epl<4>(a, st);
-    else if (a.E <= 512) route_small_epl<8>(a, st);
-    else route_small_epl<16>(a, st);
+    if (a.E <= 256) route_small_epl<4>(a, st, tm);
+    else if (a.E <= 512) route_small_epl<8>(a, st, tm);
+    else route_small_epl<16>(a, st, tm);
     tm.after();
     return hipGetLastError();
 }
@@ -425,13 +425,13 @@ hipError_t launch_route_small(const RouteArgs& a, hipStream_t st, KernelTimer& t
 hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& tm) {
     const long n = (long)a.E * a.H;
     tm.before();
-    hipLaunchKernelGGL(k_router_split, dim3((unsigned)min((n / 4 + 255) / 256, 1024L)), dim3(256), 0, st,
+    tm.launch(k_router_split, dim3((unsigned)min((n / 4 + 255) / 256, 1024L)), dim3(256), 0, st,
                        a.Wr, n, a.ws_planes);
     tm.after();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL(k_router_logits_mfma,
+    tm.launch(k_router_logits_mfma,
                        dim3((a.E + kLgExp - 1) / kLgExp, (a.T + kLgTok - 1) / kLgTok, kRouterKSplit),
                        dim3(256), 0, st, a.x, a.ws_planes, a.T, a.H, a.E, a.ws_logits);
     tm.after();
@@ -439,19 +439,19 @@ hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& t
     if (err != hipSuccess) return err;
     tm.before();
     if (a.E <= 256)
-        hipLaunchKernelGGL(k_router_topk<4>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
+        tm.launch(k_router_topk<4>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
                            a.T, a.E, a.k, a.ids, a.w);
     else if (a.E <= 512)
-        hipLaunchKernelGGL(k_router_topk<8>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
+        tm.launch(k_router_topk<8>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
                            a.T, a.E, a.k, a.ids, a.w);
     else
-        hipLaunchKernelGGL(k_router_topk<16>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
+        tm.launch(k_router_topk<16>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
                            a.T, a.E, a.k, a.ids, a.w);
     tm.after();
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    hipLaunchKernelGGL(k_router_group, dim3(a.E), dim3(kGroupThreads), 0, st, a.ids, a.T, a.E, a.k, a.counts,
+    tm.launch(k_router_group, dim3(a.E), dim3(kGroupThreads), 0, st, a.ids, a.T, a.E, a.k, a.counts,
                        a.offsets, a.perm);
     tm.after();
     return hipGetLastError();
