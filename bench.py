@@ -124,6 +124,59 @@ def time_steps(step_fn, steps, warmup):
     return time.perf_counter() - t0
 
 
+class DecodeGraph:
+    """One decode step (every layer's block call) captured as a HIP graph.
+
+    Each layer reads its activations from a fixed input buffer; a step copies that
+    step's activations in (one device copy) and replays the graph.  Before it is
+    used, every replay is checked against the eager step on the same inputs, with
+    eager work and synchronisation between the replays."""
+
+    def __init__(self, blocks, T, H):
+        import torch
+        self.blocks = blocks
+        L = len(blocks)
+        self.x = torch.zeros((L, T, H), dtype=torch.bfloat16, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self._body()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._body()
+        torch.cuda.synchronize()
+
+    def _body(self):
+        for l, blk in enumerate(self.blocks):
+            blk(self.x[l])
+
+    def step(self, xstack):
+        self.x.copy_(xstack)
+        self.graph.replay()
+
+    def eager(self, xstack):
+        self.x.copy_(xstack)
+        self._body()
+
+    def check(self, xa, xb, replays=3):
+        """Replays on xa must equal the eager step on xa bit for bit; an eager step
+        on xb runs between replays."""
+        import torch
+        self.eager(xa)
+        torch.cuda.synchronize()
+        ref = [blk.out.clone() for blk in self.blocks]
+        for r in range(replays):
+            self.step(xa)
+            torch.cuda.synchronize()
+            for l, blk in enumerate(self.blocks):
+                if not torch.equal(blk.out, ref[l]):
+                    raise RuntimeError(f"graph replay {r} differs from the eager step at layer {l}")
+            self.eager(xb)
+            torch.cuda.synchronize()
+
+
 def kernel_times(blocks, xs, steps, ev: HipEvents, names, timed):
     """Average duration per kernel name over `steps` passes over all blocks.
 
@@ -170,17 +223,24 @@ def run_decode(args, ev):
     blocks = [B.Block(layer, T, k, workspace=ws) for layer in layers]
     nx = args.steps + args.warmup
     g = synth.generator(77, "cuda")
-    xs = [[torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16) for _ in range(L)]
-          for _ in range(nx)]
+    xstk = torch.randn((nx, L, T, H), generator=g, device="cuda").to(torch.bfloat16)
+    xs = [[xstk[i, l] for l in range(L)] for i in range(nx)]
 
     split = getattr(args, "entry", "block") == "split"
+    use_graph = not split and not getattr(args, "no_graph", False)
+    if use_graph:
+        dg = DecodeGraph(blocks, T, H)
+        dg.check(xstk[0], xstk[1 % nx])
 
-    def step(i=0):
-        for l, blk in enumerate(blocks):
-            if split:
-                blk.split(xs[i % nx][l])
-            else:
-                blk(xs[i % nx][l])
+        def step(i=0):
+            dg.step(xstk[i % nx])
+    else:
+        def step(i=0):
+            for l, blk in enumerate(blocks):
+                if split:
+                    blk.split(xs[i % nx][l])
+                else:
+                    blk(xs[i % nx][l])
 
     elapsed = time_steps(step, args.steps, args.warmup)
     ms_per_step = 1e3 * elapsed / args.steps
@@ -218,7 +278,9 @@ def run_decode(args, ev):
     }
     config = {"workload": f"decode T={T} (40-layer rotation), H={H}, I={I}, E={E} top-{k} + shared, "
                           f"W4 group 64", "T": T, "H": H, "I": I, "E": E, "top_k": k,
-              "layers": L, "shared_expert": True}
+              "layers": L, "shared_expert": True,
+              "step": "hip graph of the 40 block calls (replays checked against eager)" if use_graph
+              else ("route + forward calls" if split else "eager block calls")}
     return value, ms_per_step, roofline, config
 
 
@@ -261,6 +323,74 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
     }
 
 
+def run_stack(args, ev):
+    """The 40-layer stack: T=16384 prefill through 40 independently seeded layers
+    (Zipf-biased routers, the same activations into every layer, no chaining),
+    then T=1 decode steps over the same 40 layers as one captured graph."""
+    import torch
+    from w4_dequant_grouped_amd import moe_w4 as B
+    from w4_dequant_grouped_amd import synth
+
+    T, H, I, E, k, L = args.stack_tokens, 2048, 512, 256, 8, 40
+    shape = synth.BlockShape(T=T, H=H, I=I, E=E, top_k=k, router_bias="zipf")
+    layers = make_layers(shape, L, 4000, "cuda")
+    gu_b, dn_b = expert_bytes(H, I)
+    per_expert = 2 * gu_b + dn_b
+
+    # prefill
+    ws = B.alloc_workspace(B.make_dims(T, H, I, E, k))
+    blocks = [B.Block(layer, T, k, workspace=ws) for layer in layers]
+    x = torch.randn((T, H), generator=synth.generator(4, "cuda"), device="cuda").to(torch.bfloat16)
+
+    def pstep(i=0):
+        for blk in blocks:
+            blk(x)
+
+    steps = 3
+    elapsed = time_steps(pstep, steps, 1)
+    stack_s = elapsed / steps
+    active = [int((blk.routing.counts > 0).sum().item()) for blk in blocks]
+    flops = 6.0 * (T * k + T) * H * I * L          # bf16 expert GEMMs
+    pbytes = sum(E * H * 4 + (a + 1) * per_expert + 2 * T * H * 2 for a in active)
+    kt = kernel_times(blocks, [[x] * L], 1, ev, ROUTE_LARGE + FWD_GROUPED, split_timed(len(ROUTE_LARGE)))
+    gemm_flops = {"grouped_gateup": 2.0 * (T * k + T) * H * 2 * I, "grouped_down": 2.0 * (T * k + T) * I * H}
+    prefill = {
+        "T": T, "stack_ms": round(1e3 * stack_s, 3), "ms_per_layer": round(1e3 * stack_s / L, 4),
+        "tokens_per_s": round(T / stack_s, 1),
+        "mfma_frac": round(flops / stack_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "alg_GBps": round(pbytes / stack_s / 1e9, 1),
+        "kernel_us": {n: round(v, 3) for n, v in kt.items()},
+        "gemm_mfma_frac": {n: round(f / (kt[n] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+                           for n, f in gemm_flops.items()},
+        "active_experts_per_layer": sum(active) / L,
+    }
+    del blocks, ws
+    torch.cuda.empty_cache()
+
+    # decode
+    nd, warm = args.stack_decode_steps, 5
+    ws1 = B.alloc_workspace(B.make_dims(1, H, I, E, k))
+    dblocks = [B.Block(layer, 1, k, workspace=ws1) for layer in layers]
+    xstk = torch.randn((nd + warm, L, 1, H), generator=synth.generator(5, "cuda"),
+                       device="cuda").to(torch.bfloat16)
+    dg = DecodeGraph(dblocks, 1, H)
+    dg.check(xstk[0], xstk[1])
+    elapsed = time_steps(lambda i=0: dg.step(xstk[i % (nd + warm)]), nd, warm)
+    step_s = elapsed / nd
+    dact = [int((blk.routing.counts > 0).sum().item()) for blk in dblocks]
+    dbytes = sum(E * H * 4 + (a + 1) * per_expert + 2 * H * 2 for a in dact)
+    decode = {
+        "steps": nd, "us_per_step": round(1e6 * step_s, 2), "us_per_layer": round(1e6 * step_s / L, 3),
+        "layer_tokens_per_s": round(L / step_s, 1),
+        "alg_GBps": round(dbytes / step_s / 1e9, 1),
+        "hbm_frac": round(dbytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    return {"workload": f"stack of 40 seeded layers (Zipf-biased routers): T={T} prefill, "
+                        f"then {nd} T=1 decode steps (captured graph)",
+            "weights_GB": round(L * (E * H * 4 + (E + 1) * per_expert) / 1e9, 2),
+            "prefill": prefill, "decode": decode}
+
+
 def cpu_baseline(T=1, max_calls=24, budget_s=20.0):
     """The oracle as it stands, on this host's cores, on a bounded sample."""
     import numpy as np  # noqa: F401
@@ -299,6 +429,12 @@ def main():
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the decode step as eager block calls instead of a captured graph")
+    ap.add_argument("--stack", action="store_true",
+                    help="only run the 40-layer stack (T=16384 prefill + T=1 decode steps)")
+    ap.add_argument("--stack-tokens", type=int, default=16384)
+    ap.add_argument("--stack-decode-steps", type=int, default=256)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy (fp32 negate) of MIB MiB three times: the "
                          "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -326,6 +462,12 @@ def main():
         return
     B.load_library()          # raises if the HIP library is missing: there is no fallback
     ev = HipEvents()
+    if args.stack:
+        print("[bench] stack: 40 layers", file=sys.stderr, flush=True)
+        line = {"stack": run_stack(args, ev), "n_gpus": 1, "dtype": "bf16",
+                "data": "synthetic (seeded W4 layers and activations)", "source_hash": source_hash()}
+        print(json.dumps(line), flush=True)
+        return
 
     print(f"[bench] decode: {args.layers} layers, T={args.tokens}, steps={args.steps}", file=sys.stderr, flush=True)
     value, ms_per_step, roofline, config = run_decode(args, ev)

@@ -256,3 +256,51 @@ def test_boundary_ties_go_to_the_lower_expert(T):
         check_routing(r, ref, f"ties T={T} {'split' if split else 'block'}")
         y = O.forward_grouped(x, layer, ref, shape.group)
         check_output(out, y, what=f"ties T={T}")
+
+
+# --- graph capture ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 2, 64])
+def test_graph_replays_match_eager(full_layer, T):
+    """Two block calls sharing one workspace, captured as a HIP graph: three
+    replays, with eager calls on other inputs and a synchronisation between them,
+    each equal bit for bit to the eager calls on the same inputs; the control
+    block ends all zero."""
+    shape = S(T=T, H=2048, I=512, E=256, top_k=8)
+    layer = full_layer.to("cuda")
+    ws = B.alloc_workspace(B.make_dims(T, 2048, 512, 256, 8))
+    blocks = [B.Block(layer, T, 8, workspace=ws) for _ in range(2)]
+    _, xa = make_inputs(shape, 400 + T, full_layer)
+    _, xb = make_inputs(shape, 500 + T, full_layer)
+    xa, xb = xa.cuda(), xb.cuda()
+    xin = torch.empty_like(xa)
+
+    def body():
+        for blk in blocks:
+            blk(xin)
+
+    xin.copy_(xa)
+    body()
+    torch.cuda.synchronize()
+    ref = [(blk.out.clone(), blk.routing.perm.clone(), blk.routing.ids.clone()) for blk in blocks]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    for rep in range(3):
+        xin.copy_(xa)
+        graph.replay()
+        torch.cuda.synchronize()
+        for (o, p, i), blk in zip(ref, blocks):
+            assert torch.equal(blk.routing.ids, i), f"replay {rep}: ids"
+            assert torch.equal(blk.routing.perm, p), f"replay {rep}: perm"
+            assert torch.equal(blk.out, o), f"replay {rep}: output"
+        xin.copy_(xb)
+        body()
+        torch.cuda.synchronize()
+    assert int(ws[:B.MOE_W4_CONTROL_BYTES].cpu().sum()) == 0

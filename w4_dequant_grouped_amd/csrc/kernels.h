@@ -88,7 +88,8 @@ struct DecodeBlockArgs {     // route + forward of decode rows (T <= kDecodeMaxT
 // Launches kernels and, when the caller supplies events, brackets each one with
 // an event pair.  The pair is handed to hipExtLaunchKernelGGL, so the events take
 // the dispatch's own begin and end timestamps (no separate event packets around
-// the kernel).  before() arms the next launch, after() closes the pair.
+// the kernel); without events the launch is a plain one (and can be captured into
+// a graph).  before() arms the next launch, after() closes the pair.
 struct KernelTimer {
     hipEvent_t* events = nullptr;
     int capacity = 0;
@@ -102,12 +103,11 @@ struct KernelTimer {
     template <typename F, typename... Args>
     void launch(F kernel, const dim3& grid, const dim3& block, uint32_t shmem, hipStream_t st,
                 Args... args) {
-        hipEvent_t start = nullptr, stop = nullptr;
-        if (armed && events && 2 * count + 1 < capacity) {
-            start = events[2 * count];
-            stop = events[2 * count + 1];
-        }
-        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, start, stop, 0u, args...);
+        if (armed && events && 2 * count + 1 < capacity)
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, events[2 * count], events[2 * count + 1],
+                                  0u, args...);
+        else
+            hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
     }
 };
 
