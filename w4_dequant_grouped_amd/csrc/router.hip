@@ -17,6 +17,7 @@
 //    (no atomics, no histogram shared between workgroups).
 #include "device.h"
 #include "kernels.h"
+#include "lds_copy.h"
 #include "topk.h"
 
 namespace moe_w4 {
@@ -272,6 +273,128 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(
         }
 }
 
+// Partial logits over one eighth of H for a tile of 128 tokens x 64 experts, with
+// both operands staged in LDS (used when H/8 is a multiple of 64).  Each 64-k
+// chunk of the 128 activation rows and of the 3 x 64 weight-plane rows is copied
+// global -> LDS by global_load_lds (eight rows of 128 contiguous bytes per
+// instruction, so each instruction reads whole cache lines of eight rows), into
+// one of two stages while the other is multiplied.  Wavefront (i, j) computes
+// tokens 64i..64i+63 x experts 32j..32j+31 (four by two 16x16 blocks, three
+// planes each): per 32-k step, 10 LDS operand reads feed 24 MFMAs.  A row r of a
+// stage holds its 8 pieces of 16 bytes with logical piece p at p ^ ((r>>1)&7),
+// so the 16 rows of an operand read hit 16 distinct 4-bank groups.
+constexpr int kRlTok = 128;                  // tokens per workgroup
+constexpr int kRlExp = 64;                   // experts per workgroup
+constexpr int kRlKC = 64;                    // k per chunk
+constexpr int kRlRow = kRlKC * 2;            // bytes of a row per chunk (128)
+constexpr int kRlARows = kRlTok;             // activation rows per stage
+constexpr int kRlBRows = 3 * kRlExp;         // weight-plane rows per stage
+constexpr int kRlStage = (kRlARows + kRlBRows) * kRlRow;    // 40 KiB
+constexpr int kRlRowsPerCopy = 64 * 16 / kRlRow;            // 8 rows per copy instruction
+constexpr int kRlACopies = kRlARows / kRlRowsPerCopy / 4;   // per wavefront (4)
+constexpr int kRlBCopies = kRlBRows / kRlRowsPerCopy / 4;   // per wavefront (6)
+
+__device__ __forceinline__ int rl_swz(int r) { return (r >> 1) & 7; }
+
+__global__ __launch_bounds__(256, 2) void k_router_logits_lds(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes, int T, int H, int E,
+    float* __restrict__ partial) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[2 * kRlStage];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = (int)uniform32(threadIdx.x / kWave);
+    const int wi = wave >> 1, wj = wave & 1;
+    const int tbase = blockIdx.y * kRlTok;
+    const int e0 = blockIdx.x * kRlExp;
+    const int ks = H / kRouterKSplit;          // a multiple of kRlKC here
+    const int kbeg = blockIdx.z * ks;
+    const size_t plane = (size_t)E * H;
+    const uint32_t ring = lds_addr(s_stage);
+
+    // copy addressing: lane L fills position L&7 of stage row 8q + (L>>3) of copy q
+    // with its logical piece; rows past T or E re-read the last valid row
+    const uint64_t xbase = uniform64((uint64_t)(x + kbeg));
+    const uint64_t wbase = uniform64((uint64_t)(planes + kbeg));
+    uint32_t a_off[kRlACopies];
+    uint64_t b_off[kRlBCopies];
+#pragma unroll
+    for (int i = 0; i < kRlACopies; ++i) {
+        const int row = (wave * kRlACopies + i) * kRlRowsPerCopy + (lane >> 3);
+        const int logical = (lane & 7) ^ rl_swz(row);
+        a_off[i] = (uint32_t)min(tbase + row, T - 1) * (uint32_t)(H * 2) + (uint32_t)logical * 16u;
+    }
+#pragma unroll
+    for (int i = 0; i < kRlBCopies; ++i) {
+        const int row = (wave * kRlBCopies + i) * kRlRowsPerCopy + (lane >> 3);
+        const int p = row / kRlExp, e = min(e0 + row % kRlExp, E - 1);
+        const int logical = (lane & 7) ^ rl_swz(row);
+        b_off[i] = ((uint64_t)p * plane + (uint64_t)e * H) * 2 + (uint64_t)logical * 16u;
+    }
+    auto issue = [&](int c, int st) {
+        const uint32_t sa = ring + st * kRlStage;
+        const uint64_t xa = xbase + (uint64_t)c * kRlRow;
+#pragma unroll
+        for (int i = 0; i < kRlACopies; ++i)
+            dma16_to_lds(xa, a_off[i], sa + (wave * kRlACopies + i) * kRlRowsPerCopy * kRlRow);
+        const uint32_t sb = sa + kRlARows * kRlRow;
+#pragma unroll
+        for (int i = 0; i < kRlBCopies; ++i)
+            dma16v_to_lds(reinterpret_cast<const void*>(wbase + b_off[i] + (uint64_t)c * kRlRow),
+                          sb + (wave * kRlBCopies + i) * kRlRowsPerCopy * kRlRow);
+    };
+
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int r16 = lane & 15, g = lane >> 4;
+    const int nch = ks / kRlKC;
+    issue(0, 0);
+    for (int c = 0; c < nch; ++c) {
+        const int st = c & 1;
+        wait_vmcnt<0>();
+        __syncthreads();       // chunk c visible to all; the other stage is free
+        if (c + 1 < nch) issue(c + 1, st ^ 1);
+        const uint8_t* sa = s_stage + st * kRlStage;
+        const uint8_t* sb = sa + kRlARows * kRlRow;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = ((4 * j + g) ^ rl_swz(r16)) * 16;
+            bf16x8 a[4], b[2][3];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                a[mb] = *reinterpret_cast<const bf16x8*>(sa + (64 * wi + 16 * mb + r16) * kRlRow + col);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    b[nb][p] = *reinterpret_cast<const bf16x8*>(
+                        sb + (p * kRlExp + 32 * wj + 16 * nb + r16) * kRlRow + col);
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[nb][p], acc[mb][nb],
+                                                                             0, 0, 0);
+        }
+    }
+    float* out = partial + (size_t)blockIdx.z * T * E;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int e = e0 + 32 * wj + 16 * nb + r16;
+            if (e >= E) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = tbase + 64 * wi + 16 * mb + g * 4 + q;
+                if (t < T) out[(size_t)t * E + e] = acc[mb][nb][q];
+            }
+        }
+}
+
 // One wavefront per token: logits = bias + the K-split partials (fixed order),
 // then top-k and renormalised weights (no shared state).
 template <int EPL>
@@ -431,9 +554,14 @@ hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& t
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    tm.launch(k_router_logits_mfma,
-                       dim3((a.E + kLgExp - 1) / kLgExp, (a.T + kLgTok - 1) / kLgTok, kRouterKSplit),
-                       dim3(256), 0, st, a.x, a.ws_planes, a.T, a.H, a.E, a.ws_logits);
+    if ((a.H / kRouterKSplit) % kRlKC == 0)
+        tm.launch(k_router_logits_lds,
+                  dim3((a.E + kRlExp - 1) / kRlExp, (a.T + kRlTok - 1) / kRlTok, kRouterKSplit),
+                  dim3(256), 0, st, a.x, a.ws_planes, a.T, a.H, a.E, a.ws_logits);
+    else
+        tm.launch(k_router_logits_mfma,
+                  dim3((a.E + kLgExp - 1) / kLgExp, (a.T + kLgTok - 1) / kLgTok, kRouterKSplit),
+                  dim3(256), 0, st, a.x, a.ws_planes, a.T, a.H, a.E, a.ws_logits);
     tm.after();
     err = hipGetLastError();
     if (err != hipSuccess) return err;
