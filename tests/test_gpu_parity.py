@@ -258,6 +258,21 @@ def test_boundary_ties_go_to_the_lower_expert(T):
         check_output(out, y, what=f"ties T={T}")
 
 
+# --- largest sizes the ABI accepts ------------------------------------------------------
+
+@pytest.mark.parametrize("T", [2, 64])
+def test_max_experts_and_top_k(T):
+    """E = 1024 experts (the largest accepted) with top-16: the 16-per-lane top-k,
+    1025 segments in the grouped tile list, and the single-call decode block."""
+    full_check(S(T=T, H=256, I=128, E=1024, top_k=16), 70 + T, what=f"E=1024 top16 T={T}")
+
+
+def test_max_tokens_T65536_sampled(full_layer):
+    """T = 65536 (the largest accepted) at full size: routing bit-exact over all
+    65536 tokens against the oracle, 12 sampled output rows."""
+    _sampled_full(S(T=65536, H=2048, I=512, E=256, top_k=8), 71, full_layer, "T=65536")
+
+
 # --- graph capture ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T", [1, 2, 64])
