@@ -177,6 +177,58 @@ class DecodeGraph:
             torch.cuda.synchronize()
 
 
+def step_percentiles(step_fn, n):
+    """p10 / p50 / p90 of n single-step durations (ms), each bracketed by torch events."""
+    import torch
+    pairs = []
+    for i in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step_fn(i)
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in pairs)
+    pick = lambda q: t[min(len(t) - 1, int(round(q * (len(t) - 1))))]   # noqa: E731
+    return [round(pick(0.1), 4), round(pick(0.5), 4), round(pick(0.9), 4)]
+
+
+def measure_ceilings():
+    """Secondary denominators measured on this GPU: a plain device copy (bytes read
+    plus written per second) and a large bf16 GEMM through torch (hipBLASLt)."""
+    import torch
+    n = 1 << 28                                   # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        dst.copy_(src)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbps = 10 * 2 * 4 * n / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn((m, m), generator=g, device="cuda").to(torch.bfloat16)
+    w = torch.randn((m, m), generator=g, device="cuda").to(torch.bfloat16)
+    for _ in range(2):
+        y = x @ w
+    a.record()
+    for _ in range(10):
+        y = x @ w
+    b.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 10 * 2.0 * m ** 3 / (a.elapsed_time(b) * 1e-3) / 1e12
+    del x, w, y
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(copy_gbps, 1), "bf16_gemm_TFLOPs": round(gemm_tflops, 1),
+            "copy": "1 GiB fp32 device copy (read + write bytes)",
+            "gemm": f"{m}x{m}x{m} bf16 matmul (torch / hipBLASLt)"}
+
+
 def kernel_times(blocks, xs, steps, ev: HipEvents, names, timed):
     """Average duration per kernel name over `steps` passes over all blocks.
 
@@ -245,6 +297,7 @@ def run_decode(args, ev):
     elapsed = time_steps(step, args.steps, args.warmup)
     ms_per_step = 1e3 * elapsed / args.steps
     value = L * T * args.steps / elapsed
+    pcts = step_percentiles(step, min(args.steps, 20))
 
     names = BLOCK_DECODE
     kt = kernel_times(blocks, xs, min(args.steps, 10), ev, names,
@@ -275,6 +328,7 @@ def run_decode(args, ev):
         "layer_call_alg_bytes": int(layer_bytes),
         "layer_call_hbm_frac": round(layer_bytes / (ms_per_step / L * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "active_experts_per_call": n_act,
+        "step_ms_p10_p50_p90": pcts,
     }
     config = {"workload": f"decode T={T} (40-layer rotation), H={H}, I={I}, E={E} top-{k} + shared, "
                           f"W4 group 64", "T": T, "H": H, "I": I, "E": E, "top_k": k,
@@ -303,6 +357,7 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
 
     elapsed = time_steps(step, steps, warmup)
     per_call_ms = 1e3 * elapsed / (steps * L)
+    pcts = step_percentiles(lambda i: blocks[i % L](xs[0][i % L]), 16)
     kt = kernel_times(blocks, xs, steps, ev, ROUTE_LARGE + FWD_GROUPED, split_timed(len(ROUTE_LARGE)))
     rows = T * k + T
     flops = {"grouped_gateup": 2.0 * rows * H * 2 * I, "grouped_down": 2.0 * rows * I * H}
@@ -314,6 +369,7 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
         "tokens_per_s": round(T / (per_call_ms * 1e-3), 1),
         "ms_per_layer_call": round(per_call_ms, 4),
         "layer_call_mfma_frac": round(layer_flops / (per_call_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "layer_call_ms_p10_p50_p90": pcts,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -486,6 +542,14 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(T=args.tokens)
+    print("[bench] measured ceilings", file=sys.stderr, flush=True)
+    ceil = measure_ceilings()
+    line["ceilings"] = ceil
+    rf = line["roofline"]
+    rf["frac_of_measured_copy"] = round(rf["achieved"] / ceil["copy_GBps"], 4)
+    if "prefill" in line:
+        pr = line["prefill"]["roofline"]
+        pr["frac_of_measured_gemm"] = round(pr["achieved"] / ceil["bf16_gemm_TFLOPs"], 4)
     line["source_hash"] = source_hash()
     print(json.dumps(line), flush=True)
 
