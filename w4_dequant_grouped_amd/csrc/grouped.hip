@@ -535,7 +535,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
 }
 
 // ---------------------------------------------------------------------------
-// down + routing-weighted scatter-add
+// down + routing-weighted per-(token, slot) rows
 // ---------------------------------------------------------------------------
 template <int NBW>
 __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(

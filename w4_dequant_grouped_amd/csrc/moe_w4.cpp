@@ -279,7 +279,7 @@ int moe_w4_block_timed(const moe_w4_dims* dims, const void* x, const float* rout
         a.out = static_cast<uint16_t*>(out);
         a.logits = reinterpret_cast<float*>(ws + L.logits);
         a.h = reinterpret_cast<uint16_t*>(ws + L.h);
-        // the decode path has no fp32 accumulator: its region holds the slot table
+        // the decode path writes no per-slot output rows: their region holds the slot table
         a.slots = reinterpret_cast<int32_t*>(ws + L.y);
         const hipError_t err = moe_w4::launch_block_decode(a, stream, tm);
         if (n_kernels) *n_kernels = tm.count;
