@@ -447,6 +447,60 @@ def run_stack(args, ev):
             "prefill": prefill, "decode": decode}
 
 
+def run_crossover(args, ev):
+    """Verification-batch study: one decode step (40 layers, captured graph) at each
+    T, through the GEMV path (T <= 8) and through the grouped MFMA path, with the
+    expert union |U| each T activates and the bytes it must stream."""
+    import torch
+    from w4_dequant_grouped_amd import moe_w4 as B
+    from w4_dequant_grouped_amd import synth
+
+    H, I, E, k, L = 2048, 512, 256, 8, args.layers
+    Ts = [int(t) for t in args.crossover_tokens.split(",")]
+    shape = synth.BlockShape(T=1, H=H, I=I, E=E, top_k=k)
+    layers = make_layers(shape, L, 1000, "cuda")
+    gu_b, dn_b = expert_bytes(H, I)
+    per_expert = 2 * gu_b + dn_b
+    ws = B.alloc_workspace(B.make_dims(max(Ts), H, I, E, k))
+    steps, warm = args.steps, args.warmup
+    rows = []
+    for T in Ts:
+        nx = steps + warm
+        xstk = torch.randn((nx, L, T, H), generator=synth.generator(700 + T, "cuda"),
+                           device="cuda").to(torch.bfloat16)
+        paths = [("gemv", B.MOE_W4_FORWARD_GEMV)] if T <= B.MOE_W4_GEMV_MAX_T else []
+        paths.append(("grouped", B.MOE_W4_FORWARD_GROUPED))
+        row = {"T": T}
+        for name, flags in paths:
+            print(f"[bench] crossover T={T} {name}", file=sys.stderr, flush=True)
+            blocks = [B.Block(layer, T, k, workspace=ws, flags=flags) for layer in layers]
+            dg = DecodeGraph(blocks, T, H)
+            dg.check(xstk[0], xstk[1 % nx])
+            elapsed = time_steps(lambda i=0: dg.step(xstk[i % nx]), steps, warm)
+            step_s = elapsed / steps
+            active = [int((blk.routing.counts > 0).sum().item()) for blk in blocks]
+            nbytes = sum(E * H * 4 + (a + 1) * per_expert + 2 * T * H * 2 for a in active)
+            row["active_experts"] = sum(active) / L
+            row["alg_MB_per_layer"] = round(nbytes / L / 1e6, 3)
+            row[name] = {"us_per_layer": round(1e6 * step_s / L, 3),
+                         "tokens_per_s": round(L * T / step_s, 1),
+                         "alg_GBps": round(nbytes / step_s / 1e9, 1),
+                         "hbm_frac": round(nbytes / step_s / 1e9 / HBM_PEAK_GBS, 4)}
+            del dg, blocks
+            torch.cuda.empty_cache()
+        row["faster"] = min((n for n, _ in paths), key=lambda n: row[n]["us_per_layer"])
+        rows.append(row)
+    base = rows[0]
+    for row in rows:
+        best = min(row[n]["us_per_layer"] for n in ("gemv", "grouped") if n in row)
+        b0 = min(base[n]["us_per_layer"] for n in ("gemv", "grouped") if n in base)
+        row["time_vs_T%d" % base["T"]] = round(best / b0, 3)
+        row["bytes_vs_T%d" % base["T"]] = round(row["alg_MB_per_layer"] / base["alg_MB_per_layer"], 3)
+    return {"workload": f"decode steps of {L} seeded layers (uniform-logit routers) at T rows per "
+                        f"layer-call, GEMV path vs grouped MFMA path, each step a captured graph",
+            "steps": steps, "warmup": warm, "default_gemv_max_T": B.MOE_W4_DECODE_MAX_T, "rows": rows}
+
+
 def cpu_baseline(T=1, max_calls=24, budget_s=20.0):
     """The oracle as it stands, on this host's cores, on a bounded sample."""
     import numpy as np  # noqa: F401
@@ -491,6 +545,9 @@ def main():
                     help="only run the 40-layer stack (T=16384 prefill + T=1 decode steps)")
     ap.add_argument("--stack-tokens", type=int, default=16384)
     ap.add_argument("--stack-decode-steps", type=int, default=256)
+    ap.add_argument("--crossover", action="store_true",
+                    help="only run the verification-batch study: GEMV vs grouped path per T")
+    ap.add_argument("--crossover-tokens", default="1,2,3,4,5,6,7,8,12,16,24,32,48,64")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy (fp32 negate) of MIB MiB three times: the "
                          "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -518,6 +575,11 @@ def main():
         return
     B.load_library()          # raises if the HIP library is missing: there is no fallback
     ev = HipEvents()
+    if args.crossover:
+        line = {"crossover": run_crossover(args, ev), "n_gpus": 1, "dtype": "bf16",
+                "data": "synthetic (seeded W4 layers and activations)", "source_hash": source_hash()}
+        print(json.dumps(line), flush=True)
+        return
     if args.stack:
         print("[bench] stack: 40 layers", file=sys.stderr, flush=True)
         line = {"stack": run_stack(args, ev), "n_gpus": 1, "dtype": "bf16",

@@ -55,8 +55,21 @@
 extern "C" {
 #endif
 
-/* Largest T served by the decode (GEMV) path of moe_w4_forward(). */
+/* Largest T served by the decode (GEMV) path of moe_w4_forward() by default. */
 #define MOE_W4_DECODE_MAX_T 5
+
+/* Largest T the decode (GEMV) path accepts when it is chosen explicitly. */
+#define MOE_W4_GEMV_MAX_T 8
+
+/* dims->flags: which forward path runs.  0 chooses by T (the GEMV path for
+ * T <= MOE_W4_DECODE_MAX_T, the grouped MFMA path above).  MOE_W4_FORWARD_GEMV
+ * forces the GEMV path (T <= MOE_W4_GEMV_MAX_T); MOE_W4_FORWARD_GROUPED forces the
+ * grouped path at any T (moe_w4_block then also skips its single-call schedule).
+ * Both bits, any other bit, or MOE_W4_FORWARD_GEMV with a larger T is
+ * MOE_W4_ERR_FLAGS.  Routing does not depend on the bits; route() accepts them so
+ * that one dims struct serves route() and forward(). */
+#define MOE_W4_FORWARD_GEMV 1u
+#define MOE_W4_FORWARD_GROUPED 2u
 
 /* Bytes at the start of the workspace used as the control block. */
 #define MOE_W4_CONTROL_BYTES 4096
@@ -70,10 +83,10 @@ enum {
     MOE_W4_ERR_ALIGN = -5,       /* a pointer is not aligned as documented          */
     MOE_W4_ERR_WORKSPACE = -6,   /* workspace smaller than moe_w4_workspace_bytes() */
     MOE_W4_ERR_LAUNCH = -7,      /* a HIP launch failed (see moe_w4_last_error())   */
-    MOE_W4_ERR_FLAGS = -8        /* unknown bits set in dims->flags                 */
+    MOE_W4_ERR_FLAGS = -8        /* bad dims->flags (see MOE_W4_FORWARD_GEMV)        */
 };
 
-/* Sizes of one block call.  `flags` must be 0 (reserved). */
+/* Sizes of one block call.  `flags`: 0, or one forward-path bit (above). */
 typedef struct moe_w4_dims {
     int32_t T;       /* tokens: rows of x and of out                    */
     int32_t H;       /* hidden size                                     */
@@ -81,7 +94,7 @@ typedef struct moe_w4_dims {
     int32_t E;       /* routed experts                                  */
     int32_t top_k;   /* experts chosen per token                        */
     int32_t group;   /* quantisation group along K (must be 64)         */
-    uint32_t flags;  /* reserved, 0                                     */
+    uint32_t flags;  /* 0 or MOE_W4_FORWARD_GEMV / MOE_W4_FORWARD_GROUPED */
 } moe_w4_dims;
 
 /* Packed 4-bit weights of E matrices [N][K] (layout above). */
@@ -142,7 +155,7 @@ int moe_w4_route(const moe_w4_dims* dims,
  *   shared       one expert's weights, or NULL for no shared expert
  *   topk_w, expert_offsets, perm   as produced by moe_w4_route() for this x
  *   out          bf16  [T][H]     overwritten; must not alias x
- * T <= MOE_W4_DECODE_MAX_T runs the decode path (one wavefront per weight row
+ * T <= MOE_W4_DECODE_MAX_T (or dims->flags) selects the decode path (one wavefront per weight row
  * streams each selected expert's bytes once); larger T runs the grouped MFMA
  * path.  Both accumulate in fp32; intermediate activations are rounded to bf16.
  * The grouped path rounds each routed (token, slot) row's weighted expert output

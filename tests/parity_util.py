@@ -33,9 +33,11 @@ def make_inputs(shape: synth.BlockShape, seed: int, layer=None, condition: bool 
     return layer, x
 
 
-def run_block(layer_gpu, x_gpu, shape: synth.BlockShape, workspace=None, split: bool = False):
-    """One block call: moe_w4_block, or moe_w4_route then moe_w4_forward (split)."""
-    blk = B.Block(layer_gpu, shape.T, shape.top_k, shape.group, workspace=workspace)
+def run_block(layer_gpu, x_gpu, shape: synth.BlockShape, workspace=None, split: bool = False,
+              flags: int = 0):
+    """One block call: moe_w4_block, or moe_w4_route then moe_w4_forward (split).
+    flags picks the forward path (0: by T)."""
+    blk = B.Block(layer_gpu, shape.T, shape.top_k, shape.group, workspace=workspace, flags=flags)
     out = blk.split(x_gpu) if split else blk(x_gpu)
     torch.cuda.synchronize()
     return blk.routing, out
@@ -67,12 +69,12 @@ def check_output(out_gpu: torch.Tensor, ref: np.ndarray, rows=None, what: str = 
 
 
 def full_check(shape: synth.BlockShape, seed: int, layer=None, what: str = "", condition=True,
-               split: bool = False):
+               split: bool = False, flags: int = 0):
     """Route + forward on the GPU and compare everything with the full oracle."""
     note(f"[gpu] {what}: {synth.describe(shape)} seed={seed} {'split' if split else 'block'}")
     layer, x = make_inputs(shape, seed, layer, condition)
     ref_r = O.route(x, layer.router_w, layer.router_b, shape.top_k)
-    r, out = run_block(layer.to("cuda"), x.cuda(), shape, split=split)
+    r, out = run_block(layer.to("cuda"), x.cuda(), shape, split=split, flags=flags)
     if condition:
         check_routing(r, ref_r, what)
     y = O.forward_grouped(x, layer, ref_r, shape.group)

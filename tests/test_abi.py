@@ -99,7 +99,9 @@ def _forward(lib, dims, x=FAKE, routed=None, shared=None, w=FAKE, off=FAKE, perm
 def test_route_rejects_bad_arguments(lib):
     assert _route(lib, None) == ERR_NULL
     assert _route(lib, _dims(T=0)) == OK                    # empty batch: nothing to do
-    assert _route(lib, _dims(flags=2)) == ERR_FLAGS
+    assert _route(lib, _dims(flags=4)) == ERR_FLAGS
+    assert _route(lib, _dims(flags=3)) == ERR_FLAGS         # both forward paths
+    assert _route(lib, _dims(T=0, flags=B.MOE_W4_FORWARD_GROUPED)) == OK
     assert _route(lib, _dims(T=70000)) == ERR_DIMS
     assert _route(lib, _dims(E=0)) == ERR_DIMS
     assert _route(lib, _dims(top_k=17)) == ERR_TOPK
@@ -122,7 +124,9 @@ def test_route_rejects_bad_arguments(lib):
 def test_forward_rejects_bad_arguments(lib):
     assert _forward(lib, None) == ERR_NULL
     assert _forward(lib, _dims(T=0)) == OK
-    assert _forward(lib, _dims(flags=1)) == ERR_FLAGS
+    assert _forward(lib, _dims(flags=1)) == ERR_FLAGS         # GEMV path asked for T=16 > 8
+    assert _forward(lib, _dims(flags=8)) == ERR_FLAGS
+    assert _forward(lib, _dims(T=8, flags=B.MOE_W4_FORWARD_GEMV), ws_bytes=0) == ERR_WS   # accepted flags
     assert _forward(lib, _dims(I=192)) == ERR_GROUP
     assert _forward(lib, _dims(top_k=3, E=2)) == ERR_TOPK
     assert _forward(lib, _dims(), x=None) == ERR_NULL
@@ -141,7 +145,8 @@ def test_forward_rejects_bad_arguments(lib):
 
 def test_binding_constants_match_the_header():
     text = open(os.path.join(ROOT, "include", "moe_w4.h")).read()
-    for name in ("MOE_W4_DECODE_MAX_T", "MOE_W4_CONTROL_BYTES"):
-        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+    for name in ("MOE_W4_DECODE_MAX_T", "MOE_W4_GEMV_MAX_T", "MOE_W4_CONTROL_BYTES", "MOE_W4_FORWARD_GEMV",
+                 "MOE_W4_FORWARD_GROUPED"):
+        m = re.search(r"#define\s+%s\s+(\d+)u?\b" % name, text)
         assert m, name
         assert int(m.group(1)) == getattr(B, name), name

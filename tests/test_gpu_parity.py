@@ -48,6 +48,20 @@ def test_grouped_small_dims(T):
     full_check(S(T=T, H=512, I=256, E=32, top_k=4), 50 + T, what=f"grouped-small T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 2, 5])
+def test_forced_grouped_path_small_T(T):
+    # the grouped MFMA path below its default threshold (single M-tile, mostly padding)
+    full_check(S(T=T, H=512, I=256, E=32, top_k=4), 70 + T, what=f"forced grouped T={T}",
+               flags=B.MOE_W4_FORWARD_GROUPED)
+
+
+@pytest.mark.parametrize("T", [6, 8])
+def test_forced_gemv_path_up_to_8(T):
+    # the GEMV path above its default threshold, up to the largest row count it is built for
+    full_check(S(T=T, H=512, I=256, E=32, top_k=4), 80 + T, what=f"forced gemv T={T}",
+               flags=B.MOE_W4_FORWARD_GEMV)
+
+
 def test_grouped_multi_tile_ragged():
     # 1200 routed rows over 32 experts, shared expert 300 rows = 3 M-tiles (ragged)
     full_check(S(T=300, H=512, I=256, E=32, top_k=4), 61, what="multi-tile")
@@ -110,6 +124,13 @@ def full_layer():
 def test_decode_full_size(full_layer, T):
     shape = S(T=T, H=2048, I=512, E=256, top_k=8)
     full_check(shape, 100 + T, layer=full_layer, what=f"decode full T={T}")
+
+
+@pytest.mark.parametrize("T,flags", [(1, B.MOE_W4_FORWARD_GROUPED), (4, B.MOE_W4_FORWARD_GROUPED),
+                                     (8, B.MOE_W4_FORWARD_GEMV)])
+def test_forced_paths_full_size(full_layer, T, flags):
+    shape = S(T=T, H=2048, I=512, E=256, top_k=8)
+    full_check(shape, 130 + T, layer=full_layer, what=f"forced flags={flags} full T={T}", flags=flags)
 
 
 def _sampled_full(shape, seed, layer, what, nrows=12):

@@ -140,33 +140,30 @@ __device__ __forceinline__ Slot find_slot(const int32_t* __restrict__ offsets, i
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU
 // ---------------------------------------------------------------------------
-// Weight rows per wavefront: 4 for up to two token rows, 2 beyond (the x rows
-// and accumulators of every token stay in registers).
+// Weight rows per wavefront: 4 for up to four token rows, 2 beyond (the
+// accumulators of every token stay in registers).
 template <int TMAX>
-constexpr int gu_rows_per_wave() { return TMAX <= 2 ? 4 : 2; }
+constexpr int gu_rows_per_wave() { return TMAX <= 4 ? 4 : 2; }
 template <int TMAX>
 constexpr int gu_rows_per_block() { return 4 * gu_rows_per_wave<TMAX>(); }
 
-// Rows n0 .. n0+R-1 of gate and up of expert e, for the cnt token rows tok[0..cnt):
-// h[hrow0 + i][n0 + r] = silu(gate . x) * (up . x), bf16.  One wavefront.
-template <int TMAX>
-__device__ __forceinline__ void gateup_rows(const uint16_t* __restrict__ x, int H, int I,
-                                            const W4& G, const W4& U, int e, int n0, int cnt,
-                                            const int (&tok)[TMAX], int hrow0,
-                                            uint16_t* __restrict__ h, int lane) {
-    constexpr int R = gu_rows_per_wave<TMAX>();
+// One token row: rows n0 .. n0+R-1 of gate and up of expert e,
+// h[hrow0][n0 + r] = silu(gate . x) * (up . x), bf16.  One wavefront; every lane
+// loads its own slice of x next to its weights (one memory round trip).
+__device__ __forceinline__ void gateup_rows_one(const uint16_t* __restrict__ x, int H, int I,
+                                                const W4& G, const W4& U, int e, int n0, int tok,
+                                                int hrow0, uint16_t* __restrict__ h, int lane) {
+    constexpr int R = gu_rows_per_wave<1>();
     const int ngroups = H / kGroup;
     const int nchunks = H / 32;
-    float ag[R][TMAX], au[R][TMAX];
+    float ag[R], au[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int i = 0; i < TMAX; ++i) { ag[r][i] = 0.f; au[r][i] = 0.f; }
+    for (int r = 0; r < R; ++r) { ag[r] = 0.f; au[r] = 0.f; }
 
     for (int c = lane; c < nchunks; c += kWave) {
         u32x4 cg[R], cu[R];
         uint32_t sg[R], bg[R], su[R], bu[R];
-        u32x4 xv[TMAX][4];
+        u32x4 xv[4];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const size_t row = (size_t)e * I + (n0 + r);
@@ -178,22 +175,117 @@ __device__ __forceinline__ void gateup_rows(const uint16_t* __restrict__ x, int 
             su[r] = U.scales[gi];
             bu[r] = U.biases[gi];
         }
+        load64(x + (size_t)tok * H + c * 32, xv);
+        uint32_t xi[16];
+        float xs;
+        interleave32(xv, xi, xs);
 #pragma unroll
-        for (int i = 0; i < TMAX; ++i)
-            if (i < cnt) load64(x + (size_t)tok[i] * H + c * 32, xv[i]);
+        for (int r = 0; r < R; ++r) {
+            const float s0 = bf16_to_f32(sg[r]), s1 = bf16_to_f32(su[r]);
+            ag[r] += fmaf(s0, dot32_magic(cg[r], xi), (bf16_to_f32(bg[r]) - 128.0f * s0) * xs);
+            au[r] += fmaf(s1, dot32_magic(cu[r], xi), (bf16_to_f32(bu[r]) - 128.0f * s1) * xs);
+        }
+    }
 #pragma unroll
-        for (int i = 0; i < TMAX; ++i) {
-            if (i >= cnt) break;
+    for (int r = 0; r < R; ++r) {
+        const float g = wave_sum(ag[r]);
+        const float u = wave_sum(au[r]);
+        if (lane == r) h[(size_t)hrow0 * I + n0 + r] = (uint16_t)f32_to_bf16(silu(g) * u);
+    }
+}
+
+// Several token rows.  The four wavefronts of a workgroup work on the same
+// slot, hence the same token rows: x is staged once per workgroup in LDS, 64
+// chunks of 32 values (2048 of K) at a time, already interleaved, with each
+// chunk's sum.  [t][quarter][chunk] order keeps a wavefront's 16-byte reads
+// consecutive.
+constexpr int kXChunks = 64;
+template <int TMAX>
+struct XStage {
+    u32x4 v[TMAX][4][kXChunks];
+    float s[TMAX][kXChunks];
+};
+
+// An empty asm that claims to modify v: values computed from v before it cannot
+// be reused after it.  The token loop uses it so that the compiler recomputes
+// the codes' magic pairs per token (two bit operations each) instead of holding
+// all of them in registers across the loop.
+__device__ __forceinline__ void opaque(u32x4& v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+template <int TMAX>
+__device__ __forceinline__ void gateup_rows_multi(const uint16_t* __restrict__ x, int H, int I,
+                                                  const W4& G, const W4& U, int e, int n0, int cnt,
+                                                  const int (&tok)[TMAX], int hrow0,
+                                                  uint16_t* __restrict__ h, int lane, int wave,
+                                                  XStage<TMAX>& sx) {
+    constexpr int R = gu_rows_per_wave<TMAX>();
+    constexpr int NQ = (TMAX + 3) / 4;          // token rows staged per wavefront
+    const int ngroups = H / kGroup;
+    const int nchunks = H / 32;
+    float ag[R][TMAX], au[R][TMAX];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) { ag[r][i] = 0.f; au[r][i] = 0.f; }
+
+    for (int cb = 0; cb < nchunks; cb += kXChunks) {
+        const int c = cb + lane;
+        const bool own = c < nchunks;
+        const int cl = own ? c : nchunks - 1;   // in-bounds address for idle lanes
+        // x of the token rows this wavefront stages (t = wave, wave + 4): issued
+        // first, since it is consumed first
+        u32x4 xv[NQ][4];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t)
+            if ((t & 3) == wave && t < cnt) load64(x + (size_t)tok[t] * H + cl * 32, xv[t >> 2]);
+        u32x4 cg[R], cu[R];
+        uint32_t sg[R], bg[R], su[R], bu[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const size_t row = (size_t)e * I + (n0 + r);
+            cg[r] = load_u32x4(G.codes + row * (H / 2) + cl * 16);
+            cu[r] = load_u32x4(U.codes + row * (H / 2) + cl * 16);
+            const size_t gi = row * ngroups + (cl >> 1);
+            sg[r] = G.scales[gi];
+            bg[r] = G.biases[gi];
+            su[r] = U.scales[gi];
+            bu[r] = U.biases[gi];
+        }
+        if (cb > 0) __syncthreads();            // the previous block's readers are done
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if ((t & 3) == wave && t < cnt) {
+                uint32_t xi[16];
+                float xs;
+                interleave32(xv[t >> 2], xi, xs);
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    sx.v[t][b][lane] = u32x4{xi[4 * b], xi[4 * b + 1], xi[4 * b + 2], xi[4 * b + 3]};
+                sx.s[t][lane] = xs;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if (t >= cnt) break;
+#pragma unroll
+            for (int r = 0; r < R; ++r) { opaque(cg[r]); opaque(cu[r]); }
             uint32_t xi[16];
-            float xs;
-            interleave32(xv[i], xi, xs);
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float s0 = bf16_to_f32(sg[r]), s1 = bf16_to_f32(su[r]);
-                const float pg = dot32_magic(cg[r], xi);
-                const float pu = dot32_magic(cu[r], xi);
-                ag[r][i] += fmaf(s0, pg, (bf16_to_f32(bg[r]) - 128.0f * s0) * xs);
-                au[r][i] += fmaf(s1, pu, (bf16_to_f32(bu[r]) - 128.0f * s1) * xs);
+            for (int b = 0; b < 4; ++b) {
+                const u32x4 q = sx.v[t][b][lane];
+                xi[4 * b] = q.x; xi[4 * b + 1] = q.y; xi[4 * b + 2] = q.z; xi[4 * b + 3] = q.w;
+            }
+            const float xs = sx.s[t][lane];
+            if (own) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float s0 = bf16_to_f32(sg[r]), s1 = bf16_to_f32(su[r]);
+                    ag[r][t] += fmaf(s0, dot32_magic(cg[r], xi), (bf16_to_f32(bg[r]) - 128.0f * s0) * xs);
+                    au[r][t] += fmaf(s1, dot32_magic(cu[r], xi), (bf16_to_f32(bu[r]) - 128.0f * s1) * xs);
+                }
             }
         }
     }
@@ -207,6 +299,22 @@ __device__ __forceinline__ void gateup_rows(const uint16_t* __restrict__ x, int 
             const float u = wave_sum(au[r][i]);
             if (lane == r) h[(size_t)hrow * I + n0 + r] = (uint16_t)f32_to_bf16(silu(g) * u);
         }
+    }
+}
+
+// Rows n0 .. n0 + R - 1 of gate and up of expert e for the cnt token rows
+// tok[0..cnt): h[hrow0 + i][n0 + r] = silu(gate . x_tok[i]) * (up . x_tok[i]).
+// All four wavefronts of the workgroup must call it with the same slot.
+template <int TMAX>
+__device__ __forceinline__ void gateup_rows(const uint16_t* __restrict__ x, int H, int I,
+                                            const W4& G, const W4& U, int e, int n0, int cnt,
+                                            const int (&tok)[TMAX], int hrow0,
+                                            uint16_t* __restrict__ h, int lane, int wave) {
+    if constexpr (TMAX == 1) {
+        gateup_rows_one(x, H, I, G, U, e, n0, tok[0], hrow0, h, lane);
+    } else {
+        __shared__ XStage<TMAX> s_x;
+        gateup_rows_multi<TMAX>(x, H, I, G, U, e, n0, cnt, tok, hrow0, h, lane, wave, s_x);
     }
 }
 
@@ -245,7 +353,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
             tok[i] = is_shared ? i : min(max(perm[sl.off + i], 0), T * k - 1) / k;
     }
     const int n0 = blockIdx.y * gu_rows_per_block<TMAX>() + wave * gu_rows_per_wave<TMAX>();
-    gateup_rows<TMAX>(x, H, I, G, U, e, n0, sl.cnt, tok, sl.off, h, lane);
+    gateup_rows<TMAX>(x, H, I, G, U, e, n0, sl.cnt, tok, sl.off, h, lane, wave);
 }
 
 // ---------------------------------------------------------------------------
@@ -440,7 +548,7 @@ __global__ __launch_bounds__(256) void k_decode_logits_shared(DecodeBlockArgs a)
 #pragma unroll
         for (int i = 0; i < TMAX; ++i) tok[i] = i;
         const int n0 = (blockIdx.x - nlog) * gu_rows_per_block<TMAX>() + wave * gu_rows_per_wave<TMAX>();
-        gateup_rows<TMAX>(a.x, H, a.I, a.shared.gate, a.shared.up, 0, n0, T, tok, T * a.k, a.h, lane);
+        gateup_rows<TMAX>(a.x, H, a.I, a.shared.gate, a.shared.up, 0, n0, T, tok, T * a.k, a.h, lane, wave);
     }
 }
 
@@ -552,7 +660,7 @@ __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) 
     for (int i = 0; i < TMAX; ++i) tok[i] = s_ptok[s_uoff[slot] + min(i, cnt - 1)];
     const int n0 = blockIdx.y * gu_rows_per_block<TMAX>() + wave * gu_rows_per_wave<TMAX>();
     gateup_rows<TMAX>(a.x, a.H, a.I, a.routed.gate, a.routed.up, s_u[slot], n0, cnt, tok,
-                      s_uoff[slot], a.h, lane);
+                      s_uoff[slot], a.h, lane, wave);
 }
 
 template <int TMAX, int EPL>

@@ -15,6 +15,7 @@ thread_local std::string g_last_error;
 
 constexpr size_t kAlign = 256;
 constexpr size_t kCtrlBytes = MOE_W4_CONTROL_BYTES;
+static_assert(MOE_W4_GEMV_MAX_T == moe_w4::kDecodeMaxT, "GEMV kernels are built for this many rows");
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -24,7 +25,12 @@ struct Layout {
 
 bool dims_ok(const moe_w4_dims* d, int* status) {
     if (!d) { *status = MOE_W4_ERR_NULL; return false; }
-    if (d->flags != 0u) { *status = MOE_W4_ERR_FLAGS; return false; }
+    const uint32_t path = MOE_W4_FORWARD_GEMV | MOE_W4_FORWARD_GROUPED;
+    if ((d->flags & ~path) != 0u || d->flags == path ||
+        ((d->flags & MOE_W4_FORWARD_GEMV) && d->T > MOE_W4_GEMV_MAX_T)) {
+        *status = MOE_W4_ERR_FLAGS;
+        return false;
+    }
     if (d->T < 0 || d->T > 65536 || d->E < 1 || d->E > 1024 || d->H < 256 || d->H > 16384 ||
         d->I < 128 || d->I > 16384) {
         *status = MOE_W4_ERR_DIMS;
@@ -174,8 +180,9 @@ hipError_t run_forward(const moe_w4_dims* dims, const void* x, const moe_w4_weig
     a.ws_h = reinterpret_cast<uint16_t*>(ws + L.h);
     a.ws_y = reinterpret_cast<uint16_t*>(ws + L.y);
     a.ctl = reinterpret_cast<uint32_t*>(ws);
-    return (a.T <= MOE_W4_DECODE_MAX_T) ? moe_w4::launch_forward_decode(a, stream, tm)
-                                        : moe_w4::launch_forward_grouped(a, stream, tm);
+    const bool gemv = (dims->flags & MOE_W4_FORWARD_GEMV) ||
+                      (!(dims->flags & MOE_W4_FORWARD_GROUPED) && a.T <= MOE_W4_DECODE_MAX_T);
+    return gemv ? moe_w4::launch_forward_decode(a, stream, tm) : moe_w4::launch_forward_grouped(a, stream, tm);
 }
 
 }  // namespace
@@ -256,7 +263,7 @@ int moe_w4_block_timed(const moe_w4_dims* dims, const void* x, const float* rout
     if (st != MOE_W4_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     moe_w4::KernelTimer tm = make_timer(events, capacity);
-    if (dims->T <= moe_w4::kBlockDecodeMaxT) {
+    if (dims->T <= moe_w4::kBlockDecodeMaxT && !(dims->flags & MOE_W4_FORWARD_GROUPED)) {
         const Layout L = layout(dims);
         uint8_t* ws = static_cast<uint8_t*>(workspace);
         moe_w4::DecodeBlockArgs a;
@@ -314,7 +321,7 @@ const char* moe_w4_status_string(int status) {
         case MOE_W4_ERR_ALIGN: return "a pointer is not aligned as required";
         case MOE_W4_ERR_WORKSPACE: return "workspace smaller than moe_w4_workspace_bytes()";
         case MOE_W4_ERR_LAUNCH: return "a HIP kernel launch failed";
-        case MOE_W4_ERR_FLAGS: return "unknown bits set in dims->flags";
+        case MOE_W4_ERR_FLAGS: return "dims->flags: unknown bits, both path bits, or the GEMV path with T > 8";
         default: return "unknown status";
     }
 }

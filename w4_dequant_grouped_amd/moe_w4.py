@@ -18,6 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_w4.so")
 
 MOE_W4_DECODE_MAX_T = 5
+MOE_W4_GEMV_MAX_T = 8
+MOE_W4_FORWARD_GEMV = 1
+MOE_W4_FORWARD_GROUPED = 2
 MOE_W4_CONTROL_BYTES = 4096
 
 
@@ -274,10 +277,11 @@ def moe_w4_forward_timed(dims: moe_w4_dims, x: torch.Tensor, routed_struct: moe_
 class Block:
     """One layer's routed + shared W4 experts and router, bound for repeated calls."""
 
-    def __init__(self, layer, T: int, top_k: int, group: int = 64, workspace: Optional[torch.Tensor] = None):
+    def __init__(self, layer, T: int, top_k: int, group: int = 64, workspace: Optional[torch.Tensor] = None,
+                 flags: int = 0):
         self.layer = layer
         E, I, H = layer.routed.gate.codes.shape[0], layer.routed.gate.codes.shape[1], layer.router_w.shape[1]
-        self.dims = make_dims(T, H, I, E, top_k, group)
+        self.dims = make_dims(T, H, I, E, top_k, group, flags)
         self.routed_struct = weights_struct(layer.routed)
         self.shared_struct = None if layer.shared is None else weights_struct(layer.shared)
         dev = layer.router_w.device
