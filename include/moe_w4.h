@@ -55,8 +55,10 @@
 extern "C" {
 #endif
 
-/* Largest T served by the decode (GEMV) path of moe_w4_forward() by default. */
-#define MOE_W4_DECODE_MAX_T 5
+/* Largest T served by the decode (GEMV) path of moe_w4_forward() by default:
+ * the measured crossover with the grouped path on MI355X for H=2048, I=512,
+ * E=256, top-8 (the GEMV path is faster through T=7, the grouped path from 8). */
+#define MOE_W4_DECODE_MAX_T 7
 
 /* Largest T the decode (GEMV) path accepts when it is chosen explicitly. */
 #define MOE_W4_GEMV_MAX_T 8

@@ -361,26 +361,44 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
 // ---------------------------------------------------------------------------
 constexpr int kDnRowsPerWave = 2;
 constexpr int kDnRowsPerBlock = 4 * kDnRowsPerWave;
-constexpr int kDnUnroll = 3;     // (slot, chunk) items per lane whose loads are issued together
-constexpr int kDnLdsRows = 48;   // h staged in LDS when T*k + T <= 48 rows of I <= 512
-constexpr int kDnLdsI = 512;
+constexpr int kDnUnroll = 4;     // (slot, 32-code chunk) items per lane in one batch of loads
+constexpr int kDnLdsI = 512;     // h is staged in LDS when I <= this
 
+// h rows of T <= TMAX tokens: T*k routed + T shared, k <= 16
 template <int TMAX>
+constexpr int dn_rows() { return TMAX * (kMaxTopK + 1); }
+
+// One batch of down-weight loads: kDnUnroll items per lane.
+struct DnBatch {
+    u32x4 c[kDnUnroll][kDnRowsPerWave];
+    uint32_t s[kDnUnroll][kDnRowsPerWave], b[kDnUnroll][kDnRowsPerWave];
+    int slot[kDnUnroll], cc[kDnUnroll];   // slot (-1: no item) and chunk
+};
+
+// Rows n0, n0+1 per wavefront.  A lane's items are (slot, chunk) pairs; each is
+// dotted with every token row of its slot.  Before the item loop, h (all
+// threads), the slot list (wavefront 0) and each h row's token and weight
+// (wavefront 1) go to LDS in parallel, so that no batch of weight loads waits
+// on a dependent global read, and the next batch is in flight while the
+// current one is used.  HLDS: h staged in LDS (I <= kDnLdsI), else read from
+// global memory.  A compile-time choice: a global read inside the item loop
+// would make every iteration wait for the next batch's loads too.
+template <int TMAX, bool HLDS>
 __global__ __launch_bounds__(256) void k_decode_down(
     int T, int H, int I, int E, int k, W4Set routed, W4Set shared, int has_shared,
     const float* __restrict__ topk_w, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const uint16_t* __restrict__ h,
     uint16_t* __restrict__ out, const int32_t* __restrict__ slot_table) {
+    constexpr int HR = dn_rows<TMAX>();
     __shared__ Slot s_slots[kMaxSlots];
     __shared__ int s_n;
-    __shared__ __attribute__((aligned(16))) uint16_t s_h[kDnLdsRows * kDnLdsI];
+    __shared__ int s_rt[HR];          // token of each h row
+    __shared__ float s_rw[HR];        // its routing weight (1 for the shared expert)
+    __shared__ __attribute__((aligned(16))) uint16_t s_h[HLDS ? HR * kDnLdsI : 8];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    // h is dense (rows 0 .. T*k + T - 1): stage it in LDS while wavefront 0 reads
-    // the routing, so that no h read waits behind the weight reads later
     const int hrows = T * k + T;
-    const bool h_in_lds = hrows <= kDnLdsRows && I <= kDnLdsI;
-    if (h_in_lds) {
+    if constexpr (HLDS) {
         const int n16 = hrows * I / 8;
         for (int i = threadIdx.x; i < n16; i += blockDim.x)
             reinterpret_cast<u32x4*>(s_h)[i] = reinterpret_cast<const u32x4*>(h)[i];
@@ -388,76 +406,85 @@ __global__ __launch_bounds__(256) void k_decode_down(
     if (wave == 0) {
         if (slot_table) read_slot_table(slot_table, T, k, has_shared, s_slots, &s_n, lane);
         else build_slots(offsets, E, T, k, has_shared, s_slots, &s_n, lane);
+    } else if (wave == 1) {
+        for (int r = lane; r < hrows; r += kWave) {
+            int t;
+            float w;
+            if (r >= T * k) { t = r - T * k; w = 1.0f; }
+            else { const int f = min(max(perm[r], 0), T * k - 1); t = f / k; w = topk_w[f]; }
+            s_rt[r] = t;
+            s_rw[r] = w;
+        }
     }
     __syncthreads();
     const int nslots = s_n;
-
     const int n0 = blockIdx.x * kDnRowsPerBlock + wave * kDnRowsPerWave;
     const int cpr = I / 32;            // 32-code chunks per down row
     const int ngroups = I / kGroup;
     const int nitems = nslots * cpr;
-
-    float acc[kDnRowsPerWave][TMAX];
-#pragma unroll
-    for (int r = 0; r < kDnRowsPerWave; ++r)
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t) acc[r][t] = 0.f;
-
-    for (int base = 0; base < nitems; base += kWave * kDnUnroll) {
-        u32x4 cd[kDnUnroll][kDnRowsPerWave];
-        uint32_t sd[kDnUnroll][kDnRowsPerWave], bd[kDnUnroll][kDnRowsPerWave];
-        Slot sl[kDnUnroll];
-        int cc[kDnUnroll];
+    constexpr int kStep = kWave * kDnUnroll;
+    // items past the end load slot 0, chunk 0 again (in bounds, never used)
+    auto load = [&](DnBatch& B, int base) {
 #pragma unroll
         for (int u = 0; u < kDnUnroll; ++u) {
             const int idx = base + u * kWave + lane;
             const bool ok = idx < nitems;
             const int a = ok ? idx / cpr : 0;
-            cc[u] = ok ? idx - a * cpr : 0;
-            sl[u] = s_slots[a];
-            if (!ok) sl[u].cnt = 0;
-            const bool is_shared = sl[u].e < 0;
-            const int e = is_shared ? 0 : sl[u].e;
+            B.slot[u] = ok ? a : -1;
+            B.cc[u] = ok ? idx - a * cpr : 0;
+            const Slot sl = s_slots[a];
+            const bool is_shared = sl.e < 0;
+            const int e = is_shared ? 0 : sl.e;
             const W4 D = is_shared ? shared.down : routed.down;
 #pragma unroll
             for (int r = 0; r < kDnRowsPerWave; ++r) {
                 const size_t row = (size_t)e * H + (n0 + r);
-                cd[u][r] = load_u32x4(D.codes + row * (I / 2) + cc[u] * 16);
-                const size_t gi = row * ngroups + (cc[u] >> 1);
-                sd[u][r] = D.scales[gi];
-                bd[u][r] = D.biases[gi];
+                B.c[u][r] = load_u32x4(D.codes + row * (I / 2) + B.cc[u] * 16);
+                const size_t gi = row * ngroups + (B.cc[u] >> 1);
+                B.s[u][r] = D.scales[gi];
+                B.b[u][r] = D.biases[gi];
             }
         }
+    };
+    float acc[kDnRowsPerWave][TMAX];
+#pragma unroll
+    for (int r = 0; r < kDnRowsPerWave; ++r)
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) acc[r][t] = 0.f;
+    DnBatch cur, nxt;
+    load(cur, 0);
+    for (int base = 0; base < nitems; base += kStep) {
+        load(nxt, base + kStep);                 // next batch in flight during this one
 #pragma unroll
         for (int u = 0; u < kDnUnroll; ++u) {
-            const bool is_shared = sl[u].e < 0;
-            for (int i = 0; i < sl[u].cnt; ++i) {
-                const int hrow = sl[u].off + i;
-                int t;
-                float w;
-                if (is_shared) { t = i; w = 1.0f; }
-                else { const int f = min(max(perm[hrow], 0), T * k - 1); t = f / k; w = topk_w[f]; }
+            if (cur.slot[u] < 0) continue;
+            const Slot sl = s_slots[cur.slot[u]];
+            for (int i = 0; i < sl.cnt; ++i) {
+                const int hrow = sl.off + i;
+                const int t = s_rt[hrow];
+                const float w = s_rw[hrow];
                 u32x4 hv[4];
-                if (h_in_lds) {
-                    const u32x4* q = reinterpret_cast<const u32x4*>(s_h + (size_t)hrow * I + cc[u] * 32);
+                if constexpr (HLDS) {
+                    const u32x4* q = reinterpret_cast<const u32x4*>(s_h + (size_t)hrow * I + cur.cc[u] * 32);
 #pragma unroll
                     for (int b = 0; b < 4; ++b) hv[b] = q[b];
                 } else {
-                    load64(h + (size_t)hrow * I + cc[u] * 32, hv);
+                    load64(h + (size_t)hrow * I + cur.cc[u] * 32, hv);
                 }
                 uint32_t xi[16];
                 float hs;
                 interleave32(hv, xi, hs);
 #pragma unroll
                 for (int r = 0; r < kDnRowsPerWave; ++r) {
-                    const float s0 = bf16_to_f32(sd[u][r]);
-                    const float v = w * fmaf(s0, dot32_magic(cd[u][r], xi),
-                                             (bf16_to_f32(bd[u][r]) - 128.0f * s0) * hs);
+                    const float s0 = bf16_to_f32(cur.s[u][r]);
+                    const float v = w * fmaf(s0, dot32_magic(cur.c[u][r], xi),
+                                             (bf16_to_f32(cur.b[u][r]) - 128.0f * s0) * hs);
 #pragma unroll
                     for (int tt = 0; tt < TMAX; ++tt) acc[r][tt] += (tt == t) ? v : 0.f;
                 }
             }
         }
+        cur = nxt;
     }
 #pragma unroll
     for (int r = 0; r < kDnRowsPerWave; ++r)
@@ -480,9 +507,9 @@ static hipError_t decode_t(const ForwardArgs& a, hipStream_t st, KernelTimer& tm
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    tm.launch(k_decode_down<TMAX>, dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T,
-                       a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.topk_w, a.offsets,
-                       a.perm, a.ws_h, a.out, nullptr);
+    tm.launch(a.I <= kDnLdsI ? k_decode_down<TMAX, true> : k_decode_down<TMAX, false>,
+              dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T, a.H, a.I, a.E, a.k, a.routed,
+              a.shared, a.has_shared, a.topk_w, a.offsets, a.perm, a.ws_h, a.out, nullptr);
     tm.after();
     return hipGetLastError();
 }
@@ -679,9 +706,9 @@ static hipError_t block_decode_t(const DecodeBlockArgs& a, hipStream_t st, Kerne
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    tm.launch(k_decode_down<TMAX>, dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T,
-                       a.H, a.I, a.E, a.k, a.routed, a.shared, a.has_shared, a.tw, a.offsets,
-                       a.perm, a.h, a.out, a.slots);
+    tm.launch(a.I <= kDnLdsI ? k_decode_down<TMAX, true> : k_decode_down<TMAX, false>,
+              dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T, a.H, a.I, a.E, a.k, a.routed,
+              a.shared, a.has_shared, a.tw, a.offsets, a.perm, a.h, a.out, a.slots);
     tm.after();
     return hipGetLastError();
 }

@@ -17,7 +17,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_w4.so")
 
-MOE_W4_DECODE_MAX_T = 5
+MOE_W4_DECODE_MAX_T = 7
 MOE_W4_GEMV_MAX_T = 8
 MOE_W4_FORWARD_GEMV = 1
 MOE_W4_FORWARD_GROUPED = 2
