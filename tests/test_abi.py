@@ -12,6 +12,8 @@ from w4_dequant_grouped_amd import moe_w4 as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_w4.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, ERR_NULL, ERR_DIMS, ERR_TOPK, ERR_GROUP, ERR_ALIGN, ERR_WS, ERR_LAUNCH, ERR_FLAGS = \
     0, -1, -2, -3, -4, -5, -6, -7, -8
@@ -27,8 +29,11 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_w4_\w+)\s*\(", text, re.M)))
+    names = set()
+    for path in HEADERS:
+        text = open(path).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_w4_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -150,3 +155,46 @@ def test_binding_constants_match_the_header():
         m = re.search(r"#define\s+%s\s+(\d+)u?\b" % name, text)
         assert m, name
         assert int(m.group(1)) == getattr(B, name), name
+
+
+# --- decode attention (include/moe_w4_attn.h) ------------------------------------
+
+def _adims(**kw):
+    d = dict(n_ctx=1000, n_q_heads=16, n_kv_heads=2, n_pool_blocks=20, head_dim=128, block=64, flags=0)
+    d.update(kw)
+    return B.make_attn_dims(**d)
+
+
+def _attn(lib, dims, q=FAKE, k=FAKE, v=FAKE, table=FAKE, out=FAKE + 4096, ws=FAKE, ws_bytes=1 << 40):
+    return lib.moe_w4_attn_decode(ctypes.byref(dims) if dims is not None else None, q, k, v, table, out,
+                                  ws, ws_bytes, None)
+
+
+def test_attn_workspace_bytes(lib):
+    n32 = B.moe_w4_attn_workspace_bytes(_adims(n_ctx=32768))
+    n128 = B.moe_w4_attn_workspace_bytes(_adims(n_ctx=131072))
+    assert n32 > 0 and n32 % 256 == 0
+    # at most 256 splits per key/value head: (max, sum) x 16 + 8 x 128 numerators each
+    assert n128 <= 2 * 256 * (2 * 16 + 8 * 128) * 4 + 3 * 256
+    for bad in (_adims(n_ctx=0), _adims(n_ctx=B.MOE_W4_ATTN_MAX_CTX + 1), _adims(n_kv_heads=3),
+                _adims(n_q_heads=32, n_kv_heads=1), _adims(head_dim=64), _adims(block=32),
+                _adims(n_pool_blocks=0), _adims(flags=1)):
+        assert B.moe_w4_attn_workspace_bytes(bad) == 0
+
+
+def test_attn_rejects_bad_arguments(lib):
+    assert _attn(lib, None) == ERR_NULL
+    assert _attn(lib, _adims(flags=2)) == ERR_FLAGS
+    assert _attn(lib, _adims(n_ctx=0)) == ERR_DIMS
+    assert _attn(lib, _adims(n_kv_heads=5)) == ERR_DIMS
+    assert _attn(lib, _adims(head_dim=256)) == ERR_GROUP
+    assert _attn(lib, _adims(block=128)) == ERR_GROUP
+    assert _attn(lib, _adims(), q=None) == ERR_NULL
+    assert _attn(lib, _adims(), table=None) == ERR_NULL
+    assert _attn(lib, _adims(), ws=None) == ERR_NULL
+    assert _attn(lib, _adims(), q=FAKE + 8) == ERR_ALIGN
+    assert _attn(lib, _adims(), k=FAKE + 2) == ERR_ALIGN
+    assert _attn(lib, _adims(), table=FAKE + 2) == ERR_ALIGN
+    assert _attn(lib, _adims(), ws=FAKE + 16) == ERR_ALIGN
+    d = _adims()
+    assert _attn(lib, d, ws_bytes=B.moe_w4_attn_workspace_bytes(d) - 1) == ERR_WS

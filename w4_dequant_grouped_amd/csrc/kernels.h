@@ -83,6 +83,24 @@ struct DecodeBlockArgs {     // route + forward of decode rows (T <= kDecodeMaxT
     int32_t* slots;          // [1 + 3 T k] workspace: selected experts for the down kernel
 };
 
+// Decode attention over a paged KV cache (moe_w4_attn_decode).
+constexpr int kAttnMaxSplits = 256;      // partials per key/value head (combine kernel bound)
+
+struct AttnArgs {
+    const uint16_t* q;       // bf16 [Hkv*G][128]
+    const uint16_t* k_pool;  // bf16 [n_pool][Hkv][64][128]
+    const uint16_t* v_pool;
+    const int32_t* table;    // [ceil(n_ctx / 64)]
+    int n_ctx, Hkv, G, n_pool;
+    int bpw;                 // blocks per workgroup (a multiple of 4)
+    int nsplit;              // workgroups per key/value head
+    float c;                 // softmax scale * log2(e)
+    float* part_m;           // [Hkv*nsplit][16]
+    float* part_l;           // [Hkv*nsplit][16]
+    float* part_a;           // [Hkv*nsplit][GM][128], GM = 8 (G <= 8) or 16
+    uint16_t* out;           // bf16 [Hkv*G][128]
+};
+
 // Optional per-kernel timing: events[2i] / events[2i+1] are recorded on the launch
 // stream before / after the i-th kernel of a call (while capacity allows).
 // Launches kernels and, when the caller supplies events, brackets each one with
@@ -116,5 +134,6 @@ hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& t
 hipError_t launch_forward_decode(const ForwardArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_block_decode(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm);
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t st, KernelTimer& tm);
 
 }  // namespace moe_w4

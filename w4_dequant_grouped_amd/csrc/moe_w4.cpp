@@ -1,9 +1,11 @@
 // C ABI of the W4 MoE block: argument checks, workspace layout, dispatch.
 // Declared and documented in include/moe_w4.h.
 #include "../../include/moe_w4.h"
+#include "../../include/moe_w4_attn.h"
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <string>
 
@@ -309,6 +311,97 @@ int moe_w4_block(const moe_w4_dims* dims, const void* x, const float* router_w,
     return moe_w4_block_timed(dims, x, router_w, router_b, routed, shared, topk_ids, topk_w,
                               expert_counts, expert_offsets, perm, out, workspace, workspace_bytes,
                               hip_stream, nullptr, 0, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// decode attention
+// ---------------------------------------------------------------------------
+namespace {
+
+struct AttnPlan {
+    int nblk, bpw, nsplit, gm;
+    size_t off_l, off_a, total;
+};
+
+bool attn_dims_ok(const moe_w4_attn_dims* d, int* status) {
+    if (!d) { *status = MOE_W4_ERR_NULL; return false; }
+    if (d->flags != 0u) { *status = MOE_W4_ERR_FLAGS; return false; }
+    if (d->n_ctx < 1 || d->n_ctx > MOE_W4_ATTN_MAX_CTX || d->n_q_heads < 1 || d->n_q_heads > 64 ||
+        d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads != 0 || d->n_q_heads / d->n_kv_heads > 16 ||
+        d->n_pool_blocks < 1) {
+        *status = MOE_W4_ERR_DIMS;
+        return false;
+    }
+    if (d->head_dim != 128 || d->block != 64) { *status = MOE_W4_ERR_GROUP; return false; }
+    *status = MOE_W4_OK;
+    return true;
+}
+
+// Blocks per workgroup: a multiple of 4 (one per wavefront per round) chosen so
+// that a key/value head has at most kAttnMaxSplits workgroups.
+AttnPlan attn_plan(const moe_w4_attn_dims* d) {
+    AttnPlan p;
+    p.nblk = (d->n_ctx + d->block - 1) / d->block;
+    const int per = (p.nblk + 4 * moe_w4::kAttnMaxSplits - 1) / (4 * moe_w4::kAttnMaxSplits);
+    p.bpw = 4 * (per < 1 ? 1 : per);
+    p.nsplit = (p.nblk + p.bpw - 1) / p.bpw;
+    p.gm = d->n_q_heads / d->n_kv_heads <= 8 ? 8 : 16;
+    const size_t parts = (size_t)d->n_kv_heads * p.nsplit;
+    p.off_l = align_up(parts * 16 * sizeof(float));
+    p.off_a = p.off_l + align_up(parts * 16 * sizeof(float));
+    p.total = p.off_a + align_up(parts * p.gm * 128 * sizeof(float));
+    return p;
+}
+
+}  // namespace
+
+size_t moe_w4_attn_workspace_bytes(const moe_w4_attn_dims* dims) {
+    int st;
+    if (!attn_dims_ok(dims, &st)) return 0;
+    return attn_plan(dims).total;
+}
+
+int moe_w4_attn_decode_timed(const moe_w4_attn_dims* dims, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table, void* out,
+                             void* workspace, size_t workspace_bytes, void* hip_stream,
+                             void** events, int capacity, int* n_kernels) {
+    if (n_kernels) *n_kernels = 0;
+    int st;
+    if (!attn_dims_ok(dims, &st)) return st;
+    if (!q || !k_pool || !v_pool || !block_table || !out || !workspace) return MOE_W4_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_table, 4) ||
+        !aligned(out, 16) || !aligned(workspace, kAlign))
+        return MOE_W4_ERR_ALIGN;
+    const AttnPlan p = attn_plan(dims);
+    if (workspace_bytes < p.total) return MOE_W4_ERR_WORKSPACE;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    moe_w4::AttnArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_pool = static_cast<const uint16_t*>(k_pool);
+    a.v_pool = static_cast<const uint16_t*>(v_pool);
+    a.table = block_table;
+    a.n_ctx = dims->n_ctx;
+    a.Hkv = dims->n_kv_heads;
+    a.G = dims->n_q_heads / dims->n_kv_heads;
+    a.n_pool = dims->n_pool_blocks;
+    a.bpw = p.bpw;
+    a.nsplit = p.nsplit;
+    a.c = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
+    a.part_m = reinterpret_cast<float*>(ws);
+    a.part_l = reinterpret_cast<float*>(ws + p.off_l);
+    a.part_a = reinterpret_cast<float*>(ws + p.off_a);
+    a.out = static_cast<uint16_t*>(out);
+    moe_w4::KernelTimer tm = make_timer(events, capacity);
+    const hipError_t err = moe_w4::launch_attn_decode(a, static_cast<hipStream_t>(hip_stream), tm);
+    if (n_kernels) *n_kernels = tm.count;
+    return launch_status(err);
+}
+
+int moe_w4_attn_decode(const moe_w4_attn_dims* dims, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_table, void* out,
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return moe_w4_attn_decode_timed(dims, q, k_pool, v_pool, block_table, out, workspace,
+                                    workspace_bytes, hip_stream, nullptr, 0, nullptr);
 }
 
 const char* moe_w4_status_string(int status) {

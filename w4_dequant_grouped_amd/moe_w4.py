@@ -1,6 +1,6 @@
 """Python binding of libmoe_w4.so (argument marshalling only).
 
-The names mirror the C ABI declared in include/moe_w4.h.  torch tensors supply
+The names mirror the C ABI declared in include/moe_w4.h and include/moe_w4_attn.h.  torch tensors supply
 device memory and the current HIP stream; every step of the block runs in the
 library's HIP kernels.  There is no fallback: if the library is missing, the
 calls raise.
@@ -38,9 +38,18 @@ class moe_w4_weights(ctypes.Structure):
     _fields_ = [("gate", moe_w4_mat), ("up", moe_w4_mat), ("down", moe_w4_mat)]
 
 
+class moe_w4_attn_dims(ctypes.Structure):
+    _fields_ = [("n_ctx", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("n_pool_blocks", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+MOE_W4_ATTN_MAX_CTX = 1 << 20
+
 EXPORTS = ("moe_w4_workspace_bytes", "moe_w4_route", "moe_w4_forward", "moe_w4_block",
            "moe_w4_route_timed", "moe_w4_forward_timed", "moe_w4_block_timed",
-           "moe_w4_status_string", "moe_w4_last_error")
+           "moe_w4_status_string", "moe_w4_last_error",
+           "moe_w4_attn_workspace_bytes", "moe_w4_attn_decode", "moe_w4_attn_decode_timed")
 
 _lib = None
 
@@ -77,6 +86,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_w4_status_string.restype = ctypes.c_char_p
     lib.moe_w4_last_error.argtypes = []
     lib.moe_w4_last_error.restype = ctypes.c_char_p
+    A = ctypes.POINTER(moe_w4_attn_dims)
+    lib.moe_w4_attn_workspace_bytes.argtypes = [A]
+    lib.moe_w4_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_w4_attn_decode.argtypes = [A, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_w4_attn_decode.restype = ctypes.c_int
+    lib.moe_w4_attn_decode_timed.argtypes = lib.moe_w4_attn_decode.argtypes + [P, ctypes.c_int, P]
+    lib.moe_w4_attn_decode_timed.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -314,3 +330,54 @@ class Block:
         nf = moe_w4_forward_timed(self.dims, x, self.routed_struct, self.shared_struct, self.routing,
                                   self.out, self.workspace, forward_events)
         return nr, nf
+
+
+# ---------------------------------------------------------------------------
+# decode attention over a paged KV cache (include/moe_w4_attn.h)
+# ---------------------------------------------------------------------------
+def make_attn_dims(n_ctx: int, n_q_heads: int, n_kv_heads: int, n_pool_blocks: int,
+                   head_dim: int = 128, block: int = 64, flags: int = 0) -> moe_w4_attn_dims:
+    return moe_w4_attn_dims(n_ctx, n_q_heads, n_kv_heads, head_dim, block, n_pool_blocks, flags)
+
+
+def moe_w4_attn_workspace_bytes(dims: moe_w4_attn_dims) -> int:
+    return int(load_library().moe_w4_attn_workspace_bytes(ctypes.byref(dims)))
+
+
+def moe_w4_attn_decode(dims: moe_w4_attn_dims, q: torch.Tensor, k_pool: torch.Tensor,
+                       v_pool: torch.Tensor, table: torch.Tensor, out: torch.Tensor,
+                       workspace: torch.Tensor, events=None) -> int:
+    """One decode-attention step on the current stream; returns the kernel count."""
+    for t, dt, name in ((q, torch.bfloat16, "q"), (k_pool, torch.bfloat16, "k_pool"),
+                        (v_pool, torch.bfloat16, "v_pool"), (table, torch.int32, "table"),
+                        (out, torch.bfloat16, "out"), (workspace, torch.uint8, "workspace")):
+        _dev(t, dt, name)
+    if table.numel() < (dims.n_ctx + dims.block - 1) // dims.block:
+        raise ValueError("block table shorter than the context")
+    arr, cap = _events_arg(events)
+    n = ctypes.c_int(0)
+    st = load_library().moe_w4_attn_decode_timed(
+        ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(table), _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(), arr, cap, ctypes.byref(n))
+    _check(st, "moe_w4_attn_decode")
+    return n.value
+
+
+class AttnDecode:
+    """One decode-attention step bound to its cache, for repeated calls."""
+
+    def __init__(self, shape, inputs):
+        self.inputs = inputs
+        self.dims = make_attn_dims(shape.n_ctx, shape.n_q_heads, shape.n_kv_heads,
+                                   inputs.k_pool.shape[0], shape.head_dim, shape.block)
+        n = moe_w4_attn_workspace_bytes(self.dims)
+        if n == 0:
+            raise ValueError("invalid attention dims")
+        dev = inputs.q.device
+        self.workspace = torch.zeros(n, dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(inputs.q)
+
+    def __call__(self, events=None) -> torch.Tensor:
+        x = self.inputs
+        moe_w4_attn_decode(self.dims, x.q, x.k_pool, x.v_pool, x.table, self.out, self.workspace, events)
+        return self.out
