@@ -19,6 +19,13 @@ The same line carries:
                 same workload on this host
   prefill       the T=2048 Zipf-skewed prefill layer-call (8 layers rotated):
                 tokens/s and the MFMA roofline of its dominant kernel
+
+Other modes (their own JSON line):
+  --crossover   verification batches: GEMV vs grouped path per T (1..64)
+  --stack       the 40-layer stack: T=16384 prefill, then T=1 decode steps
+  --attn        decode attention over a paged KV cache (16 query heads over 2
+                key/value heads, head dim 128, 64-token blocks) at 32K, 64K and
+                128K tokens of context, 10 caches in rotation
 """
 from __future__ import annotations
 
@@ -40,6 +47,7 @@ METRIC = "MoE-layer tokens/sec + %HBM roofline (T=1) and %MFMA peak (T=2048)"
 ROUTE_LARGE = ["router_split", "router_logits", "router_topk", "router_group"]
 BLOCK_DECODE = ["decode_logits_shared", "decode_route_gateup", "decode_down"]
 FWD_GROUPED = ["grouped_gateup", "grouped_down", "finalize"]
+ATTN = ["attn_split", "attn_combine"]
 
 
 # ---------------------------------------------------------------------------
@@ -501,6 +509,114 @@ def run_crossover(args, ev):
             "steps": steps, "warmup": warm, "default_gemv_max_T": B.MOE_W4_DECODE_MAX_T, "rows": rows}
 
 
+def run_attn(args, ev):
+    """Decode attention: one query token over n_ctx cached tokens, for the model's
+    10 full-attention layers (10 caches used in rotation, so a step reads every
+    cache from HBM).  Each step is the 10 calls captured as a HIP graph."""
+    import torch
+    from w4_dequant_grouped_amd import moe_w4 as B
+    from w4_dequant_grouped_amd import synth_attn as SA
+
+    L = 10
+    rows = []
+    for name in args.attn_contexts.split(","):
+        shape, seed = SA.ATTN_WORKLOADS[name]
+        print(f"[bench] attn {name}", file=sys.stderr, flush=True)
+        res = {"workload": name, "n_ctx": shape.n_ctx}
+        for variant in args.attn_variants.split(","):
+            if variant == "unpacked":
+                # every query head with its own copy of its cache head: the reads an
+                # unpacked kernel makes (G times the bytes)
+                sh = SA.AttnShape(n_ctx=shape.n_ctx, n_q_heads=16, n_kv_heads=16)
+            else:
+                sh = shape
+            steps = []
+            for l in range(L):
+                x = SA.draw_attn(sh, seed + 1000 * l, device="cuda")
+                if variant == "contiguous":
+                    x.table = torch.arange(sh.n_blocks, dtype=torch.int32, device="cuda")
+                steps.append(B.AttnDecode(sh, x))
+            for st in steps:
+                st()
+            torch.cuda.synchronize()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for st in steps:
+                    st()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            ref = [st.out.clone() for st in steps]
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for st in steps:
+                    st()
+            g.replay()
+            torch.cuda.synchronize()
+            for st, r in zip(steps, ref):
+                if not torch.equal(st.out, r):
+                    raise RuntimeError("attention graph replay differs from the eager calls")
+            elapsed = time_steps(lambda i=0: g.replay(), args.steps, args.warmup)
+            us = 1e6 * elapsed / (args.steps * L)
+            nbytes = SA.attn_bytes(sh)
+            ent = {"us_per_layer": round(us, 3), "alg_MB": round(nbytes / 1e6, 2),
+                   "alg_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                   "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            if variant == "paged":
+                kt = {n: 0.0 for n in ATTN}
+                reps = 5
+                evs = []
+                for r in range(reps):
+                    for st in steps:
+                        e = ev.create(4)
+                        assert st.timed(e) == 2
+                        evs.append(e)
+                torch.cuda.synchronize()
+                for e in evs:
+                    kt["attn_split"] += ev.elapsed_ms(e[0], e[1])
+                    kt["attn_combine"] += ev.elapsed_ms(e[2], e[3])
+                    ev.destroy(e)
+                kt = {n: 1e3 * v / len(evs) for n, v in kt.items()}
+                split_bytes = nbytes - 2 * sh.n_q_heads * sh.head_dim * 2   # K, V, q, table
+                ach = split_bytes / (kt["attn_split"] * 1e-6) / 1e9
+                ent["roofline"] = {"bound": "hbm", "kernel": "attn_split", "achieved": round(ach, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                                   "traffic": traffic_from_profiles("attn_split", name),
+                                   "alg_bytes_per_launch": int(split_bytes),
+                                   "avg_launch_us": round(kt["attn_split"], 3),
+                                   "kernel_us": {n: round(v, 3) for n, v in kt.items()}}
+            res[variant] = ent
+            del steps, g
+            torch.cuda.empty_cache()
+        if "unpacked" in res and "paged" in res:
+            res["packing_speedup"] = round(res["unpacked"]["us_per_layer"] / res["paged"]["us_per_layer"], 3)
+        if "contiguous" in res and "paged" in res:
+            res["paged_vs_contiguous"] = round(res["contiguous"]["us_per_layer"] / res["paged"]["us_per_layer"], 3)
+        rows.append(res)
+    return rows
+
+
+def attn_cpu_baseline(budget_s=15.0):
+    """The attention oracle on this host, on a bounded sample (32K context)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attn_oracle as A
+    from w4_dequant_grouped_amd import synth_attn as SA
+
+    shape, seed = SA.ATTN_WORKLOADS["ctx32k"]
+    x = SA.draw_attn(shape, seed)
+    calls = 0
+    t0 = time.perf_counter()
+    while calls < 20 and time.perf_counter() - t0 < budget_s:
+        A.decode_attention(x.q, x.k_pool, x.v_pool, x.table, shape.n_ctx)
+        calls += 1
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(calls / el, 3), "unit": "layer-steps/s (32K context)", "cores": threads,
+            "kind": "oracle", "sample": f"{calls} decode-attention steps at 32K context, float64 NumPy "
+                                        f"oracle, {el:.1f} s"}
+
+
 def cpu_baseline(T=1, max_calls=24, budget_s=20.0):
     """The oracle as it stands, on this host's cores, on a bounded sample."""
     import numpy as np  # noqa: F401
@@ -545,6 +661,12 @@ def main():
                     help="only run the 40-layer stack (T=16384 prefill + T=1 decode steps)")
     ap.add_argument("--stack-tokens", type=int, default=16384)
     ap.add_argument("--stack-decode-steps", type=int, default=256)
+    ap.add_argument("--attn", action="store_true",
+                    help="only run decode attention over a paged KV cache (32K/64K/128K context)")
+    ap.add_argument("--attn-contexts", default="ctx32k,ctx64k,ctx128k")
+    ap.add_argument("--attn-variants", default="paged,contiguous,unpacked",
+                    help="paged: seeded block table; contiguous: identity table; unpacked: every "
+                         "query head with its own cache head (the reads of an unpacked kernel)")
     ap.add_argument("--crossover", action="store_true",
                     help="only run the verification-batch study: GEMV vs grouped path per T")
     ap.add_argument("--crossover-tokens", default="1,2,3,4,5,6,7,8,12,16,24,32,48,64")
@@ -575,6 +697,13 @@ def main():
         return
     B.load_library()          # raises if the HIP library is missing: there is no fallback
     ev = HipEvents()
+    if args.attn:
+        line = {"attention": run_attn(args, ev), "n_gpus": 1, "dtype": "bf16",
+                "data": "synthetic (seeded bf16 q, K, V; seeded block tables)", "source_hash": source_hash()}
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = attn_cpu_baseline()
+        print(json.dumps(line), flush=True)
+        return
     if args.crossover:
         line = {"crossover": run_crossover(args, ev), "n_gpus": 1, "dtype": "bf16",
                 "data": "synthetic (seeded W4 layers and activations)", "source_hash": source_hash()}

@@ -18,10 +18,11 @@
 //                  16x16x32 bf16 MFMA chain per 16 keys (keys are the M side, query
 //                  heads the N side, so a K row is read once for all G heads); the
 //                  online softmax runs on the MFMA output layout; p V runs on the
-//                  VALU with each lane owning 8 columns of d for 16 of the keys
-//                  (V rows are d-contiguous, the wrong way round for an MFMA
-//                  operand).  The four wavefronts' states are merged in LDS and
-//                  written as one partial (max, sum, numerator) per head.
+//                  VALU with each lane owning 8 columns of d for 16 of the keys,
+//                  two keys per v_dot2_f32_bf16 (V rows are d-contiguous, the
+//                  wrong way round for an MFMA operand).  The four wavefronts'
+//                  states are merged in LDS and written as one partial (max,
+//                  sum, numerator) per head.
 //   k_attn_combine grid (Hq, 8): merges the partials of every split.
 #include "device.h"
 #include "kernels.h"
@@ -42,12 +43,9 @@ struct AttnLds {
     float acc[kAttnWaves][GM][kAttnD];
 };
 
-__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
-
 // GM: query heads per group the accumulators are sized for (a.G <= GM).
 template <int GM>
-__global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
+__global__ __launch_bounds__(256, GM <= 8 ? 2 : 1) void k_attn_split(AttnArgs a) {
     __shared__ AttnLds<GM> sm;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -139,22 +137,33 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[g][e] *= cg;
         }
+        // keys 4j + r4 and 4j + 4 + r4 in pairs: one v_dot2_f32_bf16 per head and
+        // column takes both (p rounded to bf16, V pairs gathered by byte permutes)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int key = 4 * j + r4;
-            const u32x4 v = key < nvalid ? vf[j] : u32x4{0u, 0u, 0u, 0u};
-            const float vv[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                                 bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-            float pk[GM];
+        for (int j = 0; j < 16; j += 2) {
+            const int ka = 4 * j + r4, kb = ka + 4;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 va = ka < nvalid ? vf[j] : z;
+            const u32x4 vb = kb < nvalid ? vf[j + 1] : z;
+            const uint32_t vp[8] = {
+                __builtin_amdgcn_perm(vb.x, va.x, 0x05040100u), __builtin_amdgcn_perm(vb.x, va.x, 0x07060302u),
+                __builtin_amdgcn_perm(vb.y, va.y, 0x05040100u), __builtin_amdgcn_perm(vb.y, va.y, 0x07060302u),
+                __builtin_amdgcn_perm(vb.z, va.z, 0x05040100u), __builtin_amdgcn_perm(vb.z, va.z, 0x07060302u),
+                __builtin_amdgcn_perm(vb.w, va.w, 0x05040100u), __builtin_amdgcn_perm(vb.w, va.w, 0x07060302u)};
+            uint32_t pp[GM];
 #pragma unroll
             for (int g4 = 0; g4 < GM / 4; ++g4) {
-                const float4 q4 = *reinterpret_cast<const float4*>(&sm.p[wave][key][4 * g4]);
-                pk[4 * g4] = q4.x; pk[4 * g4 + 1] = q4.y; pk[4 * g4 + 2] = q4.z; pk[4 * g4 + 3] = q4.w;
+                const float4 pa = *reinterpret_cast<const float4*>(&sm.p[wave][ka][4 * g4]);
+                const float4 pb = *reinterpret_cast<const float4*>(&sm.p[wave][kb][4 * g4]);
+                pp[4 * g4] = pack_bf16x2(pa.x, pb.x);
+                pp[4 * g4 + 1] = pack_bf16x2(pa.y, pb.y);
+                pp[4 * g4 + 2] = pack_bf16x2(pa.z, pb.z);
+                pp[4 * g4 + 3] = pack_bf16x2(pa.w, pb.w);
             }
 #pragma unroll
             for (int g = 0; g < GM; ++g)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pk[g], vv[e], acc[g][e]);
+                for (int e = 0; e < 8; ++e) acc[g][e] = dot2_bf16(pp[g], vp[e], acc[g][e]);
         }
     }
 

@@ -377,7 +377,13 @@ class AttnDecode:
         self.workspace = torch.zeros(n, dtype=torch.uint8, device=dev)
         self.out = torch.empty_like(inputs.q)
 
-    def __call__(self, events=None) -> torch.Tensor:
+    def __call__(self) -> torch.Tensor:
         x = self.inputs
-        moe_w4_attn_decode(self.dims, x.q, x.k_pool, x.v_pool, x.table, self.out, self.workspace, events)
+        moe_w4_attn_decode(self.dims, x.q, x.k_pool, x.v_pool, x.table, self.out, self.workspace)
         return self.out
+
+    def timed(self, events) -> int:
+        """One call with an event pair per kernel; returns the kernel count."""
+        x = self.inputs
+        return moe_w4_attn_decode(self.dims, x.q, x.k_pool, x.v_pool, x.table, self.out, self.workspace,
+                                  events)
