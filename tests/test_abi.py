@@ -198,3 +198,41 @@ def test_attn_rejects_bad_arguments(lib):
     assert _attn(lib, _adims(), ws=FAKE + 16) == ERR_ALIGN
     d = _adims()
     assert _attn(lib, d, ws_bytes=B.moe_w4_attn_workspace_bytes(d) - 1) == ERR_WS
+
+
+# --- Gated DeltaNet scan (include/moe_w4_gdn.h) -----------------------------------
+
+def _gdims(**kw):
+    d = dict(T=100, n_v_heads=32, n_k_heads=16, dim=128, flags=0)
+    d.update(kw)
+    return B.moe_w4_gdn_dims(d["T"], d["n_v_heads"], d["n_k_heads"], d["dim"], d["flags"])
+
+
+def _gdn(lib, dims, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, out=FAKE + 4096):
+    return lib.moe_w4_gdn_scan(ctypes.byref(dims) if dims is not None else None, q, k, v, g, beta, state,
+                               out, None)
+
+
+def test_gdn_rejects_bad_arguments(lib):
+    assert _gdn(lib, None) == ERR_NULL
+    assert _gdn(lib, _gdims(flags=1)) == ERR_FLAGS
+    assert _gdn(lib, _gdims(T=-1)) == ERR_DIMS
+    assert _gdn(lib, _gdims(T=B.MOE_W4_GDN_MAX_T + 1)) == ERR_DIMS
+    assert _gdn(lib, _gdims(n_k_heads=5)) == ERR_DIMS
+    assert _gdn(lib, _gdims(n_v_heads=0)) == ERR_DIMS
+    assert _gdn(lib, _gdims(dim=64)) == ERR_GROUP
+    assert _gdn(lib, _gdims(T=0)) == OK                 # nothing to do
+    assert _gdn(lib, _gdims(), q=None) == ERR_NULL
+    assert _gdn(lib, _gdims(), state=None) == ERR_NULL
+    assert _gdn(lib, _gdims(), q=FAKE + 8) == ERR_ALIGN
+    assert _gdn(lib, _gdims(), g=FAKE + 2) == ERR_ALIGN
+    assert _gdn(lib, _gdims(), state=FAKE + 4) == ERR_ALIGN
+    assert _gdn(lib, _gdims(), out=FAKE + 2) == ERR_ALIGN
+
+
+def test_size_limits_match_the_headers():
+    for header, name, value in (("moe_w4_attn.h", "MOE_W4_ATTN_MAX_CTX", B.MOE_W4_ATTN_MAX_CTX),
+                                ("moe_w4_gdn.h", "MOE_W4_GDN_MAX_T", B.MOE_W4_GDN_MAX_T)):
+        text = open(os.path.join(ROOT, "include", header)).read()
+        m = re.search(r"#define\s+%s\s+\(1 << (\d+)\)" % name, text)
+        assert m and (1 << int(m.group(1))) == value, name

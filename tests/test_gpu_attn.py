@@ -1,10 +1,10 @@
 """GPU parity of decode attention over a paged KV cache, through the C ABI.
 
 Every case compares moe_w4_attn_decode with the float64 oracle on the same seeded
-inputs.  Tolerance: max|gpu - ref| / max|ref| <= 4e-3.  The output is rounded
-once to bf16 (relative error <= 2^-9 ~ 2e-3 per element); scores, softmax and
-sums are fp32 (errors near 1e-6 at these lengths), so twice the rounding bound
-leaves room without hiding a wrong weight or row.
+inputs.  Tolerance: max|gpu - ref| / max|ref| <= 5e-3.  The output is rounded
+once to bf16 (round to nearest moves a value by at most half an ulp, 2^-8 ~
+3.9e-3 of itself); the softmax weights enter the p.V sums rounded to bf16 too,
+but their rounding errors average out over the keys; scores and sums are fp32.
 """
 import numpy as np
 import pytest
@@ -16,7 +16,7 @@ from w4_dequant_grouped_amd import synth_attn as SA
 
 pytestmark = pytest.mark.gpu
 
-TOL = 4e-3
+TOL = 5e-3
 
 
 @pytest.fixture(scope="module", autouse=True)

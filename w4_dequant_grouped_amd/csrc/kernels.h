@@ -101,6 +101,18 @@ struct AttnArgs {
     uint16_t* out;           // bf16 [Hkv*G][128]
 };
 
+// Gated DeltaNet scan (moe_w4_gdn_scan).
+struct GdnArgs {
+    const uint16_t* q;       // bf16 [T][Hk][128]
+    const uint16_t* k;
+    const uint16_t* v;       // bf16 [T][Hv][128]
+    const float* g;          // [T][Hv] log decay
+    const float* beta;       // [T][Hv]
+    float* state;            // [Hv][128][128], read then overwritten
+    uint16_t* out;           // bf16 [T][Hv][128]
+    int T, Hv, Hk, rep;      // rep = Hv / Hk
+};
+
 // Optional per-kernel timing: events[2i] / events[2i+1] are recorded on the launch
 // stream before / after the i-th kernel of a call (while capacity allows).
 // Launches kernels and, when the caller supplies events, brackets each one with
@@ -135,5 +147,6 @@ hipError_t launch_forward_decode(const ForwardArgs& a, hipStream_t st, KernelTim
 hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_block_decode(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t st, KernelTimer& tm);
+hipError_t launch_gdn_scan(const GdnArgs& a, hipStream_t st, KernelTimer& tm);
 
 }  // namespace moe_w4

@@ -46,10 +46,19 @@ class moe_w4_attn_dims(ctypes.Structure):
 
 MOE_W4_ATTN_MAX_CTX = 1 << 20
 
+
+class moe_w4_gdn_dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("n_v_heads", ctypes.c_int32), ("n_k_heads", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+MOE_W4_GDN_MAX_T = 1 << 20
+
 EXPORTS = ("moe_w4_workspace_bytes", "moe_w4_route", "moe_w4_forward", "moe_w4_block",
            "moe_w4_route_timed", "moe_w4_forward_timed", "moe_w4_block_timed",
            "moe_w4_status_string", "moe_w4_last_error",
-           "moe_w4_attn_workspace_bytes", "moe_w4_attn_decode", "moe_w4_attn_decode_timed")
+           "moe_w4_attn_workspace_bytes", "moe_w4_attn_decode", "moe_w4_attn_decode_timed",
+           "moe_w4_gdn_scan", "moe_w4_gdn_scan_timed")
 
 _lib = None
 
@@ -93,6 +102,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_w4_attn_decode.restype = ctypes.c_int
     lib.moe_w4_attn_decode_timed.argtypes = lib.moe_w4_attn_decode.argtypes + [P, ctypes.c_int, P]
     lib.moe_w4_attn_decode_timed.restype = ctypes.c_int
+    D = ctypes.POINTER(moe_w4_gdn_dims)
+    lib.moe_w4_gdn_scan.argtypes = [D, P, P, P, P, P, P, P, P]
+    lib.moe_w4_gdn_scan.restype = ctypes.c_int
+    lib.moe_w4_gdn_scan_timed.argtypes = lib.moe_w4_gdn_scan.argtypes + [P, ctypes.c_int, P]
+    lib.moe_w4_gdn_scan_timed.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -387,3 +401,29 @@ class AttnDecode:
         x = self.inputs
         return moe_w4_attn_decode(self.dims, x.q, x.k_pool, x.v_pool, x.table, self.out, self.workspace,
                                   events)
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet scan (include/moe_w4_gdn.h)
+# ---------------------------------------------------------------------------
+def moe_w4_gdn_scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, state: torch.Tensor, out: torch.Tensor, events=None) -> int:
+    """One scan on the current stream: state is updated in place, out overwritten.
+    Returns the kernel count."""
+    for t, dt, name in ((q, torch.bfloat16, "q"), (k, torch.bfloat16, "k"), (v, torch.bfloat16, "v"),
+                        (g, torch.float32, "g"), (beta, torch.float32, "beta"),
+                        (state, torch.float32, "state"), (out, torch.bfloat16, "out")):
+        _dev(t, dt, name)
+    T, Hk, d = q.shape
+    Hv = v.shape[1]
+    if k.shape != q.shape or v.shape != (T, Hv, d) or g.shape != (T, Hv) or beta.shape != (T, Hv) \
+            or state.shape != (Hv, d, d) or out.shape != (T, Hv, d):
+        raise ValueError("inconsistent Gated DeltaNet shapes")
+    dims = moe_w4_gdn_dims(T, Hv, Hk, d, 0)
+    arr, cap = _events_arg(events)
+    n = ctypes.c_int(0)
+    st = load_library().moe_w4_gdn_scan_timed(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
+        _stream(), arr, cap, ctypes.byref(n))
+    _check(st, "moe_w4_gdn_scan")
+    return n.value
