@@ -26,6 +26,9 @@ Other modes (their own JSON line):
   --attn        decode attention over a paged KV cache (16 query heads over 2
                 key/value heads, head dim 128, 64-token blocks) at 32K, 64K and
                 128K tokens of context, 10 caches in rotation
+  --gdn         the Gated DeltaNet scan (32 value heads over 16 query/key heads,
+                dimension 128): prefill T=512 and T=2048, and T=1 decode steps
+                over 30 layer states in rotation
 """
 from __future__ import annotations
 
@@ -48,6 +51,7 @@ ROUTE_LARGE = ["router_split", "router_logits", "router_topk", "router_group"]
 BLOCK_DECODE = ["decode_logits_shared", "decode_route_gateup", "decode_down"]
 FWD_GROUPED = ["grouped_gateup", "grouped_down", "finalize"]
 ATTN = ["attn_split", "attn_combine"]
+VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector peak (256 CUs x 2.4 GHz), TFLOP/s
 
 
 # ---------------------------------------------------------------------------
@@ -596,6 +600,105 @@ def run_attn(args, ev):
     return rows
 
 
+def run_gdn(args, ev):
+    """Gated DeltaNet scan: prefill scans (T=512, 2048) over 4 layers in rotation, and
+    T=1 decode steps over 30 layer states in rotation (a step is the 30 scans,
+    captured as a HIP graph and checked against the eager calls)."""
+    import torch
+    from w4_dequant_grouped_amd import moe_w4 as B
+    from w4_dequant_grouped_amd import synth_gdn as SG
+
+    res = {}
+    for name, L in (("prefill512", 4), ("prefill2048", 4), ("decode", 30)):
+        shape, seed = SG.GDN_WORKLOADS[name]
+        print(f"[bench] gdn {name}", file=sys.stderr, flush=True)
+        xs = [SG.draw_gdn(shape, seed + 100 * l, device="cuda") for l in range(L)]
+        outs = [torch.empty_like(x.v) for x in xs]
+        states = [x.state.clone() for x in xs]
+
+        def body():
+            for x, o, st in zip(xs, outs, states):
+                B.moe_w4_gdn_scan(x.q, x.k, x.v, x.g, x.beta, st, o)
+
+        body()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            body()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        # a replay must equal the eager calls from the same states
+        snap = [st.clone() for st in states]
+        body()
+        torch.cuda.synchronize()
+        ref = [o.clone() for o in outs] + [st.clone() for st in states]
+        for st, s0 in zip(states, snap):
+            st.copy_(s0)
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(outs + states, ref)):
+            raise RuntimeError("Gated DeltaNet graph replay differs from the eager calls")
+        steps = args.steps if name == "decode" else max(5, args.steps // 10)
+        elapsed = time_steps(lambda i=0: g.replay(), steps, args.warmup)
+        us = 1e6 * elapsed / (steps * L)
+        evs = []
+        for r in range(3):
+            for x, o, st in zip(xs, outs, states):
+                e = ev.create(2)
+                assert B.moe_w4_gdn_scan(x.q, x.k, x.v, x.g, x.beta, st, o, events=e) == 1
+                evs.append(e)
+        torch.cuda.synchronize()
+        k_us = 1e3 * sum(ev.elapsed_ms(e[0], e[1]) for e in evs) / len(evs)
+        for e in evs:
+            ev.destroy(e)
+        nbytes, flops = SG.gdn_bytes(shape), SG.gdn_flops(shape)
+        ent = {"T": shape.T, "layers": L, "us_per_layer": round(us, 3),
+               "tokens_per_s": round(shape.T / (us * 1e-6), 1), "alg_MB": round(nbytes / 1e6, 3),
+               "alg_GFLOP": round(flops / 1e9, 3), "kernel_us": round(k_us, 3)}
+        if name == "decode":
+            ach = nbytes / (k_us * 1e-6) / 1e9
+            ent["roofline"] = {"bound": "hbm", "kernel": "gdn_scan", "achieved": round(ach, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                               "traffic": traffic_from_profiles("gdn_scan", name),
+                               "alg_bytes_per_launch": int(nbytes), "avg_launch_us": round(k_us, 3)}
+        else:
+            ach = flops / (k_us * 1e-6) / 1e12
+            ent["roofline"] = {"bound": "alu", "kernel": "gdn_scan", "achieved": round(ach, 2),
+                               "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(ach / VALU_FP32_PEAK_TFLOPS, 4),
+                               "traffic": traffic_from_profiles("gdn_scan", name),
+                               "alg_flops_per_launch": int(flops), "avg_launch_us": round(k_us, 3)}
+        res[name] = ent
+        del xs, outs, states, g
+        torch.cuda.empty_cache()
+    return res
+
+
+def gdn_cpu_baseline(budget_s=15.0):
+    """The scan oracle on this host, on a bounded sample (T=512, full heads)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import gdn_oracle as D
+    from w4_dequant_grouped_amd import synth_gdn as SG
+
+    shape, seed = SG.GDN_WORKLOADS["prefill512"]
+    x = SG.draw_gdn(shape, seed)
+    calls = 0
+    t0 = time.perf_counter()
+    while calls < 10 and time.perf_counter() - t0 < budget_s:
+        D.gdn_scan(x.q, x.k, x.v, x.g, x.beta, x.state)
+        calls += 1
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(calls * shape.T / el, 1), "unit": "tokens/s (one layer, T=512)", "cores": threads,
+            "kind": "oracle", "sample": f"{calls} scans of T=512 over 32 value heads, float64 NumPy oracle, "
+                                        f"{el:.1f} s"}
+
+
 def attn_cpu_baseline(budget_s=15.0):
     """The attention oracle on this host, on a bounded sample (32K context)."""
     from threadpoolctl import threadpool_info
@@ -661,6 +764,8 @@ def main():
                     help="only run the 40-layer stack (T=16384 prefill + T=1 decode steps)")
     ap.add_argument("--stack-tokens", type=int, default=16384)
     ap.add_argument("--stack-decode-steps", type=int, default=256)
+    ap.add_argument("--gdn", action="store_true",
+                    help="only run the Gated DeltaNet scan (prefill T=512/2048, T=1 decode steps)")
     ap.add_argument("--attn", action="store_true",
                     help="only run decode attention over a paged KV cache (32K/64K/128K context)")
     ap.add_argument("--attn-contexts", default="ctx32k,ctx64k,ctx128k")
@@ -697,6 +802,14 @@ def main():
         return
     B.load_library()          # raises if the HIP library is missing: there is no fallback
     ev = HipEvents()
+    if args.gdn:
+        line = {"gated_deltanet": run_gdn(args, ev), "n_gpus": 1, "dtype": "fp32 state, bf16 io",
+                "data": "synthetic (seeded q, k, v, decays, write strengths, states)",
+                "source_hash": source_hash()}
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = gdn_cpu_baseline()
+        print(json.dumps(line), flush=True)
+        return
     if args.attn:
         line = {"attention": run_attn(args, ev), "n_gpus": 1, "dtype": "bf16",
                 "data": "synthetic (seeded bf16 q, K, V; seeded block tables)", "source_hash": source_hash()}

@@ -84,30 +84,53 @@ __global__ __launch_bounds__(256) void k_gdn_scan(GdnArgs a) {
             if (lane == 0) s_kq[t] = p;
         }
         __syncthreads();
-        // the sequential steps
-        for (int t = 0; t < nt; ++t) {
+        // the sequential steps: the next token's operands are read from LDS while
+        // the current token's dependent chain (dots, row sums, update) runs
+        struct Tok {
+            float k[8], q[8];
+            float al, b, v, kq;
+        };
+        auto fetch = [&](Tok& o, int t) {
             const float4 k0 = *reinterpret_cast<const float4*>(&s_k[t][col]);
             const float4 k1 = *reinterpret_cast<const float4*>(&s_k[t][col + 4]);
             const float4 q0 = *reinterpret_cast<const float4*>(&s_q[t][col]);
             const float4 q1 = *reinterpret_cast<const float4*>(&s_q[t][col + 4]);
-            const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-            const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            o.k[0] = k0.x; o.k[1] = k0.y; o.k[2] = k0.z; o.k[3] = k0.w;
+            o.k[4] = k1.x; o.k[5] = k1.y; o.k[6] = k1.z; o.k[7] = k1.w;
+            o.q[0] = q0.x; o.q[1] = q0.y; o.q[2] = q0.z; o.q[3] = q0.w;
+            o.q[4] = q1.x; o.q[5] = q1.y; o.q[6] = q1.z; o.q[7] = q1.w;
+            o.al = s_a[t];
+            o.b = s_b[t];
+            o.v = s_v[t][rl];
+            o.kq = s_kq[t];
+        };
+        auto step = [&](const Tok& x, int t) {
             float dk0 = 0.f, dk1 = 0.f, dq0 = 0.f, dq1 = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                dk0 = fmaf(S[e], kv[e], dk0);
-                dk1 = fmaf(S[e + 1], kv[e + 1], dk1);
-                dq0 = fmaf(S[e], qv[e], dq0);
-                dq1 = fmaf(S[e + 1], qv[e + 1], dq1);
+                dk0 = fmaf(S[e], x.k[e], dk0);
+                dk1 = fmaf(S[e + 1], x.k[e + 1], dk1);
+                dq0 = fmaf(S[e], x.q[e], dq0);
+                dq1 = fmaf(S[e + 1], x.q[e + 1], dq1);
             }
             const float dk = row16_sum(dk0 + dk1);
             const float dq = row16_sum(dq0 + dq1);
-            const float al = s_a[t];
-            const float cc = s_b[t] * (s_v[t][rl] - al * dk);
+            const float cc = x.b * (x.v - x.al * dk);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) S[e] = fmaf(al, S[e], cc * kv[e]);
-            if ((lane & 15) == 0) s_o[t][rl] = fmaf(al, dq, cc * s_kq[t]);
+            for (int e = 0; e < 8; ++e) S[e] = fmaf(x.al, S[e], cc * x.k[e]);
+            if ((lane & 15) == 0) s_o[t][rl] = fmaf(x.al, dq, cc * x.kq);
+        };
+        // two tokens per iteration, alternating operand sets (no register copies)
+        Tok ta, tb;
+        fetch(ta, 0);
+        int t = 0;
+        for (; t + 1 < nt; t += 2) {
+            fetch(tb, t + 1);
+            step(ta, t);
+            fetch(ta, min(t + 2, nt - 1));
+            step(tb, t + 1);
         }
+        if (t < nt) step(ta, t);
         __syncthreads();
         // outputs: bf16 pairs, 32 bytes per token
         for (int i = threadIdx.x; i < nt * (kGdnRows / 2); i += blockDim.x) {
