@@ -609,7 +609,9 @@ def run_gdn(args, ev):
     from w4_dequant_grouped_amd import synth_gdn as SG
 
     res = {}
-    for name, L in (("prefill512", 4), ("prefill2048", 4), ("decode", 30)):
+    layers = {"prefill512": 4, "prefill2048": 4, "decode": 30}
+    for name in args.gdn_workloads.split(","):
+        L = layers[name]
         shape, seed = SG.GDN_WORKLOADS[name]
         print(f"[bench] gdn {name}", file=sys.stderr, flush=True)
         xs = [SG.draw_gdn(shape, seed + 100 * l, device="cuda") for l in range(L)]
@@ -766,6 +768,7 @@ def main():
     ap.add_argument("--stack-decode-steps", type=int, default=256)
     ap.add_argument("--gdn", action="store_true",
                     help="only run the Gated DeltaNet scan (prefill T=512/2048, T=1 decode steps)")
+    ap.add_argument("--gdn-workloads", default="prefill512,prefill2048,decode")
     ap.add_argument("--attn", action="store_true",
                     help="only run decode attention over a paged KV cache (32K/64K/128K context)")
     ap.add_argument("--attn-contexts", default="ctx32k,ctx64k,ctx128k")
