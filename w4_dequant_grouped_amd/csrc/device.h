@@ -121,10 +121,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // Within each row of 16 lanes, DPP moves (quad_perm xor 1, xor 2, row_half_mirror,
 // row_mirror) pair every lane with partners covering the whole row; four
 // readlanes then combine the rows.  No LDS traffic, fixed summation order.
+// Every control used here reads a lane of the same row, so the bound-control bit
+// never takes effect with all lanes active; it is set because it lets the
+// compiler fold each move into the add that consumes it (v_add_f32_dpp).
 
 template <int ctrl>
 __device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, true);
 }
 template <int ctrl>
 __device__ __forceinline__ float dpp_f(float v) {
