@@ -36,7 +36,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z) from the hardware exp2 and reciprocal (v_exp_f32,
+// v_rcp_f32: about one ulp each, five VALU ops in all instead of an IEEE
+// division).  Every caller rounds the result to bf16, far coarser than that.
+// Limits: e^-z overflows to +inf for very negative z, giving z * 0 = -0; for
+// large z it underflows to 0, giving z.
+__device__ __forceinline__ float silu(float z) {
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * z);
+    return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // --- 4-bit code unpacking -----------------------------------------------------
 // A dword of packed codes holds k = 0..7 of a row: byte i = (c[2i+1] << 4) | c[2i].

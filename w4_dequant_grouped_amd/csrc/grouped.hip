@@ -25,7 +25,10 @@
 //                     slot order, in fp32, rounded to bf16 (deterministic).
 // A segment is a routed expert's rows (offsets[e]..offsets[e+1], tokens via the
 // permutation) or the shared expert's rows (all tokens, weight 1).  Persistent
-// 4-wavefront workgroups, three per CU, take tiles from per-XCD queues.
+// 4-wavefront workgroups, three per CU, take tiles from per-XCD queues; each
+// queue is a contiguous run of the tile sequence, in which blocks of up to four
+// M-tiles of one segment take each N-tile together, so a weight tile is fetched
+// into an XCD's L2 once per block rather than once per M-tile.
 //
 // MFMA operand layout used (16x16x32, wave64): lane l supplies A row l%16 and B
 // column l%16, each with 8 k values for the k-slot group l/16; D element
@@ -96,40 +99,74 @@ __device__ int build_mtile_prefix(const int32_t* __restrict__ offsets, int E, in
     return s_pre[nseg];
 }
 
-__device__ __forceinline__ TileCtx locate(int mt, const int* s_pre, int nseg, int E, int T, int k,
-                                          const int32_t* __restrict__ offsets) {
-    int lo = 0, hi = nseg - 1;           // last seg with s_pre[seg] <= mt
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= mt) lo = mid; else hi = mid - 1;
+// Last segment s with s_pre[s] <= key.  s_pre is nondecreasing and s_pre[0] = 0,
+// so that is the number of segments with s_pre[s] <= key, minus one: the lanes
+// test 64 segments per step with one LDS read each, and the reads of all steps
+// are independent (one LDS round trip instead of a chain of them).
+__device__ __forceinline__ int find_segment(const int* s_pre, int nseg, int key, int lane) {
+    int cnt = 0;
+    for (int base = 0; base < nseg; base += kWave) {
+        const int s = base + lane;
+        const bool ok = (s < nseg) && (s_pre[min(s, nseg - 1)] <= key);
+        cnt += __popcll(__ballot(ok));
     }
+    return (int)__builtin_amdgcn_readfirstlane(cnt - 1);
+}
+
+__device__ __forceinline__ TileCtx locate(int seg, int mt, const int* s_pre, int E, int T, int k,
+                                          const int32_t* __restrict__ offsets) {
     // every lane holds the same values: keep them in scalar registers
-    lo = (int)__builtin_amdgcn_readfirstlane(lo);
     TileCtx c;
-    c.seg = lo;
-    c.shared = (lo >= E);
-    c.e = c.shared ? 0 : lo;
-    c.m0 = (int)__builtin_amdgcn_readfirstlane((mt - s_pre[lo]) * kBM);
-    c.rows = (int)__builtin_amdgcn_readfirstlane(min(kBM, seg_count(offsets, lo, E, T, k) - c.m0));
-    c.hbase = (int)__builtin_amdgcn_readfirstlane(seg_first(offsets, lo, E, T, k));
+    c.seg = seg;
+    c.shared = (seg >= E);
+    c.e = c.shared ? 0 : seg;
+    c.m0 = (int)__builtin_amdgcn_readfirstlane((mt - s_pre[seg]) * kBM);
+    c.rows = (int)__builtin_amdgcn_readfirstlane(min(kBM, seg_count(offsets, seg, E, T, k) - c.m0));
+    c.hbase = (int)__builtin_amdgcn_readfirstlane(seg_first(offsets, seg, E, T, k));
     return c;
 }
 
-// Tiles are handed out dynamically from 8 queues in the control block.  Queue q
-// holds the M-tiles mt = q (mod 8), each followed by its NT N-tiles; tile index
-// i = q + 8 j of queue entry j maps to (M-tile, N-tile) below.  Workgroup b runs
-// on XCD b mod 8 (round-robin dispatch) and serves queue b mod 8 first, so the
-// N-tiles of one M-tile, which share its gathered activation rows, are normally
-// taken by workgroups of one XCD and find those rows in its L2.  A workgroup
-// whose queue is empty takes tiles from the others.
-__device__ __forceinline__ void tile_coords(int i, int NT, int& mt, int& nt) {
-    mt = (i & 7) + 8 * (i / (8 * NT));
-    nt = (i >> 3) % NT;
+// Tile order.  The n_mt * NT tiles form one sequence: segment by segment, each
+// segment's M-tiles in blocks of kMtBlock, and within a block N-tile by N-tile,
+// the block's M-tiles innermost.  The tiles of one block that share an N-tile
+// read the same weight tile, and the NT tiles of one M-tile read the same
+// gathered activation rows; consecutive entries are taken at nearly the same
+// time by the workgroups of one XCD, so both kinds of operand reach that XCD's
+// L2 once instead of once per M-tile (weights) or per N-tile (activations).
+constexpr int kMtBlock = 4;
+
+// q / d for 0 <= q and d = 1..4 (the M-tiles of a block), by constant divisors.
+__device__ __forceinline__ int div_small(int q, int d) {
+    return d == 4 ? (q >> 2) : d == 3 ? q / 3 : d == 2 ? (q >> 1) : q;
 }
 
-// Entries in queue q.
+// Sequence entry e -> (segment, global M-tile index, N-tile).  s_pre is the
+// exclusive M-tile prefix over the segments; segment s holds entries
+// [s_pre[s] * NT, s_pre[s + 1] * NT).
+__device__ __forceinline__ void tile_coords(int e, int NT, const int* s_pre, int nseg, int lane,
+                                            int& seg, int& mt, int& nt) {
+    static_assert(kMtBlock >= 1 && kMtBlock <= 4, "div_small covers blocks of up to 4 M-tiles");
+    seg = find_segment(s_pre, nseg, e / NT, lane);   // s_pre[s] * NT <= e  <=>  s_pre[s] <= e / NT
+    const int first = s_pre[seg];
+    const int m_s = s_pre[seg + 1] - first;
+    const int r = e - first * NT;
+    const int b = r / (kMtBlock * NT);
+    const int rr = r - b * (kMtBlock * NT);
+    const int cnt = min(kMtBlock, m_s - b * kMtBlock);
+    nt = div_small(rr, cnt);
+    mt = first + b * kMtBlock + (rr - nt * cnt);
+}
+
+// The sequence is cut into 8 contiguous queues of nearly equal length in the
+// control block.  Workgroup b runs on XCD b mod 8 (round-robin dispatch) and
+// serves queue b mod 8 first, so each queue's blocks are normally processed by
+// the workgroups of one XCD.  A workgroup whose queue is empty takes tiles from
+// the others.
+__device__ __forceinline__ int queue_start(int q, int n_mt, int NT) {
+    return (int)(((long long)n_mt * NT * q) >> 3);
+}
 __device__ __forceinline__ int queue_len(int q, int n_mt, int NT) {
-    return (n_mt > q) ? ((n_mt - q + 7) / 8) * NT : 0;
+    return queue_start(q + 1, n_mt, NT) - queue_start(q, n_mt, NT);
 }
 
 __device__ __forceinline__ uint32_t queue_take(uint32_t* ctl, int q) {
@@ -149,7 +186,7 @@ __device__ __forceinline__ int grab_tile(uint32_t* ctl, int n_mt, int NT, int& q
             const uint32_t j = queue_take(ctl, qq);
             if ((int)j < lim) {
                 q = qq;
-                return qq + 8 * (int)j;
+                return queue_start(qq, n_mt, NT) + (int)j;
             }
         }
         empty |= 1u << qq;
@@ -170,7 +207,7 @@ struct TileQueue {
         if (pending) taken = queue_take(ctl, q);
     }
     __device__ __forceinline__ int next(uint32_t* ctl, int n_mt, int NT) {
-        if (pending && (int)taken < queue_len(q, n_mt, NT)) return q + 8 * (int)taken;
+        if (pending && (int)taken < queue_len(q, n_mt, NT)) return queue_start(q, n_mt, NT) + (int)taken;
         if (pending) empty |= 1u << q;
         return grab_tile(ctl, n_mt, NT, q, empty);
     }
@@ -310,42 +347,78 @@ __device__ __forceinline__ void issue_chunk(uint32_t ring, int wave, const TileS
 }
 
 
-// One K chunk of MFMAs over MB valid 16-row blocks (compile-time, so each step
-// is branch-free and the A-fragment reads of a step are issued together).
+// Operands of one K chunk that are read from LDS before the chunk's MFMA work:
+// the wavefront's packed codes and scale/bias words, and the A fragments of the
+// first MFMA step.  They are read right after the barrier that publishes the
+// chunk, ahead of the next chunk's copy instructions, so their LDS latency
+// overlaps the copy issue instead of stalling the first dequantisation.
 template <int NMAT, int NBW, int MB>
-__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const uint8_t* s_b, const uint8_t* s_sb,
-                                          int lane, f32x4 (&acc)[MB][NMAT][NBW]) {
-    const int arow = lane & 15;
-    const int agrp = (lane >> 4) * 4;      // logical 16-byte chunk of the lane's 32 k values
-    const uint32_t magic = 0x64006400u;
-    const uint32_t* sb = reinterpret_cast<const uint32_t*>(s_sb);
-    const int half = (lane >> 5) * 16;     // lanes 32..63 take the chunk's odd group
-    DqConst q[NMAT][NBW];
+struct ChunkOps {
     u32x4 codes[NMAT][NBW];
+    uint32_t sw[NMAT][NBW], bw[NMAT][NBW];
+    bf16x8 a0[MB];
+};
+
+// A fragments of MFMA step j: row (mb * 16 + lane % 16), the lane's logical
+// 16-byte piece (4 * (lane / 16) + j), stored XOR-swizzled by row.
+template <int MB>
+__device__ __forceinline__ void read_a_step(bf16x8 (&a)[MB], const uint8_t* s_a, int lane, int j) {
+    const int arow = lane & 15;
+    const int col = (((lane >> 4) * 4 + j) ^ arow) * 16;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        a[mb] = *reinterpret_cast<const bf16x8*>(s_a + (mb * 16 + arow) * kARow + col);
+}
+
+template <int NMAT, int NBW, int MB>
+__device__ __forceinline__ void read_chunk_ops(ChunkOps<NMAT, NBW, MB>& o, const uint8_t* s_a,
+                                               const uint8_t* s_b, const uint8_t* s_sb, int lane) {
+    const int arow = lane & 15;
+    const uint32_t* sb = reinterpret_cast<const uint32_t*>(s_sb);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
             const int p = m * NBW + nb;
-            const uint32_t sw = sb[p * 32 + arow], bw = sb[p * 32 + 16 + arow];
-            q[m][nb] = make_dq(bf16_to_f32((sw >> half) & 0xFFFFu), bf16_to_f32((bw >> half) & 0xFFFFu));
-            codes[m][nb] = *reinterpret_cast<const u32x4*>(
+            o.sw[m][nb] = sb[p * 32 + arow];
+            o.bw[m][nb] = sb[p * 32 + 16 + arow];
+            o.codes[m][nb] = *reinterpret_cast<const u32x4*>(
                 s_b + p * kBBlk + arow * kBRowBytes + (((lane >> 4) ^ (arow >> 2)) & 3) * 16);
         }
+    read_a_step<MB>(o.a0, s_a, lane, 0);
+}
+
+// One K chunk of MFMAs over MB valid 16-row blocks (compile-time, so each step
+// is branch-free).  The A fragments of step j + 1 are read before step j's
+// dequantisation and MFMAs (two register sets in turn); a scheduling barrier
+// keeps the compiler from sinking those reads next to their use, where each
+// pair of MFMAs would wait a full LDS round trip.
+template <int NMAT, int NBW, int MB>
+__device__ __forceinline__ void mma_chunk(ChunkOps<NMAT, NBW, MB>& o, const uint8_t* s_a, int lane,
+                                          f32x4 (&acc)[MB][NMAT][NBW]) {
+    const uint32_t magic = 0x64006400u;
+    const int half = (lane >> 5) * 16;     // lanes 32..63 take the chunk's odd group
+    DqConst q[NMAT][NBW];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+            q[m][nb] = make_dq(bf16_to_f32((o.sw[m][nb] >> half) & 0xFFFFu),
+                               bf16_to_f32((o.bw[m][nb] >> half) & 0xFFFFu));
+    bf16x8 a1[MB];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int col = ((agrp + j) ^ arow) * 16;
-        bf16x8 a[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            a[mb] = *reinterpret_cast<const bf16x8*>(s_a + (mb * 16 + arow) * kARow + col);
+        bf16x8 (&cur)[MB] = (j & 1) ? a1 : o.a0;
+        bf16x8 (&nxt)[MB] = (j & 1) ? o.a0 : a1;
+        if (j < 3) read_a_step<MB>(nxt, s_a, lane, j + 1);
+        __builtin_amdgcn_sched_barrier(0);
         bf16x8 b[NMAT][NBW];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
-                const uint32_t d = (j == 0) ? codes[m][nb].x : (j == 1) ? codes[m][nb].y
-                                 : (j == 2) ? codes[m][nb].z : codes[m][nb].w;
+                const uint32_t d = (j == 0) ? o.codes[m][nb].x : (j == 1) ? o.codes[m][nb].y
+                                 : (j == 2) ? o.codes[m][nb].z : o.codes[m][nb].w;
                 b[m][nb] = dequant8_mix(d, q[m][nb], magic);
             }
 #pragma unroll
@@ -354,7 +427,7 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const uint8_t* s_b
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb)
-                    acc[mb][m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[m][nb],
+                    acc[mb][m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[mb], b[m][nb],
                                                                             acc[mb][m][nb], 0, 0, 0);
     }
 }
@@ -362,17 +435,20 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const uint8_t* s_b
 // K-loop over the two-stage ring.  Iteration c waits for this wavefront's copies
 // (vmcnt 0), then a barrier makes every wavefront's part of chunk c visible and
 // frees the stage read in iteration c-1, which receives chunk c+1 while chunk c
-// is multiplied.  The loop is unrolled by two so that each stage's LDS offsets
-// are compile-time constants.  Nothing is copied past the end of K.
+// is multiplied.  The chunk's first operands are read from LDS before the copies
+// of chunk c+1 are issued.  The loop is unrolled by two so that each stage's LDS
+// offsets are compile-time constants.  Nothing is copied past the end of K.
 template <int NMAT, int NBW, int MB, int ST>
 __device__ __forceinline__ void kloop_step(uint8_t* s_stage, uint32_t ring, int wave, int lane,
                                            const TileSrc<NMAT, NBW>& t, int c, int nch, bool has_a,
                                            f32x4 (&acc)[MB][NMAT][NBW]) {
     wait_vmcnt<0>();
     __syncthreads();           // chunk c visible to all; the other stage is free
+    ChunkOps<NMAT, NBW, MB> o;
+    read_chunk_ops<NMAT, NBW, MB>(o, s_stage + off_a(ST), s_stage + off_b(ST, wave),
+                                  s_stage + off_sb(ST, wave), lane);
     if (c + 1 < nch) issue_chunk(ring, wave, t, c + 1, has_a);
-    mma_chunk<NMAT, NBW, MB>(s_stage + off_a(ST), s_stage + off_b(ST, wave), s_stage + off_sb(ST, wave),
-                             lane, acc);
+    mma_chunk<NMAT, NBW, MB>(o, s_stage + off_a(ST), lane, acc);
 }
 
 template <int NMAT, int NBW, int MB>
@@ -499,9 +575,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
     if (threadIdx.x == 0) s_next = grab_tile(ctl, n_mt, NT, tq.q, tq.empty);
     __syncthreads();
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
-        int mt, nt;
-        tile_coords(i, NT, mt, nt);
-        const TileCtx c = locate(mt, s_pre, nseg, E, T, k, offsets);
+        int seg, mt, nt;
+        tile_coords(i, NT, s_pre, nseg, lane, seg, mt, nt);
+        const TileCtx c = locate(seg, mt, s_pre, E, T, k, offsets);
         const W4Set& Wset = c.shared ? shared : routed;
         __syncthreads();                 // previous tile's readers are done
         for (int r = threadIdx.x; r < c.rows; r += kThreads)
@@ -561,9 +637,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
     if (threadIdx.x == 0) s_next = grab_tile(ctl, n_mt, NT, tq.q, tq.empty);
     __syncthreads();
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
-        int mt, nt;
-        tile_coords(i, NT, mt, nt);
-        const TileCtx c = locate(mt, s_pre, nseg, E, T, k, offsets);
+        int seg, mt, nt;
+        tile_coords(i, NT, s_pre, nseg, lane, seg, mt, nt);
+        const TileCtx c = locate(seg, mt, s_pre, E, T, k, offsets);
         const W4Set& Wset = c.shared ? shared : routed;
         __syncthreads();
         for (int r = threadIdx.x; r < c.rows; r += kThreads) {
