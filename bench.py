@@ -350,13 +350,16 @@ def run_decode(args, ev):
     return value, ms_per_step, roofline, config
 
 
-def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
+def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2, zipf=True):
+    """One prefill layer-call of T tokens over an L-layer rotation: tokens/s, %MFMA
+    over the layer and of the dominant kernel, and %HBM of the layer-call's
+    algorithmic bytes (W_r, every active expert's W4 bytes once, x and out)."""
     import torch
     from w4_dequant_grouped_amd import moe_w4 as B
     from w4_dequant_grouped_amd import synth
 
     H, I, E, k = 2048, 512, 256, 8
-    shape = synth.BlockShape(T=T, H=H, I=I, E=E, top_k=k, router_bias="zipf")
+    shape = synth.BlockShape(T=T, H=H, I=I, E=E, top_k=k, router_bias="zipf" if zipf else "none")
     layers = make_layers(shape, L, 3000, "cuda")
     ws = B.alloc_workspace(B.make_dims(T, H, I, E, k))
     blocks = [B.Block(layer, T, k, workspace=ws) for layer in layers]
@@ -372,22 +375,51 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2):
     pcts = step_percentiles(lambda i: blocks[i % L](xs[0][i % L]), 16)
     kt = kernel_times(blocks, xs, steps, ev, ROUTE_LARGE + FWD_GROUPED, split_timed(len(ROUTE_LARGE)))
     rows = T * k + T
+    # active experts of each layer's routing (after the last call on its input)
+    active = []
+    for l, blk in enumerate(blocks):
+        blk(xs[0][l])
+        off = blk.routing.offsets.cpu()
+        active.append(int(((off[1:] - off[:-1]) > 0).sum()))
+    gu, dn = expert_bytes(H, I)
+    layer_bytes = sum(E * H * 4 + (a + 1) * (2 * gu + dn) + 2 * T * H * 2 for a in active) / L
+    layer_bytes = float(layer_bytes)
     flops = {"grouped_gateup": 2.0 * rows * H * 2 * I, "grouped_down": 2.0 * rows * I * H}
     dom = max(flops, key=lambda n: kt[n])
     tflops = flops[dom] / (kt[dom] * 1e-6) / 1e12
     layer_flops = flops["grouped_gateup"] + flops["grouped_down"]
+    a_mean = sum(active) / L
+    # algorithmic bytes per launch: every active expert's (and the shared one's)
+    # weights once, the activations read once, the expert-sorted outputs once
+    kbytes = {"grouped_gateup": (a_mean + 1) * 2 * gu + T * H * 2 + rows * I * 2,
+              "grouped_down": (a_mean + 1) * dn + rows * I * 2 + rows * H * 2}
+    if zipf:
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(tflops, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profiles(dom, "prefill"),
+                "alg_flops_per_launch": flops[dom]}
+    else:
+        # at this size the layer's arithmetic intensity (about 64 flop/B) is far
+        # below the ridge point, so HBM bounds it
+        gbs = kbytes[dom] / (kt[dom] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profiles(dom, f"prefill{T}"),
+                "alg_bytes_per_launch": int(kbytes[dom]),
+                "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
     return {
-        "workload": f"prefill T={T} Zipf-skewed router bias, 8-layer rotation, same shapes",
+        "workload": (f"prefill T={T} " + ("Zipf-skewed router bias" if zipf else "uniform-ish routing (no bias)")
+                     + f", {L}-layer rotation, same shapes"),
         "tokens_per_s": round(T / (per_call_ms * 1e-3), 1),
         "ms_per_layer_call": round(per_call_ms, 4),
         "layer_call_mfma_frac": round(layer_flops / (per_call_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "active_experts_per_call": round(sum(active) / L, 2),
+        "layer_call_alg_bytes": int(layer_bytes),
+        "layer_call_hbm_frac": round(layer_bytes / (per_call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_call_ms_p10_p50_p90": pcts,
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(tflops, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profiles(dom, "prefill"),
-                     "alg_flops_per_launch": flops[dom], "avg_launch_us": round(kt[dom], 3),
-                     "kernel_us": {n: round(v, 3) for n, v in kt.items()}},
+        "roofline": dict(roof, avg_launch_us=round(kt[dom], 3),
+                         kernel_us={n: round(v, 3) for n, v in kt.items()}),
     }
 
 
@@ -760,6 +792,9 @@ def main():
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", type=int, default=0, metavar="T",
+                    help="run only the prefill layer-call at T tokens (2048: Zipf-skewed router; "
+                         "any other T: uniform-ish routing) and print its JSON")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the decode step as eager block calls instead of a captured graph")
     ap.add_argument("--stack", action="store_true",
@@ -825,6 +860,12 @@ def main():
                 "data": "synthetic (seeded W4 layers and activations)", "source_hash": source_hash()}
         print(json.dumps(line), flush=True)
         return
+    if args.prefill_only:
+        T = args.prefill_only
+        line = {"prefill": run_prefill(args, ev, T=T, zipf=(T == 2048)), "n_gpus": 1, "dtype": "bf16",
+                "data": "synthetic (seeded W4 layers and activations)", "source_hash": source_hash()}
+        print(json.dumps(line), flush=True)
+        return
     if args.stack:
         print("[bench] stack: 40 layers", file=sys.stderr, flush=True)
         line = {"stack": run_stack(args, ev), "n_gpus": 1, "dtype": "bf16",
@@ -845,6 +886,9 @@ def main():
     if not args.no_prefill:
         print("[bench] prefill T=2048 zipf", file=sys.stderr, flush=True)
         line["prefill"] = run_prefill(args, ev)
+        torch.cuda.empty_cache()
+        print("[bench] prefill T=512 uniform", file=sys.stderr, flush=True)
+        line["prefill_T512"] = run_prefill(args, ev, T=512, zipf=False)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
