@@ -249,8 +249,7 @@ constexpr int kSBWave = kWave * 4;                 // scale/bias words of a wave
 constexpr int kSBBuf = kWaves * kSBWave;           // per stage (1 KiB)
 constexpr int kStageBytes = kABuf + kBBuf + kSBBuf;
 constexpr int kStages = 2;                         // 50 KiB: three workgroups share a CU's 160 KiB
-constexpr int kRowsPerWaveDma = kBM / kWaves;      // A rows copied by each wavefront
-constexpr int kDmaPerWave = kRowsPerWaveDma / 4;   // 4 rows (1 KiB) per A copy instruction
+constexpr int kDmaPerWave = kBM / kWaves / 4;      // A copies per wavefront in a full tile (4 rows, 1 KiB each)
 
 // Per-tile copy addressing.  The bases are wave-uniform (SGPRs, advanced per
 // chunk with scalar adds); the lane offsets are computed once per tile, so a
@@ -274,17 +273,19 @@ __device__ __forceinline__ uint32_t off_sb(int st, int wave) {
     return (uint32_t)(st * kStageBytes + kABuf + kBBuf + wave * kSBWave);
 }
 
-// Lane offsets of the A copies: wavefront w copies rows [16w, 16w+16), four rows
-// (64 lanes x 16 bytes) per instruction; the lane's row is lrow and its 16-byte
-// piece is stored XOR-swizzled by row.  row_of(lrow) gives the source row index
-// (clamped by the caller to the tile's rows, so every address stays inside the
-// operand).
+// Lane offsets of the A copies: copy i of wavefront w moves the four rows of
+// group g = w + 4 i (rows 4 g .. 4 g + 3; 64 lanes x 16 bytes), so a tile of MB
+// row blocks takes exactly MB copies from every wavefront and no wavefront
+// waits longer than the others at the chunk barrier.  The lane's row is lrow and
+// its 16-byte piece is stored XOR-swizzled by row.  row_of(lrow) gives the source
+// row index (clamped by the caller to the tile's rows, so every address stays
+// inside the operand).
 template <typename RowOf>
 __device__ __forceinline__ void a_offsets(uint32_t (&off)[kDmaPerWave], int wave, int lane,
                                           uint32_t row_bytes, RowOf row_of) {
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-        const int lrow = wave * kRowsPerWaveDma + i * 4 + (lane >> 4);
+        const int lrow = (wave + kWaves * i) * 4 + (lane >> 4);
         const int logical = (lane & 15) ^ (lrow & 15);
         off[i] = (uint32_t)row_of(lrow) * row_bytes + (uint32_t)logical * 16u;
     }
@@ -324,18 +325,17 @@ __device__ __forceinline__ void b_addressing(TileSrc<NMAT, NBW>& t, const W4 (&m
     t.K = K;
 }
 
-// Copies of chunk c into stage c mod kStages: the wavefront's A rows (only if
-// any of its 16 rows is in the tile's row blocks), then B codes, then
-// scale/bias -- a fixed count per wavefront.
-template <int NMAT, int NBW>
-__device__ __forceinline__ void issue_chunk(uint32_t ring, int wave, const TileSrc<NMAT, NBW>& t,
-                                            int c, bool has_a) {
+// Copies of chunk c into stage c mod kStages: the wavefront's MB A copies (row
+// groups of the tile's row blocks only), then B codes, then scale/bias -- the
+// same count for every wavefront.
+template <int MB, int NMAT, int NBW>
+__device__ __forceinline__ void issue_chunk(uint32_t ring, int wave, const TileSrc<NMAT, NBW>& t, int c) {
     const int st = c % kStages;
-    if (has_a) {
+    {
         const uint64_t ab = t.a_base + (uint64_t)c * (kKC * 2);
 #pragma unroll
-        for (int i = 0; i < kDmaPerWave; ++i)
-            dma16_to_lds(ab, t.a_off[i], ring + off_a(st) + (wave * kRowsPerWaveDma + i * 4) * kARow);
+        for (int i = 0; i < MB; ++i)
+            dma16_to_lds(ab, t.a_off[i], ring + off_a(st) + (wave + kWaves * i) * 4 * kARow);
     }
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
@@ -440,14 +440,14 @@ __device__ __forceinline__ void mma_chunk(ChunkOps<NMAT, NBW, MB>& o, const uint
 // offsets are compile-time constants.  Nothing is copied past the end of K.
 template <int NMAT, int NBW, int MB, int ST>
 __device__ __forceinline__ void kloop_step(uint8_t* s_stage, uint32_t ring, int wave, int lane,
-                                           const TileSrc<NMAT, NBW>& t, int c, int nch, bool has_a,
+                                           const TileSrc<NMAT, NBW>& t, int c, int nch,
                                            f32x4 (&acc)[MB][NMAT][NBW]) {
     wait_vmcnt<0>();
     __syncthreads();           // chunk c visible to all; the other stage is free
     ChunkOps<NMAT, NBW, MB> o;
     read_chunk_ops<NMAT, NBW, MB>(o, s_stage + off_a(ST), s_stage + off_b(ST, wave),
                                   s_stage + off_sb(ST, wave), lane);
-    if (c + 1 < nch) issue_chunk(ring, wave, t, c + 1, has_a);
+    if (c + 1 < nch) issue_chunk<MB>(ring, wave, t, c + 1);
     mma_chunk<NMAT, NBW, MB>(o, s_stage + off_a(ST), lane, acc);
 }
 
@@ -456,13 +456,12 @@ __device__ __forceinline__ void tile_kloop(uint8_t* s_stage, int wave, int lane,
                                            const TileSrc<NMAT, NBW>& t,
                                            f32x4 (&acc)[MB][NMAT][NBW]) {
     static_assert(kStages == 2, "the loop below alternates two stages");
-    const bool has_a = wave < MB;          // wave w copies rows [16 w, 16 w + 16)
     const int nch = t.K / kKC;
     const uint32_t ring = lds_addr(s_stage);
-    issue_chunk(ring, wave, t, 0, has_a);
+    issue_chunk<MB>(ring, wave, t, 0);
     for (int c = 0; c < nch; c += 2) {
-        kloop_step<NMAT, NBW, MB, 0>(s_stage, ring, wave, lane, t, c, nch, has_a, acc);
-        if (c + 1 < nch) kloop_step<NMAT, NBW, MB, 1>(s_stage, ring, wave, lane, t, c + 1, nch, has_a, acc);
+        kloop_step<NMAT, NBW, MB, 0>(s_stage, ring, wave, lane, t, c, nch, acc);
+        if (c + 1 < nch) kloop_step<NMAT, NBW, MB, 1>(s_stage, ring, wave, lane, t, c + 1, nch, acc);
     }
     __syncthreads();           // both stages free for the next tile
 }
