@@ -393,11 +393,14 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2, zipf=True):
     # weights once, the activations read once, the expert-sorted outputs once
     kbytes = {"grouped_gateup": (a_mean + 1) * 2 * gu + T * H * 2 + rows * I * 2,
               "grouped_down": (a_mean + 1) * dn + rows * I * 2 + rows * H * 2}
-    if zipf:
+    tkey = "prefill" if zipf else f"prefill{T}"
+    if T >= 2048:
+        # the MFMA target of the large prefill layer (the roofline's ridge is near
+        # 312 flop/B; this layer sits at about 250)
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(tflops, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_profiles(dom, "prefill"),
+                "traffic": traffic_from_profiles(dom, tkey),
                 "alg_flops_per_launch": flops[dom]}
     else:
         # at this size the layer's arithmetic intensity (about 64 flop/B) is far
@@ -405,7 +408,7 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2, zipf=True):
         gbs = kbytes[dom] / (kt[dom] * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profiles(dom, f"prefill{T}"),
+                "traffic": traffic_from_profiles(dom, tkey),
                 "alg_bytes_per_launch": int(kbytes[dom]),
                 "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
     return {
@@ -421,6 +424,30 @@ def run_prefill(args, ev, T=2048, L=8, steps=5, warmup=2, zipf=True):
         "roofline": dict(roof, avg_launch_us=round(kt[dom], 3),
                          kernel_us={n: round(v, 3) for n, v in kt.items()}),
     }
+
+
+def run_tiny(args, steps=200, warmup=20):
+    """The tiny block (T=16, hidden 256, 16 experts top-2 + shared, intermediate 128):
+    a correctness-sized workload, launch-bound, reported as block calls and tokens/s."""
+    import torch
+    from w4_dequant_grouped_amd import moe_w4 as B
+    from w4_dequant_grouped_amd import synth
+
+    wl = synth.WORKLOADS["tiny"]
+    sh = wl.shape
+    layer = synth.draw_layer(sh, wl.seed, device="cuda")
+    blk = B.Block(layer, sh.T, sh.top_k, sh.group)
+    x = synth.draw_x(sh.T, sh.H, wl.seed, device="cuda")
+
+    def step(i=0):
+        blk(x)
+
+    elapsed = time_steps(step, steps, warmup)
+    us = 1e6 * elapsed / steps
+    return {"workload": "tiny block: " + wl.note, "us_per_call": round(us, 2),
+            "tokens_per_s": round(sh.T / (us * 1e-6), 1),
+            "call_us_p10_p50_p90": [round(1e3 * v, 2) for v in step_percentiles(step, 50)],
+            "path": "moe_w4_block (grouped path at T=16: four router launches and three forward launches)"}
 
 
 def run_stack(args, ev):
@@ -890,6 +917,11 @@ def main():
         print("[bench] prefill T=512 uniform", file=sys.stderr, flush=True)
         line["prefill_T512"] = run_prefill(args, ev, T=512, zipf=False)
         torch.cuda.empty_cache()
+        print("[bench] prefill T=2048 uniform", file=sys.stderr, flush=True)
+        line["prefill_T2048_uniform"] = run_prefill(args, ev, T=2048, zipf=False)
+        torch.cuda.empty_cache()
+        print("[bench] tiny block", file=sys.stderr, flush=True)
+        line["tiny"] = run_tiny(args)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(T=args.tokens)
