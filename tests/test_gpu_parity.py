@@ -67,6 +67,14 @@ def test_grouped_multi_tile_ragged():
     full_check(S(T=300, H=512, I=256, E=32, top_k=4), 61, what="multi-tile")
 
 
+@pytest.mark.parametrize("T", [2, 5, 100, 300])
+def test_tile_counts_not_powers_of_two(T):
+    # H=768, I=384: six N-tiles per M-tile in both grouped GEMMs, 6 and 3 K-chunks, the
+    # tiled router's fallback logits kernel (H/8 = 96); T=300 gives every routed expert
+    # two M-tiles and the shared expert five (a block of four and a partial block)
+    full_check(S(T=T, H=768, I=384, E=12, top_k=3), 90 + T, what=f"H=768 I=384 T={T}")
+
+
 def test_one_expert_takes_every_token():
     shape = S(T=700, H=256, I=128, E=8, top_k=2)
     layer = synth.draw_layer(shape, 62)
