@@ -430,8 +430,10 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ p
 // from the others: no histogram, no atomics.  Thread tid owns a contiguous run
 // of the flattened (t, j) entries, read kGroupBatch x 4 at a time with every
 // load of a batch issued together (once to count, once more, from L2, to write
-// its part of the permutation).
-constexpr int kGroupThreads = 256;
+// its part of the permutation).  1024 threads keep each thread's run short (at
+// T = 16384 two batches per pass instead of eight), since the kernel is bound by
+// its dependent batches of loads.
+constexpr int kGroupThreads = 1024;
 constexpr int kGroupBatch = 16;          // int4 loads per thread issued together
 
 __device__ __forceinline__ void group_load(const int32_t* __restrict__ ids, int n, int q,
