@@ -224,7 +224,6 @@ def forward_grouped(x, layer, routing: Routing, group: int) -> np.ndarray:
     T, H = xf.shape
     k = routing.ids.shape[1]
     y = np.zeros((T, H), dtype=np.float64)
-    routed = _ExpertCache(layer.routed, group)
     E = routing.counts.shape[0]
     for e in range(E):
         lo, hi = int(routing.offsets[e]), int(routing.offsets[e + 1])
@@ -233,7 +232,9 @@ def forward_grouped(x, layer, routing: Routing, group: int) -> np.ndarray:
         flat = routing.perm[lo:hi]
         tok = flat // k
         slot = flat % k
-        Wg, Wu, Wd = routed(e)
+        # each expert is dequantised, used once and dropped, so a full-size
+        # layer never holds more than one expanded expert
+        Wg, Wu, Wd = _ExpertCache(layer.routed, group)(e)
         Y = swiglu_mlp(xf[tok], Wg, Wu, Wd)
         y[tok] += routing.weights[tok, slot][:, None] * Y
     if layer.shared is not None:

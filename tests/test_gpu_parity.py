@@ -154,16 +154,23 @@ def _sampled_full(shape, seed, layer, what, nrows=12):
 
 
 def test_prefill_512_full_size(full_layer):
+    """T=512 prefill at full size: routing bit-exact and the whole [512, 2048]
+    output against the oracle's grouped form (every expert dequantised once)."""
     wl = synth.WORKLOADS["prefill512"]
-    _sampled_full(wl.shape, wl.seed, full_layer, "prefill T=512")
+    full_check(wl.shape, wl.seed, layer=full_layer, what="prefill T=512 (whole output)")
 
 
 def test_prefill_2048_zipf_full_size():
+    """T=2048 prefill with the Zipf router bias at full size: routing bit-exact and
+    the whole [2048, 2048] output against the oracle; the routing has empty
+    experts and experts above four times the mean load, so the grouped GEMMs run
+    one-block tiles, full four-tile blocks of heavy experts and skipped segments."""
     wl = synth.WORKLOADS["prefill2048_zipf"]
     layer = synth.draw_layer(wl.shape, wl.seed)
-    ref_r = _sampled_full(wl.shape, wl.seed, layer, "prefill T=2048 zipf")
-    counts = ref_r.counts
+    _, x = make_inputs(wl.shape, wl.seed, layer)
+    counts = O.route(x, layer.router_w, layer.router_b, wl.shape.top_k).counts
     assert (counts == 0).any() and counts.max() > 4 * counts.mean()
+    full_check(wl.shape, wl.seed, layer=layer, what="prefill T=2048 zipf (whole output)")
 
 
 # --- properties -------------------------------------------------------------------------
@@ -326,8 +333,9 @@ def test_max_tokens_T65536_sampled(full_layer):
 def test_graph_replays_match_eager(full_layer, T):
     """Two block calls sharing one workspace, captured as a HIP graph: three
     replays, with eager calls on other inputs and a synchronisation between them,
-    each equal bit for bit to the eager calls on the same inputs; the control
-    block ends all zero."""
+    each equal bit for bit to the eager calls on the same inputs; the first
+    replay's routing is bit-exact and its output within tolerance against the
+    oracle; the control block ends all zero."""
     shape = S(T=T, H=2048, I=512, E=256, top_k=8)
     layer = full_layer.to("cuda")
     ws = B.alloc_workspace(B.make_dims(T, 2048, 512, 256, 8))
@@ -362,6 +370,14 @@ def test_graph_replays_match_eager(full_layer, T):
             assert torch.equal(blk.routing.ids, i), f"replay {rep}: ids"
             assert torch.equal(blk.routing.perm, p), f"replay {rep}: perm"
             assert torch.equal(blk.out, o), f"replay {rep}: output"
+        if rep == 0:
+            # the replayed layer against the oracle itself, not only the eager call
+            xa_cpu = xa.cpu()
+            ref_r = O.route(xa_cpu, full_layer.router_w, None, 8)
+            check_routing(blocks[1].routing, ref_r, f"graph replay T={T}")
+            rows = None if T <= 2 else sampled_rows(T, 6, 400 + T)
+            y = O.forward_dense(xa_cpu, full_layer, ref_r, 64, rows=rows)
+            check_output(blocks[1].out, y, rows=rows, what=f"graph replay T={T}")
         xin.copy_(xb)
         body()
         torch.cuda.synchronize()

@@ -165,6 +165,29 @@ def test_router_bias_changes_selection():
     assert r0.ids[0, 0] == 0
 
 
+def test_router_bias_enters_the_weights():
+    """Hand-worked top-2 of three experts with a router bias.  x is all ones over
+    64 hidden units and W_r's rows are constant, so the raw logits are exactly
+    (1, 2, 0); the bias (0, -1.5, 2) makes them (1, 0.5, 2).  The biased logits
+    choose experts 0 and 2 (the raw ones would choose 0 and 1), and the weights
+    are the softmax of the biased chosen logits: 1/(1+e) and e/(1+e).  A bias
+    that steered only the choice would give the softmax of the raw logits
+    (1, 0) instead: e/(1+e) and 1/(1+e), the two weights swapped."""
+    x = torch.ones((1, 64), dtype=torch.bfloat16)
+    wr = torch.zeros((3, 64), dtype=torch.float32)
+    wr[0] = 1.0 / 64
+    wr[1] = 2.0 / 64
+    br = torch.tensor([0.0, -1.5, 2.0])
+    r = O.route(x, wr, br, 2)
+    assert list(r.logits[0]) == [1.0, 0.5, 2.0]
+    assert list(r.ids[0]) == [0, 2]
+    e = math.e
+    np.testing.assert_allclose(r.weights[0], [1.0 / (1.0 + e), e / (1.0 + e)], rtol=1e-14, atol=0)
+    r0 = O.route(x, wr, None, 2)
+    assert list(r0.ids[0]) == [0, 1]
+    np.testing.assert_allclose(r0.weights[0], [1.0 / (1.0 + e), e / (1.0 + e)], rtol=1e-14, atol=0)
+
+
 # ---------------------------------------------------------------------------
 # grouping
 # ---------------------------------------------------------------------------
@@ -248,6 +271,22 @@ def test_grouped_equals_dense(bias):
     yg = O.forward_grouped(x, layer, r, 64)
     yd = O.forward_dense(x, layer, r, 64)
     assert O.relative_error(yg, yd) <= 1e-12
+
+
+def test_dense_rows_subset_equals_grouped_rows():
+    """forward_dense over a subset of tokens, in the caller's (unsorted) order and
+    with a shared dequantisation cache across two calls, returns exactly those rows
+    of the grouped form: the sampled full-size parity checks rest on this."""
+    shape, layer, x = _tiny_layer(14, T=23, H=128, I=64, E=8, k=3, bias=True)
+    r = O.route(x, layer.router_w, layer.router_b, 3)
+    yg = O.forward_grouped(x, layer, r, 64)
+    rows = [17, 0, 22, 5, 9]
+    cache = {}
+    yd = O.forward_dense(x, layer, r, 64, rows=rows, cache=cache)
+    assert yd.shape == (len(rows), shape.H)
+    assert O.relative_error(yd, yg[rows]) <= 1e-12
+    yd2 = O.forward_dense(x, layer, r, 64, rows=[3, 17], cache=cache)
+    assert O.relative_error(yd2, yg[[3, 17]]) <= 1e-12
 
 
 def test_zero_routed_weights_leave_only_shared():

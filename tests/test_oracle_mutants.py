@@ -4,7 +4,8 @@ Each case replaces one function of the CPU oracle, inside this test only, with a
 version holding one plausible mistake (nibble order, a zero-point subtraction, a
 wrong sign, ties to the higher index, a missing renormalisation, ids in logit
 order, a reversed segment order, a swapped gate/up, a dropped routing weight, a
-dropped shared expert, an ignored router bias) and runs the pins of
+dropped shared expert, an ignored router bias, a bias that steers only the
+choice, a sampled dense row taken from the wrong token) and runs the pins of
 test_oracle.py against it: at least one pin must fail.  The oracle itself is
 never modified.
 """
@@ -18,7 +19,7 @@ import test_oracle as P
 
 _orig = {name: getattr(O, name) for name in
          ("unpack_codes", "dequant", "select_experts", "group_by_expert", "silu", "swiglu_mlp",
-          "forward_grouped", "router_logits")}
+          "forward_grouped", "forward_dense", "router_logits", "route")}
 
 
 def _pins():
@@ -34,9 +35,11 @@ def _pins():
         P.test_topk_shift_invariance_and_unit_sum,
         P.test_topk_ties_go_to_lower_index,
         P.test_router_bias_changes_selection,
+        P.test_router_bias_enters_the_weights,
         P.test_grouping_matches_brute_force_counting_sort,
         P.test_single_expert_top1_no_shared_is_textbook_swiglu,
         P.test_block_matches_textbook_mixture,
+        P.test_dense_rows_subset_equals_grouped_rows,
         P.test_zero_routed_weights_leave_only_shared,
         P.test_zero_input_gives_zero_output,
         P.test_duplicate_rows_route_and_output_identically,
@@ -130,6 +133,28 @@ def _logits_without_bias(x, router_w, router_b=None):
     return _orig["router_logits"](x, router_w, None)
 
 
+def _route_bias_selects_only(x, router_w, router_b, top_k):
+    """The bias steers the choice, but the weights come from the raw logits."""
+    biased = _orig["route"](x, router_w, router_b, top_k)
+    if router_b is None:
+        return biased
+    raw = _orig["router_logits"](x, router_w, None)
+    w = np.empty_like(biased.weights)
+    for t in range(raw.shape[0]):
+        p = np.exp(raw[t] - raw[t].max())
+        w[t] = p[biased.ids[t]] / p[biased.ids[t]].sum()
+    return dataclasses.replace(biased, weights=w)
+
+
+def _dense_rows_misindexed(x, layer, routing, group, rows=None, cache=None):
+    """Output row i computed from token i instead of token rows[i]."""
+    if rows is None:
+        return _orig["forward_dense"](x, layer, routing, group, cache=cache)
+    rows = list(rows)
+    full = _orig["forward_dense"](x, layer, routing, group, cache=cache)
+    return full[list(range(len(rows)))]
+
+
 SLIPS = {
     "nibble order swapped": ("unpack_codes", _unpack_swapped_nibbles),
     "zero point 8 subtracted": ("dequant", _dequant_zero_point),
@@ -143,6 +168,8 @@ SLIPS = {
     "routing weight dropped": ("forward_grouped", _forward_without_weights),
     "shared expert dropped": ("forward_grouped", _forward_without_shared),
     "router bias ignored": ("router_logits", _logits_without_bias),
+    "router bias used for selection only": ("route", _route_bias_selects_only),
+    "dense rows misindexed": ("forward_dense", _dense_rows_misindexed),
 }
 
 
