@@ -30,8 +30,18 @@
  *  - Workspace: `workspace` must hold at least moe_w4_workspace_bytes(dims)
  *    bytes, be 256-byte aligned, and be ZERO-FILLED before the first call that
  *    uses it.  Its first MOE_W4_CONTROL_BYTES bytes are a control block (ticket
- *    and work-queue counters) that every call leaves zero again.  route() and forward() for the same dims may share one workspace;
- *    calls that may run concurrently need distinct workspaces.
+ *    and work-queue counters) that every call leaves zero again, except the
+ *    error counter at MOE_W4_CONTROL_ERRORS_OFFSET.  route() and forward() for
+ *    the same dims may share one workspace; calls that may run concurrently need
+ *    distinct workspaces.
+ *  - A dirty control block is detected, counted and repaired where it matters
+ *    most: the grouped GEMMs of forward() (T > MOE_W4_DECODE_MAX_T) count the
+ *    tiles they run; a call that ran fewer than its tile list holds, or met
+ *    arrival counts past its grid, adds one to the error counter, and its last
+ *    kernel clears every work-queue word, so the next call starts clean.  (The
+ *    output of the call that found the block dirty is unspecified.)  The
+ *    one-launch router (route() for T <= 8) counts an arrival ticket beyond its
+ *    grid as an error and clears the ticket.
  *
  * Weight layout (moe_w4_mat), for E matrices of shape [N][K]:
  *    codes   uint8  [E][N][K/2]   byte j of a row holds k = 2j in bits 0..3 and
@@ -75,6 +85,11 @@ extern "C" {
 
 /* Bytes at the start of the workspace used as the control block. */
 #define MOE_W4_CONTROL_BYTES 4096
+
+/* Byte offset, within the control block, of a uint32 counter of calls that found
+ * the control block dirty (not zero-filled, or shared with a concurrent call).
+ * The library only ever increments it; the caller may read or clear it. */
+#define MOE_W4_CONTROL_ERRORS_OFFSET 4092
 
 enum {
     MOE_W4_OK = 0,

@@ -151,7 +151,7 @@ def test_forward_rejects_bad_arguments(lib):
 def test_binding_constants_match_the_header():
     text = open(os.path.join(ROOT, "include", "moe_w4.h")).read()
     for name in ("MOE_W4_DECODE_MAX_T", "MOE_W4_GEMV_MAX_T", "MOE_W4_CONTROL_BYTES", "MOE_W4_FORWARD_GEMV",
-                 "MOE_W4_FORWARD_GROUPED"):
+                 "MOE_W4_FORWARD_GROUPED", "MOE_W4_CONTROL_ERRORS_OFFSET"):
         m = re.search(r"#define\s+%s\s+(\d+)u?\b" % name, text)
         assert m, name
         assert int(m.group(1)) == getattr(B, name), name

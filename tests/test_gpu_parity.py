@@ -225,6 +225,47 @@ def test_grouped_is_deterministic():
     assert torch.equal(o1, o2)
 
 
+# Control-block words of the grouped GEMMs (uint32 index): gate/up tile queues at
+# 32 + 32 q, down queues at 288 + 32 q, 64-bit exit words at 544 and 576; the
+# error counter is the block's last word (MOE_W4_CONTROL_ERRORS_OFFSET).
+_CTL_GATEUP_QUEUE0 = 32
+_CTL_ERRORS = B.MOE_W4_CONTROL_ERRORS_OFFSET // 4
+
+
+@pytest.mark.parametrize("dirt", ["one queue advanced", "garbage"])
+def test_dirty_control_block_is_counted_and_repaired(dirt):
+    """The workspace rule broken on purpose from the host: the control block is not
+    zero when a grouped forward starts, either one gate/up queue word already five
+    tiles in (those tiles would be skipped silently) or the whole block filled with
+    random words (a workspace that was never zero-filled).  The call adds to the
+    error counter and its last kernel clears the queue and exit words, so the next
+    call on the same workspace matches the oracle and adds no error."""
+    shape = S(T=300, H=512, I=256, E=32, top_k=4)
+    layer, x = make_inputs(shape, 700)
+    lg, xg = layer.to("cuda"), x.cuda()
+    blk = B.Block(lg, shape.T, shape.top_k)
+    ctl = blk.workspace[:B.MOE_W4_CONTROL_BYTES].view(torch.int32)
+    if dirt == "garbage":
+        g = torch.Generator().manual_seed(701)
+        ctl.copy_(torch.randint(-2 ** 31, 2 ** 31 - 1, (ctl.numel(),), generator=g, dtype=torch.int32))
+        ctl[_CTL_ERRORS] = 0
+    else:
+        ctl[_CTL_GATEUP_QUEUE0] = 5
+    blk(xg)
+    torch.cuda.synchronize()
+    errors = int(ctl[_CTL_ERRORS].item())
+    assert errors >= 1, f"{dirt}: dirty control block not counted"
+    if dirt != "garbage":
+        rest = torch.cat([ctl[:_CTL_ERRORS], ctl[_CTL_ERRORS + 1:]])
+        assert int(rest.abs().sum().item()) == 0, "control block not cleared"
+    r, out = blk.routing, blk(xg)
+    torch.cuda.synchronize()
+    assert int(ctl[_CTL_ERRORS].item()) == errors, "a clean call counted an error"
+    ref_r = O.route(x, layer.router_w, layer.router_b, shape.top_k)
+    check_routing(r, ref_r, f"after {dirt}")
+    check_output(out, O.forward_grouped(x, layer, ref_r, shape.group), what=f"after {dirt}")
+
+
 def test_token_permutation_invariance_gpu():
     shape = S(T=96, H=512, I=256, E=32, top_k=4)
     layer, x = make_inputs(shape, 304)

@@ -169,22 +169,23 @@ __device__ __forceinline__ int queue_len(int q, int n_mt, int NT) {
     return queue_start(q + 1, n_mt, NT) - queue_start(q, n_mt, NT);
 }
 
-__device__ __forceinline__ uint32_t queue_take(uint32_t* ctl, int q) {
-    return __hip_atomic_fetch_add(ctl + kCtlQueue + q * kCtlQueueStride, 1u, __ATOMIC_RELAXED,
+// `qb` is the first queue word of a kernel's set in the control block.
+__device__ __forceinline__ uint32_t queue_take(uint32_t* qb, int q) {
+    return __hip_atomic_fetch_add(qb + q * kCtlQueueStride, 1u, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Next tile index for this workgroup, or -1 when every queue is empty.  `q`
 // is the queue to try first and, on success, the queue the tile came from;
 // `empty` remembers the queues already found empty.
-__device__ __forceinline__ int grab_tile(uint32_t* ctl, int n_mt, int NT, int& q, uint32_t& empty) {
+__device__ __forceinline__ int grab_tile(uint32_t* qb, int n_mt, int NT, int& q, uint32_t& empty) {
     for (int d = 0; d < 8; ++d) {
         const int qq = (q + d) & 7;
         if (empty & (1u << qq)) continue;
         const int lim = queue_len(qq, n_mt, NT);
         if (lim > 0) {
-            const uint32_t j = queue_take(ctl, qq);
-            if ((int)j < lim) {
+            const uint32_t j = queue_take(qb, qq);
+            if (j < (uint32_t)lim) {           // unsigned: any stale value past the queue is empty
                 q = qq;
                 return queue_start(qq, n_mt, NT) + (int)j;
             }
@@ -196,35 +197,42 @@ __device__ __forceinline__ int grab_tile(uint32_t* ctl, int n_mt, int NT, int& q
 
 // Tile scheduling state of a workgroup (meaningful in thread 0 only).  While a
 // tile is processed, the next entry of the current queue is already being
-// taken; its result is needed only when the tile is done.
+// taken; its result is needed only when the tile is done.  `ran` counts the
+// tiles the workgroup ran.
 struct TileQueue {
     int q;               // current queue
     uint32_t empty;      // queues found empty
     uint32_t taken;      // entry taken from queue q for the next tile
     bool pending;
-    __device__ __forceinline__ void prefetch(uint32_t* ctl) {
+    uint32_t ran;
+    __device__ __forceinline__ void prefetch(uint32_t* qb) {
         pending = !(empty & (1u << q));
-        if (pending) taken = queue_take(ctl, q);
+        if (pending) taken = queue_take(qb, q);
     }
-    __device__ __forceinline__ int next(uint32_t* ctl, int n_mt, int NT) {
-        if (pending && (int)taken < queue_len(q, n_mt, NT)) return queue_start(q, n_mt, NT) + (int)taken;
+    __device__ __forceinline__ int next(uint32_t* qb, int n_mt, int NT) {
+        if (pending && taken < (uint32_t)queue_len(q, n_mt, NT)) return queue_start(q, n_mt, NT) + (int)taken;
         if (pending) empty |= 1u << q;
-        return grab_tile(ctl, n_mt, NT, q, empty);
+        return grab_tile(qb, n_mt, NT, q, empty);
     }
 };
 
-// The last workgroup to finish clears the queues for the next launch.
-__device__ __forceinline__ void release_queues(uint32_t* ctl) {
+// Exit accounting of a grouped GEMM: one 64-bit word holds the workgroups that
+// have left (high half) and the tiles they ran (low half), updated with one
+// atomic per workgroup.  In a call that found its queue words zero, arrival
+// counts stay below the grid size and the last workgroup out sees every tile of
+// the list run; anything else means the control block was dirty (not
+// zero-filled, or shared with a concurrent call), which is counted in the error
+// word.  The queues and this word are cleared by k_finalize, the call's last
+// kernel, so the next call starts clean either way.
+__device__ __forceinline__ void report_exit(uint32_t* ctl, int exit_word, uint32_t ran, uint32_t tiles) {
     if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(ctl + kCtlExit, 1u, __ATOMIC_RELAXED,
+        uint64_t* w = reinterpret_cast<uint64_t*>(ctl + exit_word);
+        const uint64_t prev = __hip_atomic_fetch_add(w, (1ull << 32) | ran, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == gridDim.x - 1) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                __hip_atomic_store(ctl + kCtlQueue + q * kCtlQueueStride, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(ctl + kCtlExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        const uint32_t arrived = (uint32_t)(prev >> 32);
+        const bool dirty = arrived >= gridDim.x ||
+                           (arrived == gridDim.x - 1 && (uint32_t)prev + ran != tiles);
+        if (dirty) __hip_atomic_fetch_add(ctl + kCtlErrors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -569,9 +577,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
     const int NT = I / BN;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = (int)uniform32(threadIdx.x / kWave);
-    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false};    // thread 0's scheduling state
+    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false, 0u};    // thread 0's scheduling state
+    uint32_t* const qb = ctl + kCtlQueueGateUp;
 
-    if (threadIdx.x == 0) s_next = grab_tile(ctl, n_mt, NT, tq.q, tq.empty);
+    if (threadIdx.x == 0) s_next = grab_tile(qb, n_mt, NT, tq.q, tq.empty);
     __syncthreads();
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
         int seg, mt, nt;
@@ -582,7 +591,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
         for (int r = threadIdx.x; r < c.rows; r += kThreads)
             s_tok[r] = c.shared ? (c.m0 + r) : min(max(perm[c.hbase + c.m0 + r], 0), T * k - 1) / k;
         __syncthreads();
-        if (threadIdx.x == 0) tq.prefetch(ctl);
+        if (threadIdx.x == 0) { tq.prefetch(qb); ++tq.ran; }
         const int nbase = nt * BN + wave * 16 * NBW;
 
         TileSrc<2, NBW> ts;
@@ -603,10 +612,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
             case 4: gateup_tile<NBW, 4>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
             default: gateup_tile<NBW, kMB>(s_stage, I, wave, lane, ts, c.rows, rowbase, nbase, h); break;
         }
-        if (threadIdx.x == 0) s_next = tq.next(ctl, n_mt, NT);
+        if (threadIdx.x == 0) s_next = tq.next(qb, n_mt, NT);
         __syncthreads();
     }
-    release_queues(ctl);
+    report_exit(ctl, kCtlExitGateUp, tq.ran, (uint32_t)(n_mt * NT));
 }
 
 // ---------------------------------------------------------------------------
@@ -631,9 +640,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
     const int NT = H / BN;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = (int)uniform32(threadIdx.x / kWave);
-    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false};    // thread 0's scheduling state
+    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false, 0u};    // thread 0's scheduling state
+    uint32_t* const qb = ctl + kCtlQueueDown;
 
-    if (threadIdx.x == 0) s_next = grab_tile(ctl, n_mt, NT, tq.q, tq.empty);
+    if (threadIdx.x == 0) s_next = grab_tile(qb, n_mt, NT, tq.q, tq.empty);
     __syncthreads();
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
         int seg, mt, nt;
@@ -650,7 +660,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
             }
         }
         __syncthreads();
-        if (threadIdx.x == 0) tq.prefetch(ctl);
+        if (threadIdx.x == 0) { tq.prefetch(qb); ++tq.ran; }
         const int nbase = nt * BN + wave * 16 * NBW;
         TileSrc<1, NBW> ts;
         ts.a_base = uniform64((uint64_t)(h + (size_t)(c.hbase + c.m0) * I));
@@ -669,10 +679,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
             case 4: down_tile<NBW, 4>(s_stage, H, wave, lane, ts, c.rows, nbase, s_dst, s_w, y); break;
             default: down_tile<NBW, kMB>(s_stage, H, wave, lane, ts, c.rows, nbase, s_dst, s_w, y); break;
         }
-        if (threadIdx.x == 0) s_next = tq.next(ctl, n_mt, NT);
+        if (threadIdx.x == 0) s_next = tq.next(qb, n_mt, NT);
         __syncthreads();
     }
-    release_queues(ctl);
+    report_exit(ctl, kCtlExitDown, tq.ran, (uint32_t)(n_mt * NT));
 }
 
 __device__ __forceinline__ void add_bf16x8(float (&acc)[8], const u32x4 v) {
@@ -682,9 +692,18 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], const u32x4 v) {
 
 // out[t][n] = bf16(sum_j y[t*k + j][n] + y[T*k + t][n]), eight columns per thread:
 // the k slot rows of a token are adjacent, so every read is a 16-byte load.
+// Workgroup 0 also clears both GEMMs' queue and exit words: both kernels have
+// finished, so the next call finds them zero whatever state this one found.
 __global__ __launch_bounds__(256) void k_finalize(const uint16_t* __restrict__ y,
                                                   uint16_t* __restrict__ out, int T, int H, int k,
-                                                  int has_shared) {
+                                                  int has_shared, uint32_t* ctl) {
+    if (blockIdx.x == 0 && threadIdx.x < 20) {
+        const int i = threadIdx.x;
+        const int word = i < 8    ? kCtlQueueGateUp + i * kCtlQueueStride
+                         : i < 16 ? kCtlQueueDown + (i - 8) * kCtlQueueStride
+                                  : (i < 18 ? kCtlExitGateUp + (i - 16) : kCtlExitDown + (i - 18));
+        __hip_atomic_store(ctl + word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     const long n8 = (long)T * H / 8;
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
         const long t = i / (H / 8);
@@ -744,7 +763,7 @@ hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTi
     const long nblk = ((long)a.T * a.H / 8 + 255) / 256;
     tm.before();
     tm.launch(k_finalize, dim3((unsigned)(nblk < 4096 ? nblk : 4096)), dim3(256), 0, st,
-                       a.ws_y, a.out, a.T, a.H, a.k, a.has_shared);
+                       a.ws_y, a.out, a.T, a.H, a.k, a.has_shared, a.ctl);
     tm.after();
     return hipGetLastError();
 }

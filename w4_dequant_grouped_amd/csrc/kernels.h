@@ -58,11 +58,17 @@ struct ForwardArgs {
     uint32_t* ctl;           // workspace control block (zero between calls)
 };
 
-// Control block words (the block is kCtlWords words, zero between calls).
+// Control block words (MOE_W4_CONTROL_BYTES / 4 of them; zero between calls
+// except the error counter).
 constexpr int kCtlTicket = 0;            // one-launch router: arrival ticket
-constexpr int kCtlQueue = 32;            // grouped GEMMs: 8 per-XCD tile queues, 128 B apart
-constexpr int kCtlQueueStride = 32;
-constexpr int kCtlExit = kCtlQueue + 8 * kCtlQueueStride;   // grouped GEMMs: exit ticket
+constexpr int kCtlQueueStride = 32;      // 128 B between the queue words of a set
+constexpr int kCtlQueueGateUp = 32;      // gate/up GEMM: 8 per-XCD tile queues
+constexpr int kCtlQueueDown = kCtlQueueGateUp + 8 * kCtlQueueStride;   // down GEMM: 8 more
+constexpr int kCtlExitGateUp = kCtlQueueDown + 8 * kCtlQueueStride;    // 64-bit: arrivals, tiles done
+constexpr int kCtlExitDown = kCtlExitGateUp + 32;                      // 64-bit, likewise
+constexpr int kCtlErrors = 1023;         // sticky count of control blocks found dirty
+static_assert(kCtlExitGateUp % 2 == 0 && kCtlExitDown % 2 == 0, "64-bit exit words");
+static_assert(kCtlExitDown + 2 <= kCtlErrors, "control block layout");
 
 struct DecodeBlockArgs {     // route + forward of decode rows (T <= kDecodeMaxT)
     const uint16_t* x;

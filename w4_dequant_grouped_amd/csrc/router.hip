@@ -96,6 +96,12 @@ __global__ __launch_bounds__(kSmallRouteThreads) void k_route_small(
         const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == gridDim.x - 1);
+        if (prev >= gridDim.x) {
+            // a ticket past the grid: the control block was dirty when this call
+            // began; count it and clear the ticket for the next call
+            __hip_atomic_fetch_add(ticket + kCtlErrors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();
     if (!s_last) return;

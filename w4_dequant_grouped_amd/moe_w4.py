@@ -22,6 +22,7 @@ MOE_W4_GEMV_MAX_T = 8
 MOE_W4_FORWARD_GEMV = 1
 MOE_W4_FORWARD_GROUPED = 2
 MOE_W4_CONTROL_BYTES = 4096
+MOE_W4_CONTROL_ERRORS_OFFSET = 4092
 
 
 class moe_w4_dims(ctypes.Structure):
