@@ -781,30 +781,71 @@ def attn_cpu_baseline(budget_s=15.0):
                                         f"oracle, {el:.1f} s"}
 
 
-def cpu_baseline(T=1, max_calls=24, budget_s=20.0):
-    """The oracle as it stands, on this host's cores, on a bounded sample."""
-    import numpy as np  # noqa: F401
+def _thread_counts():
+    """Threads of the host's BLAS and OpenMP pools (threadpoolctl), and the CPU count."""
     from threadpoolctl import threadpool_info
+    info = threadpool_info()
+    blas = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] + [1])
+    omp = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "openmp"] + [0])
+    return blas, omp, os.cpu_count()
 
+
+def cpu_baseline(shape=None, seed=1000, max_calls=24, budget_s=20.0, what="decode"):
+    """The oracle as it stands, on this host's cores, on a bounded sample: whole
+    layer-calls (route + grouped forward) of one seeded layer of ``shape`` with
+    fresh activations per call, until ``max_calls`` calls or ``budget_s`` seconds.
+    The oracle's matrix products run on the BLAS pool; its dequantisation and
+    routing loops run on one thread."""
     from oracle import moe_w4_oracle as O
     from w4_dequant_grouped_amd import synth
 
-    shape = synth.BlockShape(T=T, H=2048, I=512, E=256, top_k=8)
-    layer = synth.draw_layer(shape, 1000, device="cpu")
+    if shape is None:
+        shape = synth.BlockShape(T=1, H=2048, I=512, E=256, top_k=8)
+    layer = synth.draw_layer(shape, seed, device="cpu")
     calls = 0
     t0 = time.perf_counter()
-    while calls < max_calls and time.perf_counter() - t0 < budget_s:
-        x = synth.draw_x(T, shape.H, 500 + calls)
+    while calls < max_calls and (calls == 0 or time.perf_counter() - t0 < budget_s):
+        x = synth.draw_x(shape.T, shape.H, 500 + calls)
         r = O.route(x, layer.router_w, layer.router_b, shape.top_k)
         O.forward_grouped(x, layer, r, shape.group)
         calls += 1
     el = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(calls * T / el, 3), "unit": "layer-tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{calls} decode layer-calls (T={T}) of one seeded full-size layer, "
-                      f"float64 NumPy oracle (route + grouped forward), {el:.1f} s",
-            "host_cpus": os.cpu_count()}
+    blas, omp, ncpu = _thread_counts()
+    unit = "layer-tokens/s" if shape.T == 1 else "tokens/s"
+    return {"value": round(calls * shape.T / el, 3), "unit": unit, "cores": blas,
+            "blas_threads": blas, "openmp_threads": omp, "host_cpus": ncpu, "kind": "oracle",
+            "sample": f"{calls} whole {what} layer-call(s) ({synth.describe(shape)}) of one seeded "
+                      f"layer, float64 NumPy oracle (route + grouped forward), {el:.1f} s; matrix "
+                      f"products on {blas} BLAS threads, dequantisation and routing on one"}
+
+
+def stack_cpu_baseline(nrows=16, budget_s=20.0):
+    """The oracle on a fixed sample of the 40-layer stack workload: nrows token rows
+    of one T=16384 layer (Zipf-biased router), routed over all 16384 tokens and then
+    run through the per-token dense form, one row at a time."""
+    from oracle import moe_w4_oracle as O
+    from w4_dequant_grouped_amd import synth
+
+    wl = synth.WORKLOADS["stack40"]
+    layer = synth.draw_layer(wl.shape, 4000, device="cpu")
+    x = synth.draw_x(wl.shape.T, wl.shape.H, 4)
+    t0 = time.perf_counter()
+    r = O.route(x, layer.router_w, layer.router_b, wl.shape.top_k)
+    t_route = time.perf_counter() - t0
+    rows, cache, done = list(range(0, wl.shape.T, wl.shape.T // nrows))[:nrows], {}, 0
+    t1 = time.perf_counter()
+    for t in rows:
+        O.forward_dense(x, layer, r, wl.shape.group, rows=[t], cache=cache)
+        done += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    el = time.perf_counter() - t1
+    blas, omp, ncpu = _thread_counts()
+    return {"value": round(done / el, 3), "unit": "token rows/s (sampled, per layer)", "cores": blas,
+            "blas_threads": blas, "openmp_threads": omp, "host_cpus": ncpu, "kind": "oracle",
+            "sample": f"routing of all {wl.shape.T} tokens of one seeded stack layer ({t_route:.1f} s), then "
+                      f"{done} evenly spaced token rows through the per-token dense form ({el:.1f} s), "
+                      f"float64 NumPy oracle; sampled, not a whole layer-call"}
 
 
 def main():
@@ -897,6 +938,8 @@ def main():
         print("[bench] stack: 40 layers", file=sys.stderr, flush=True)
         line = {"stack": run_stack(args, ev), "n_gpus": 1, "dtype": "bf16",
                 "data": "synthetic (seeded W4 layers and activations)", "source_hash": source_hash()}
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = stack_cpu_baseline()
         print(json.dumps(line), flush=True)
         return
 
@@ -923,8 +966,22 @@ def main():
         print("[bench] tiny block", file=sys.stderr, flush=True)
         line["tiny"] = run_tiny(args)
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(T=args.tokens)
+        from w4_dequant_grouped_amd import synth
+        print("[bench] cpu baseline (oracle): decode", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(synth.BlockShape(T=args.tokens, H=2048, I=512, E=256, top_k=8),
+                                            what="decode")
+        if "prefill" in line:
+            print("[bench] cpu baseline (oracle): prefill", file=sys.stderr, flush=True)
+            line["prefill"]["cpu_baseline"] = cpu_baseline(
+                synth.WORKLOADS["prefill2048_zipf"].shape, seed=3000, max_calls=1, what="prefill T=2048 Zipf")
+            line["prefill_T512"]["cpu_baseline"] = cpu_baseline(
+                synth.WORKLOADS["prefill512"].shape, seed=3000, max_calls=1, what="prefill T=512")
+            line["prefill_T2048_uniform"]["cpu_baseline"] = {
+                "same_as": "prefill.cpu_baseline",
+                "note": "the oracle's cost does not depend on the routing skew; not timed twice"}
+            wl = synth.WORKLOADS["tiny"]
+            line["tiny"]["cpu_baseline"] = cpu_baseline(wl.shape, seed=wl.seed, max_calls=200, budget_s=5.0,
+                                                        what="tiny")
     print("[bench] measured ceilings", file=sys.stderr, flush=True)
     ceil = measure_ceilings()
     line["ceilings"] = ceil
