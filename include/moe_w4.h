@@ -100,8 +100,13 @@ enum {
     MOE_W4_ERR_ALIGN = -5,       /* a pointer is not aligned as documented          */
     MOE_W4_ERR_WORKSPACE = -6,   /* workspace smaller than moe_w4_workspace_bytes() */
     MOE_W4_ERR_LAUNCH = -7,      /* a HIP launch failed (see moe_w4_last_error())   */
-    MOE_W4_ERR_FLAGS = -8        /* bad dims->flags (see MOE_W4_FORWARD_GEMV)        */
+    MOE_W4_ERR_FLAGS = -8,       /* bad dims->flags (see MOE_W4_FORWARD_GEMV)        */
+    MOE_W4_ERR_SCRATCH = -9      /* shape too large for moe_w4_block_noalloc()      */
 };
+
+/* Size of the device scratch that moe_w4_block_noalloc() uses in place of a
+ * workspace (32 MiB per GPU). */
+#define MOE_W4_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Sizes of one block call.  `flags`: 0, or one forward-path bit (above). */
 typedef struct moe_w4_dims {
@@ -240,6 +245,32 @@ int moe_w4_block_timed(const moe_w4_dims* dims, const void* x,
                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
                        void* out, void* workspace, size_t workspace_bytes, void* hip_stream,
                        void** events, int capacity, int* n_kernels);
+
+/*
+ * moe_w4_block() for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, outputs and errors as moe_w4_block() without `workspace` and
+ * `workspace_bytes`: the kernels use a device scratch array of
+ * MOE_W4_NOALLOC_SCRATCH_BYTES bytes that the library holds, one copy per GPU,
+ * until the process ends.  The caller still passes every input and output.
+ *  - Shapes whose moe_w4_workspace_bytes() exceeds MOE_W4_NOALLOC_SCRATCH_BYTES
+ *    return MOE_W4_ERR_SCRATCH and enqueue nothing (at H=2048, I=512, E=256,
+ *    top-8 with a shared expert that is T <= 560).
+ *  - The call allocates nothing: no hipMalloc, no hipFree, no allocating library
+ *    routine.  The first call with a given device current looks up that device's
+ *    scratch address (hipGetSymbolAddress) and keeps it.
+ *  - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *    call's contents; its control block starts zero-filled and every call leaves
+ *    it zero.  Calls that may overlap on one GPU (other streams, other host
+ *    threads) race on the scratch: serialise them, or use moe_w4_block() with
+ *    distinct workspaces.
+ */
+int moe_w4_block_noalloc(const moe_w4_dims* dims, const void* x,
+                         const float* router_w, const float* router_b,
+                         const moe_w4_weights* routed, const moe_w4_weights* shared,
+                         int32_t* topk_ids, float* topk_w,
+                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                         void* out, void* hip_stream);
 
 /* Static description of a status code. */
 const char* moe_w4_status_string(int status);

@@ -15,8 +15,8 @@ HEADER = os.path.join(ROOT, "include", "moe_w4.h")
 HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
            if h.endswith(".h")]
 
-OK, ERR_NULL, ERR_DIMS, ERR_TOPK, ERR_GROUP, ERR_ALIGN, ERR_WS, ERR_LAUNCH, ERR_FLAGS = \
-    0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, ERR_NULL, ERR_DIMS, ERR_TOPK, ERR_GROUP, ERR_ALIGN, ERR_WS, ERR_LAUNCH, ERR_FLAGS, ERR_SCRATCH = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 FAKE = 0x7F0000000000          # aligned, never dereferenced: every call below fails validation
 
@@ -47,7 +47,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, ERR_NULL, ERR_DIMS, ERR_TOPK, ERR_GROUP, ERR_ALIGN, ERR_WS, ERR_LAUNCH, ERR_FLAGS):
+    for code in (OK, ERR_NULL, ERR_DIMS, ERR_TOPK, ERR_GROUP, ERR_ALIGN, ERR_WS, ERR_LAUNCH, ERR_FLAGS,
+                 ERR_SCRATCH):
         s = B.moe_w4_status_string(code)
         assert s and s != "unknown status"
     assert B.moe_w4_status_string(12345) == "unknown status"
@@ -148,6 +149,38 @@ def test_forward_rejects_bad_arguments(lib):
     assert _forward(lib, d, ws_bytes=B.moe_w4_workspace_bytes(d) - 256) == ERR_WS
 
 
+def _noalloc(lib, dims, x=FAKE, wr=FAKE, br=None, routed=None, shared=None, ids=FAKE, w=FAKE, cnt=FAKE,
+             off=FAKE, perm=FAKE, out=FAKE + 4096):
+    routed = routed if routed is not None else _weights()
+    return lib.moe_w4_block_noalloc(ctypes.byref(dims) if dims is not None else None, x, wr, br,
+                                    ctypes.byref(routed), None if shared is None else ctypes.byref(shared),
+                                    ids, w, cnt, off, perm, out, None)
+
+
+def test_noalloc_rejects_bad_arguments_before_touching_the_gpu(lib):
+    """Every rejection below happens on the host, before the device scratch is
+    looked up; shapes whose workspace would not fit the scratch get their own
+    status."""
+    assert _noalloc(lib, None) == ERR_NULL
+    assert _noalloc(lib, _dims(T=0)) == OK
+    assert _noalloc(lib, _dims(flags=3)) == ERR_FLAGS
+    assert _noalloc(lib, _dims(top_k=0)) == ERR_TOPK
+    assert _noalloc(lib, _dims(group=32)) == ERR_GROUP
+    full = dict(H=2048, I=512, E=256, top_k=8)
+    assert _noalloc(lib, _dims(T=2048, **full)) == ERR_SCRATCH
+    assert _noalloc(lib, _dims(), x=None) == ERR_NULL
+    assert _noalloc(lib, _dims(), out=None) == ERR_NULL
+    assert _noalloc(lib, _dims(), routed=_weights(codes=None)) == ERR_NULL
+    assert _noalloc(lib, _dims(), x=FAKE + 2) == ERR_ALIGN
+    assert _noalloc(lib, _dims(), routed=_weights(codes=FAKE + 8)) == ERR_ALIGN
+    assert _noalloc(lib, _dims(), perm=FAKE + 1) == ERR_ALIGN
+    # the largest accepted T at the full-size shape is the one the header states
+    fits = [T for T in (512, 560, 561, 580, 600, 1024)
+            if B.moe_w4_workspace_bytes(_dims(T=T, **full)) <= B.MOE_W4_NOALLOC_SCRATCH_BYTES]
+    assert max(fits) == 560
+    assert _noalloc(lib, _dims(T=561, **full)) == ERR_SCRATCH
+
+
 def test_binding_constants_match_the_header():
     text = open(os.path.join(ROOT, "include", "moe_w4.h")).read()
     for name in ("MOE_W4_DECODE_MAX_T", "MOE_W4_GEMV_MAX_T", "MOE_W4_CONTROL_BYTES", "MOE_W4_FORWARD_GEMV",
@@ -155,6 +188,8 @@ def test_binding_constants_match_the_header():
         m = re.search(r"#define\s+%s\s+(\d+)u?\b" % name, text)
         assert m, name
         assert int(m.group(1)) == getattr(B, name), name
+    m = re.search(r"#define\s+MOE_W4_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.MOE_W4_NOALLOC_SCRATCH_BYTES
 
 
 # --- decode attention (include/moe_w4_attn.h) ------------------------------------

@@ -8,9 +8,18 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
+
+// Device scratch of moe_w4_block_noalloc(): the workspace of callers that cannot
+// allocate.  Every GPU the library runs on holds its own copy until the process
+// ends; static storage starts zero-filled, so its control block starts zero.
+// Host code never passes this name to a kernel (on the host it stands for a
+// host-side shadow, not the device copy): it uses the per-device address that
+// hipGetSymbolAddress returns.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[MOE_W4_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -315,6 +324,69 @@ int moe_w4_block(const moe_w4_dims* dims, const void* x, const float* router_w,
 }
 
 // ---------------------------------------------------------------------------
+// moe_w4_block without a caller workspace: the kernels run on the device copy of
+// `scratch` of the current device.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call made with that device current and kept for later calls.
+int device_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return launch_status(err);
+    if (dev < 0 || dev >= kMaxDevices) {
+        g_last_error = "device ordinal beyond the no-allocation entry point's table";
+        return MOE_W4_ERR_LAUNCH;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return launch_status(err);
+        if (!p) {
+            g_last_error = "hipGetSymbolAddress returned a null scratch address";
+            return MOE_W4_ERR_LAUNCH;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MOE_W4_OK;
+}
+
+}  // namespace
+
+int moe_w4_block_noalloc(const moe_w4_dims* dims, const void* x, const float* router_w,
+                         const float* router_b, const moe_w4_weights* routed,
+                         const moe_w4_weights* shared, int32_t* topk_ids, float* topk_w,
+                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                         void* out, void* hip_stream) {
+    int st;
+    if (!dims_ok(dims, &st)) return st;
+    if (dims->T == 0) return MOE_W4_OK;
+    const size_t need = layout(dims).total;
+    if (need > (size_t)MOE_W4_NOALLOC_SCRATCH_BYTES) return MOE_W4_ERR_SCRATCH;
+    // every argument is checked before the scratch address is looked up, with a
+    // stand-in workspace pointer of the required alignment
+    void* const stand_in = reinterpret_cast<void*>(kAlign);
+    st = check_route(dims, x, router_w, router_b, topk_ids, topk_w, expert_counts, expert_offsets,
+                     perm, stand_in, need);
+    if (st != MOE_W4_OK) return st;
+    st = check_forward(dims, x, routed, shared, topk_w, expert_offsets, perm, out, stand_in, need);
+    if (st != MOE_W4_OK) return st;
+    void* ws = nullptr;
+    st = device_scratch(&ws);
+    if (st != MOE_W4_OK) return st;
+    return moe_w4_block_timed(dims, x, router_w, router_b, routed, shared, topk_ids, topk_w,
+                              expert_counts, expert_offsets, perm, out, ws,
+                              (size_t)MOE_W4_NOALLOC_SCRATCH_BYTES, hip_stream, nullptr, 0, nullptr);
+}
+
+// ---------------------------------------------------------------------------
 // decode attention
 // ---------------------------------------------------------------------------
 namespace {
@@ -458,6 +530,9 @@ const char* moe_w4_status_string(int status) {
         case MOE_W4_ERR_WORKSPACE: return "workspace smaller than moe_w4_workspace_bytes()";
         case MOE_W4_ERR_LAUNCH: return "a HIP kernel launch failed";
         case MOE_W4_ERR_FLAGS: return "dims->flags: unknown bits, both path bits, or the GEMV path with T > 8";
+        case MOE_W4_ERR_SCRATCH:
+            return "the shape needs more workspace than moe_w4_block_noalloc's device scratch "
+                   "(MOE_W4_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

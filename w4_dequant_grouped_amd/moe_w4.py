@@ -23,6 +23,7 @@ MOE_W4_FORWARD_GEMV = 1
 MOE_W4_FORWARD_GROUPED = 2
 MOE_W4_CONTROL_BYTES = 4096
 MOE_W4_CONTROL_ERRORS_OFFSET = 4092
+MOE_W4_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class moe_w4_dims(ctypes.Structure):
@@ -56,7 +57,7 @@ class moe_w4_gdn_dims(ctypes.Structure):
 MOE_W4_GDN_MAX_T = 1 << 20
 
 EXPORTS = ("moe_w4_workspace_bytes", "moe_w4_route", "moe_w4_forward", "moe_w4_block",
-           "moe_w4_route_timed", "moe_w4_forward_timed", "moe_w4_block_timed",
+           "moe_w4_route_timed", "moe_w4_forward_timed", "moe_w4_block_timed", "moe_w4_block_noalloc",
            "moe_w4_status_string", "moe_w4_last_error",
            "moe_w4_attn_workspace_bytes", "moe_w4_attn_decode", "moe_w4_attn_decode_timed",
            "moe_w4_gdn_scan", "moe_w4_gdn_scan_timed")
@@ -88,6 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_w4_block.restype = ctypes.c_int
     lib.moe_w4_block_timed.argtypes = lib.moe_w4_block.argtypes + [P, ctypes.c_int, P]
     lib.moe_w4_block_timed.restype = ctypes.c_int
+    lib.moe_w4_block_noalloc.argtypes = [ctypes.POINTER(moe_w4_dims), P, P, P, W, W, P, P, P, P, P, P, P]
+    lib.moe_w4_block_noalloc.restype = ctypes.c_int
     lib.moe_w4_route_timed.argtypes = lib.moe_w4_route.argtypes + [P, ctypes.c_int, P]
     lib.moe_w4_route_timed.restype = ctypes.c_int
     lib.moe_w4_forward_timed.argtypes = lib.moe_w4_forward.argtypes + [P, ctypes.c_int, P]
@@ -267,6 +270,26 @@ def moe_w4_block(dims: moe_w4_dims, x: torch.Tensor, router_w: torch.Tensor,
     n = ctypes.c_int(0)
     _check(lib.moe_w4_block_timed(*args, arr, cap, ctypes.byref(n)), "moe_w4_block_timed")
     return n.value
+
+
+def moe_w4_block_noalloc(dims: moe_w4_dims, x: torch.Tensor, router_w: torch.Tensor,
+                         router_b: Optional[torch.Tensor], routed_struct: moe_w4_weights,
+                         shared_struct: Optional[moe_w4_weights], routing: Routing,
+                         out: torch.Tensor) -> None:
+    """Route and forward in one library call on the library's own device scratch
+    (no workspace argument; the call allocates nothing)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(router_w, torch.float32, "router_w")
+    if router_b is not None:
+        _dev(router_b, torch.float32, "router_b")
+    _check_routing(routing)
+    _dev(out, torch.bfloat16, "out")
+    st = load_library().moe_w4_block_noalloc(
+        ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(router_b), ctypes.byref(routed_struct),
+        None if shared_struct is None else ctypes.byref(shared_struct), _ptr(routing.ids),
+        _ptr(routing.weights), _ptr(routing.counts), _ptr(routing.offsets), _ptr(routing.perm),
+        _ptr(out), _stream())
+    _check(st, "moe_w4_block_noalloc")
 
 
 def _events_arg(events):
