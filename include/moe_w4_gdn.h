@@ -70,6 +70,37 @@ int moe_w4_gdn_scan_timed(const moe_w4_gdn_dims* dims, const void* q, const void
                           void* out, void* hip_stream, void** events, int capacity,
                           int* n_kernels);
 
+/*
+ * The same scan computed in chunks of 64 tokens, for prefill.  Same arguments,
+ * layouts, results (within rounding) and errors as moe_w4_gdn_scan(), plus a
+ * device workspace of at least moe_w4_gdn_chunked_workspace_bytes(dims) bytes,
+ * 16-byte aligned, owned by the caller (no initial contents are needed).
+ *
+ * Within a chunk the recurrence is rewritten so that only a 64 x 64 triangular
+ * solve stays sequential: with G the running sum of the log decays, the chunk's
+ * state corrections solve (I + A) U = diag(beta) (V - Gamma K S0^T), A[t][s] =
+ * beta_t exp(G_t - G_s) k_t . k_s for s < t, and the outputs and the next state
+ * are matrix products of U, S0, Q and K (the chunked form of the published
+ * gated delta rule).  Products run on bf16 MFMA with fp32 accumulation; fp32
+ * operands (the state, the solve's results) enter as bf16 hi + lo pairs, so the
+ * state keeps about 16 significant bits per product term.  The sequence is
+ * processed in segments of 1024 tokens, two kernels each; the state carries over
+ * in `state`.  Errors as moe_w4_gdn_scan(), and MOE_W4_ERR_NULL for a NULL
+ * workspace, MOE_W4_ERR_ALIGN for a misaligned one, MOE_W4_ERR_WORKSPACE for one
+ * that is too small.
+ */
+size_t moe_w4_gdn_chunked_workspace_bytes(const moe_w4_gdn_dims* dims);
+
+int moe_w4_gdn_scan_chunked(const moe_w4_gdn_dims* dims, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, float* state, void* out,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* The same with per-kernel timing events (two kernels per 1024-token segment). */
+int moe_w4_gdn_scan_chunked_timed(const moe_w4_gdn_dims* dims, const void* q, const void* k,
+                                  const void* v, const float* g, const float* beta, float* state,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  void* hip_stream, void** events, int capacity, int* n_kernels);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,11 +1,13 @@
 """GPU parity of the Gated DeltaNet scan, through the C ABI.
 
-Every case compares moe_w4_gdn_scan with the float64 oracle on the same seeded
-inputs.  Outputs: max|gpu - ref| / max|ref| <= 5e-3 (one round-to-nearest to
+Every case compares moe_w4_gdn_scan (the register-resident scan) or
+moe_w4_gdn_scan_chunked (the chunked MFMA form) with the float64 oracle on the
+same seeded inputs.  Outputs: max|gpu - ref| / max|ref| <= 5e-3 (one round-to-nearest to
 bf16 moves a value by at most half an ulp, 2^-8 ~ 3.9e-3 of itself; the fp32
 recurrence adds errors near 1e-6).  Final state:
 <= 1e-4 (fp32 throughout; the decay forgets old rounding errors within a few
-dozen tokens).
+dozen tokens).  The chunked form splits fp32 operands into bf16 hi + lo pairs,
+about 16 significant bits per product term, inside the same state bound.
 """
 import numpy as np
 import pytest
@@ -28,19 +30,21 @@ def _gpu():
     B.load_library()
 
 
-def gpu_scan(x):
+def gpu_scan(x, chunked=False):
     g = x.to("cuda")
     out = torch.empty_like(g.v)
     state = g.state.clone()
-    B.moe_w4_gdn_scan(g.q, g.k, g.v, g.g, g.beta, state, out)
+    scan = B.moe_w4_gdn_scan_chunked if chunked else B.moe_w4_gdn_scan
+    scan(g.q, g.k, g.v, g.g, g.beta, state, out)
     torch.cuda.synchronize()
     return out, state
 
 
-def check(shape, seed, what):
+def check(shape, seed, what, chunked=False):
+    what = f"{'chunked ' if chunked else ''}{what}"
     print(f"[gpu-gdn] {what}: T={shape.T} Hv={shape.n_v_heads} Hk={shape.n_k_heads} seed={seed}", flush=True)
     x = SG.draw_gdn(shape, seed)
-    out, state = gpu_scan(x)
+    out, state = gpu_scan(x, chunked)
     ref_o, ref_s = D.gdn_scan(x.q, x.k, x.v, x.g, x.beta, x.state)
     got_o = out.float().cpu().numpy().astype(np.float64)
     got_s = state.cpu().numpy().astype(np.float64)
@@ -129,3 +133,80 @@ def test_graph_replays_match_eager():
         step()
         torch.cuda.synchronize()
         x.v.mul_(-1.0)
+
+
+# --- the chunked MFMA form ---------------------------------------------------------
+
+def test_chunked_tiny():
+    shape, seed = SG.GDN_WORKLOADS["tiny"]
+    check(shape, seed, "tiny", chunked=True)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 100, 1023, 1024, 1025])
+def test_chunked_chunk_and_segment_boundaries(T):
+    # 64-token chunks, 1024-token segments (two launches each); a lone token past both
+    check(SG.GdnShape(T=T), 700 + T, f"T={T}", chunked=True)
+
+
+@pytest.mark.parametrize("Hv,Hk", [(8, 8), (8, 2), (6, 3)])
+def test_chunked_head_mappings(Hv, Hk):
+    check(SG.GdnShape(T=130, n_v_heads=Hv, n_k_heads=Hk), 800 + Hv + Hk, f"Hv={Hv} Hk={Hk}", chunked=True)
+
+
+@pytest.mark.parametrize("name", ["prefill512", "prefill2048"])
+def test_chunked_workloads(name):
+    shape, seed = SG.GDN_WORKLOADS[name]
+    check(shape, seed, name, chunked=True)
+
+
+def test_chunked_split_sequence_carries_the_state():
+    """Two chunked calls with the state carried through memory (the split falls
+    inside a chunk) give the one-call result within the tolerances."""
+    x = SG.draw_gdn(SG.GdnShape(T=300), 900).to("cuda")
+    out1 = torch.empty_like(x.v)
+    s1 = x.state.clone()
+    B.moe_w4_gdn_scan_chunked(x.q, x.k, x.v, x.g, x.beta, s1, out1)
+    out2 = torch.empty_like(x.v)
+    s2 = x.state.clone()
+    for a, b in ((0, 123), (123, 300)):
+        o = torch.empty_like(x.v[a:b])
+        B.moe_w4_gdn_scan_chunked(x.q[a:b].contiguous(), x.k[a:b].contiguous(), x.v[a:b].contiguous(),
+                                  x.g[a:b].contiguous(), x.beta[a:b].contiguous(), s2, o)
+        out2[a:b] = o
+    torch.cuda.synchronize()
+    eo = (out1.float() - out2.float()).abs().max().item() / out1.float().abs().max().item()
+    es = (s1 - s2).abs().max().item() / s1.abs().max().item()
+    assert eo <= OUT_TOL and es <= STATE_TOL, (eo, es)
+
+
+def test_chunked_workspace_size_and_graph_replays():
+    """The workspace the library asks for (one 1024-token segment at most), and
+    three graph replays of a chunked call equal to the eager call bit for bit."""
+    assert B.moe_w4_gdn_chunked_workspace_bytes(1, 32, 16) == 32 * (64 * 128 + 2 * 64 * 64 + 128) * 4
+    assert B.moe_w4_gdn_chunked_workspace_bytes(5000, 32, 16) == 16 * 32 * (64 * 128 + 2 * 64 * 64 + 128) * 4
+    x = SG.draw_gdn(SG.GdnShape(T=200), 901).to("cuda")
+    out = torch.empty_like(x.v)
+    state = x.state.clone()
+    ws = torch.empty(B.moe_w4_gdn_chunked_workspace_bytes(200, 32, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        state.copy_(x.state)
+        B.moe_w4_gdn_scan_chunked(x.q, x.k, x.v, x.g, x.beta, state, out, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_s = out.clone(), state.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for r in range(3):
+        out.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(state, ref_s), r

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmoe_w4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["router.hip", "decode.hip", "grouped.hip", "attn.hip", "gdn.hip", "moe_w4.cpp"]
+SOURCES = ["router.hip", "decode.hip", "grouped.hip", "attn.hip", "gdn.hip", "gdn_chunked.hip", "moe_w4.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

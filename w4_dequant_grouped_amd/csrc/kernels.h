@@ -119,6 +119,23 @@ struct GdnArgs {
     int T, Hv, Hk, rep;      // rep = Hv / Hk
 };
 
+// Chunked Gated DeltaNet scan (moe_w4_gdn_scan_chunked).  The sequence is
+// processed in segments of kGdnSegT tokens (chunks of 64), each a prep launch
+// over all its chunks and a scan launch; the state carries over in `state`.
+constexpr int kGdnSegT = 1024;
+struct GdnChunkArgs {
+    const uint16_t* q;       // bf16 [T][Hk][128]
+    const uint16_t* k;
+    const uint16_t* v;       // bf16 [T][Hv][128]
+    const float* g;          // [T][Hv]
+    const float* beta;       // [T][Hv]
+    float* state;            // [Hv][128][128]
+    uint16_t* out;           // bf16 [T][Hv][128]
+    float* ws;               // per (chunk, value head): W, Pm, Tb, gamma, d of one segment
+    int T, Hv, Hk, rep;
+    int t0, nt;              // segment: first token, tokens
+};
+
 // Optional per-kernel timing: events[2i] / events[2i+1] are recorded on the launch
 // stream before / after the i-th kernel of a call (while capacity allows).
 // Launches kernels and, when the caller supplies events, brackets each one with
@@ -154,5 +171,7 @@ hipError_t launch_forward_grouped(const ForwardArgs& a, hipStream_t st, KernelTi
 hipError_t launch_block_decode(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_gdn_scan(const GdnArgs& a, hipStream_t st, KernelTimer& tm);
+hipError_t launch_gdn_chunked(const GdnChunkArgs& a, hipStream_t st, KernelTimer& tm);
+size_t gdn_chunked_workspace_floats(int T, int Hv);
 
 }  // namespace moe_w4

@@ -519,6 +519,64 @@ int moe_w4_gdn_scan(const moe_w4_gdn_dims* dims, const void* q, const void* k, c
     return moe_w4_gdn_scan_timed(dims, q, k, v, g, beta, state, out, hip_stream, nullptr, 0, nullptr);
 }
 
+namespace {
+int gdn_dims_status(const moe_w4_gdn_dims* dims) {
+    if (!dims) return MOE_W4_ERR_NULL;
+    if (dims->flags != 0u) return MOE_W4_ERR_FLAGS;
+    if (dims->T < 0 || dims->T > MOE_W4_GDN_MAX_T || dims->n_v_heads < 1 || dims->n_v_heads > 128 ||
+        dims->n_k_heads < 1 || dims->n_v_heads % dims->n_k_heads != 0)
+        return MOE_W4_ERR_DIMS;
+    if (dims->dim != 128) return MOE_W4_ERR_GROUP;
+    return MOE_W4_OK;
+}
+}  // namespace
+
+size_t moe_w4_gdn_chunked_workspace_bytes(const moe_w4_gdn_dims* dims) {
+    if (gdn_dims_status(dims) != MOE_W4_OK) return 0;
+    return moe_w4::gdn_chunked_workspace_floats(dims->T, dims->n_v_heads) * sizeof(float);
+}
+
+int moe_w4_gdn_scan_chunked_timed(const moe_w4_gdn_dims* dims, const void* q, const void* k,
+                                  const void* v, const float* g, const float* beta, float* state,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  void* hip_stream, void** events, int capacity, int* n_kernels) {
+    if (n_kernels) *n_kernels = 0;
+    const int st = gdn_dims_status(dims);
+    if (st != MOE_W4_OK) return st;
+    if (dims->T == 0) return MOE_W4_OK;
+    if (!q || !k || !v || !g || !beta || !state || !out || !workspace) return MOE_W4_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 4) || !aligned(beta, 4) ||
+        !aligned(state, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+        return MOE_W4_ERR_ALIGN;
+    if (workspace_bytes < moe_w4_gdn_chunked_workspace_bytes(dims)) return MOE_W4_ERR_WORKSPACE;
+    moe_w4::GdnChunkArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.out = static_cast<uint16_t*>(out);
+    a.ws = static_cast<float*>(workspace);
+    a.T = dims->T;
+    a.Hv = dims->n_v_heads;
+    a.Hk = dims->n_k_heads;
+    a.rep = dims->n_v_heads / dims->n_k_heads;
+    a.t0 = 0;
+    a.nt = 0;
+    moe_w4::KernelTimer tm = make_timer(events, capacity);
+    const hipError_t err = moe_w4::launch_gdn_chunked(a, static_cast<hipStream_t>(hip_stream), tm);
+    if (n_kernels) *n_kernels = tm.count;
+    return launch_status(err);
+}
+
+int moe_w4_gdn_scan_chunked(const moe_w4_gdn_dims* dims, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, float* state, void* out,
+                            void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return moe_w4_gdn_scan_chunked_timed(dims, q, k, v, g, beta, state, out, workspace, workspace_bytes,
+                                         hip_stream, nullptr, 0, nullptr);
+}
+
 const char* moe_w4_status_string(int status) {
     switch (status) {
         case MOE_W4_OK: return "ok";

@@ -60,7 +60,8 @@ EXPORTS = ("moe_w4_workspace_bytes", "moe_w4_route", "moe_w4_forward", "moe_w4_b
            "moe_w4_route_timed", "moe_w4_forward_timed", "moe_w4_block_timed", "moe_w4_block_noalloc",
            "moe_w4_status_string", "moe_w4_last_error",
            "moe_w4_attn_workspace_bytes", "moe_w4_attn_decode", "moe_w4_attn_decode_timed",
-           "moe_w4_gdn_scan", "moe_w4_gdn_scan_timed")
+           "moe_w4_gdn_scan", "moe_w4_gdn_scan_timed", "moe_w4_gdn_chunked_workspace_bytes",
+           "moe_w4_gdn_scan_chunked", "moe_w4_gdn_scan_chunked_timed")
 
 _lib = None
 
@@ -111,6 +112,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_w4_gdn_scan.restype = ctypes.c_int
     lib.moe_w4_gdn_scan_timed.argtypes = lib.moe_w4_gdn_scan.argtypes + [P, ctypes.c_int, P]
     lib.moe_w4_gdn_scan_timed.restype = ctypes.c_int
+    lib.moe_w4_gdn_chunked_workspace_bytes.argtypes = [D]
+    lib.moe_w4_gdn_chunked_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_w4_gdn_scan_chunked.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_w4_gdn_scan_chunked.restype = ctypes.c_int
+    lib.moe_w4_gdn_scan_chunked_timed.argtypes = lib.moe_w4_gdn_scan_chunked.argtypes + [P, ctypes.c_int, P]
+    lib.moe_w4_gdn_scan_chunked_timed.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -450,4 +457,37 @@ def moe_w4_gdn_scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
         _stream(), arr, cap, ctypes.byref(n))
     _check(st, "moe_w4_gdn_scan")
+    return n.value
+
+
+def moe_w4_gdn_chunked_workspace_bytes(T: int, n_v_heads: int, n_k_heads: int, dim: int = 128) -> int:
+    return int(load_library().moe_w4_gdn_chunked_workspace_bytes(
+        ctypes.byref(moe_w4_gdn_dims(T, n_v_heads, n_k_heads, dim, 0))))
+
+
+def moe_w4_gdn_scan_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                            beta: torch.Tensor, state: torch.Tensor, out: torch.Tensor,
+                            workspace: Optional[torch.Tensor] = None, events=None) -> int:
+    """The chunked scan on the current stream (same arguments as moe_w4_gdn_scan plus a
+    workspace; one is allocated when none is given).  Returns the kernel count."""
+    for t, dt, name in ((q, torch.bfloat16, "q"), (k, torch.bfloat16, "k"), (v, torch.bfloat16, "v"),
+                        (g, torch.float32, "g"), (beta, torch.float32, "beta"),
+                        (state, torch.float32, "state"), (out, torch.bfloat16, "out")):
+        _dev(t, dt, name)
+    T, Hk, d = q.shape
+    Hv = v.shape[1]
+    if k.shape != q.shape or v.shape != (T, Hv, d) or g.shape != (T, Hv) or beta.shape != (T, Hv) \
+            or state.shape != (Hv, d, d) or out.shape != (T, Hv, d):
+        raise ValueError("inconsistent Gated DeltaNet shapes")
+    dims = moe_w4_gdn_dims(T, Hv, Hk, d, 0)
+    if workspace is None:
+        workspace = torch.empty(max(moe_w4_gdn_chunked_workspace_bytes(T, Hv, Hk, d), 16),
+                                dtype=torch.uint8, device=q.device)
+    _dev(workspace, torch.uint8, "workspace")
+    arr, cap = _events_arg(events)
+    n = ctypes.c_int(0)
+    st = load_library().moe_w4_gdn_scan_chunked_timed(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(), arr, cap, ctypes.byref(n))
+    _check(st, "moe_w4_gdn_scan_chunked")
     return n.value
