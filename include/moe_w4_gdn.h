@@ -84,7 +84,7 @@ int moe_w4_gdn_scan_timed(const moe_w4_gdn_dims* dims, const void* q, const void
  * gated delta rule).  Products run on bf16 MFMA with fp32 accumulation; fp32
  * operands (the state, the solve's results) enter as bf16 hi + lo pairs, so the
  * state keeps about 16 significant bits per product term.  The sequence is
- * processed in segments of 1024 tokens, two kernels each; the state carries over
+ * processed in segments of 2048 tokens, two kernels each; the state carries over
  * in `state`.  Errors as moe_w4_gdn_scan(), and MOE_W4_ERR_NULL for a NULL
  * workspace, MOE_W4_ERR_ALIGN for a misaligned one, MOE_W4_ERR_WORKSPACE for one
  * that is too small.
@@ -95,7 +95,7 @@ int moe_w4_gdn_scan_chunked(const moe_w4_gdn_dims* dims, const void* q, const vo
                             const float* g, const float* beta, float* state, void* out,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* The same with per-kernel timing events (two kernels per 1024-token segment). */
+/* The same with per-kernel timing events (two kernels per 2048-token segment). */
 int moe_w4_gdn_scan_chunked_timed(const moe_w4_gdn_dims* dims, const void* q, const void* k,
                                   const void* v, const float* g, const float* beta, float* state,
                                   void* out, void* workspace, size_t workspace_bytes,

@@ -142,9 +142,9 @@ def test_chunked_tiny():
     check(shape, seed, "tiny", chunked=True)
 
 
-@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 100, 1023, 1024, 1025])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 100, 1000, 2047, 2048, 2049])
 def test_chunked_chunk_and_segment_boundaries(T):
-    # 64-token chunks, 1024-token segments (two launches each); a lone token past both
+    # 64-token chunks, 2048-token segments (two launches each); a lone token past both
     check(SG.GdnShape(T=T), 700 + T, f"T={T}", chunked=True)
 
 
@@ -180,10 +180,13 @@ def test_chunked_split_sequence_carries_the_state():
 
 
 def test_chunked_workspace_size_and_graph_replays():
-    """The workspace the library asks for (one 1024-token segment at most), and
+    """The workspace the library asks for (one 2048-token segment at most), and
     three graph replays of a chunked call equal to the eager call bit for bit."""
-    assert B.moe_w4_gdn_chunked_workspace_bytes(1, 32, 16) == 32 * (64 * 128 + 2 * 64 * 64 + 128) * 4
-    assert B.moe_w4_gdn_chunked_workspace_bytes(5000, 32, 16) == 16 * 32 * (64 * 128 + 2 * 64 * 64 + 128) * 4
+    # per chunk: 20608 words per value head (-W, Pm and Vt fragments, gamma, d) and
+    # 4096 per key head (K^T fragments); a 64-word sink
+    per_chunk = (32 * 20608 + 16 * 4096) * 4
+    assert B.moe_w4_gdn_chunked_workspace_bytes(1, 32, 16) == per_chunk + 256
+    assert B.moe_w4_gdn_chunked_workspace_bytes(5000, 32, 16) == 32 * per_chunk + 256
     x = SG.draw_gdn(SG.GdnShape(T=200), 901).to("cuda")
     out = torch.empty_like(x.v)
     state = x.state.clone()

@@ -5,28 +5,36 @@
 // one model, one chip", paragraph 2: the model's linear-attention layers keep a
 // fixed-size state):
 //     S_t = a_t S_{t-1} + beta_t (v_t - a_t S_{t-1} k_t) k_t^T,   o_t = S_t q_t
-// rewritten per chunk so that everything except a 64-step triangular solve is a
-// matrix product.  Within a chunk (positions t, s = 0..63), with G_t the running
-// sum of the log decays g and gamma_t = exp(G_t):
+// rewritten per chunk so that everything except a 64 x 64 triangular inverse is
+// a matrix product.  Within a chunk (positions t, s = 0..63), with G_t the
+// running sum of the log decays g and gamma_t = exp(G_t):
 //     u_t := beta_t (v_t - a_t S_{t-1} k_t)   satisfies   (I + A) U = diag(beta) (V - Gamma K S_0^T)
 //     A[t][s] = beta_t exp(G_t - G_s) k_t.k_s   (s < t)
 // so with Tinv = (I + A)^-1, Tb = Tinv diag(beta), Tbg = Tinv diag(beta gamma):
-//     U   = Tb V - W S_0^T,            W = Tbg K
+//     U   = Vt - W S_0^T,              Vt = Tb V,  W = Tbg K
 //     O   = Gamma Q S_0^T + Pm U,      Pm[t][s] = exp(G_t - G_s) q_t.k_s   (s <= t)
 //     S_C = gamma_63 S_0 + U^T diag(d) K,   d_s = exp(G_63 - G_s)
 // (all decays appear as exp of a non-positive difference, never as a ratio).
 //
-// k_gdn_prep: one workgroup per (chunk, value head), all chunks at once: K K^T
-//   and Q K^T on MFMA (bf16 inputs, exact products, fp32 sums), the decay masks,
-//   Tinv by forward substitution (one wavefront, a column per lane, fp32), and W
-//   = Tbg K on MFMA.  It stores W, Pm, Tb and the decays gamma and d in the workspace.
+// k_gdn_prep: one workgroup per (chunk, value head), every chunk at once.  K K^T
+//   and K Q^T on MFMA; the masks and decays; Tinv in three levels (four 16 x 16
+//   diagonal blocks by forward substitution in fp32, then the 16- and 32-wide
+//   off-diagonal blocks as products of inverses); W^T = K^T Tbg^T and Vt = Tb V
+//   on MFMA.  Everything the sequential scan needs is written to the workspace
+//   already in the lane layout of its MFMA operands.
 // k_gdn_chunk_scan: one workgroup per (16 value rows, value head), chunk after
-//   chunk.  The state is held as S^T in the layout of a 16x16x16 MFMA result
-//   (lane l: key columns 4(l/16)..+3 of a 16-column block, value row l%16), which
-//   is also the layout of that MFMA's B operand, so the state, U and the outputs
-//   feed the next products without transposes.  fp32 operands (the state, W, U,
-//   Pm, Tb) enter the bf16 MFMA as hi + lo bf16 pairs: hi*hi + hi*lo + lo*hi when
-//   both sides are split, hi*x + lo*x against exact bf16 data (q, k, v).
+//   chunk, two barriers per chunk.  The state is held as S^T in the layout of an
+//   MFMA result (lane l: key rows 4(l/16)..+3 of a 16-key block, value row
+//   l%16); two such blocks side by side are exactly a 32-deep B operand, so the
+//   state, U and d U feed the next products straight from registers or LDS.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16, lane l holding A[l%16][8(l/16)+e],
+// B[8(l/16)+e][l%16] and C[4(l/16)+r][l%16].  Operands that the scan builds from
+// two result blocks use the contraction order "paired blocks": slot e of lane
+// group g is index 4g+e of the first 16-block for e < 4 and index 16+4g+(e-4) of
+// the second; the workspace fragments that meet them are written in that same
+// order.  fp32 operands enter as bf16 hi + lo pairs: hi*hi + hi*lo + lo*hi when
+// both sides are split, hi*x + lo*x against exact bf16 data (q, k, v).
 #include "device.h"
 #include "kernels.h"
 
@@ -38,103 +46,115 @@ constexpr int kC = 64;            // tokens per chunk
 constexpr int kD = 128;           // head dimension
 constexpr int kRB = 16;           // value rows per scan workgroup
 
+// Workspace, in 4-byte words.  Per (chunk, value head):
+//   -W  fragments [token block 4][key group 4]    2048 B each: 64 lanes x 16 B hi, then lo
+//   Pm  fragments [token block 4][token group 2]  same format (group 1 only for blocks 2, 3)
+//   Vt  fragments [token block 4][value block 8]  64 lanes x 4 floats, result layout
+//   gamma [64], d [64]
+// then per (chunk, key head): K^T fragments [key block 8][token group 2], 64 lanes x 8 bf16,
+// and last a 64-word sink for the scan's stores of rows past the sequence (so
+// that every lane stores and the memory counters it waits on are the same on
+// every chunk).
+constexpr int kFragSplit = 512;                       // words of a split fragment
+constexpr int kOffW = 0;
+constexpr int kOffP = kOffW + 16 * kFragSplit;
+constexpr int kOffV = kOffP + 8 * kFragSplit;
+constexpr int kOffG = kOffV + 32 * 256;
+constexpr int kHeadWords = kOffG + 2 * kC;            // 20608
+constexpr int kKeyWords = 16 * 256;                   // 4096
+constexpr int kSinkWords = 64;
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ f32x4 mfma32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// fp32 x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), four at a time
-struct Split4 {
-    s16x4 hi, lo;
+// x = hi + lo, hi = bf16(x), lo = bf16(x - hi); four values -> two dwords each
+struct Half4 {
+    u32x2 hi, lo;
 };
-__device__ __forceinline__ Split4 split4(const f32x4& x) {
-    Split4 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t hb = f32_to_bf16(x[e]);
-        r.hi[e] = (short)hb;
-        r.lo[e] = (short)f32_to_bf16(x[e] - bf16_to_f32(hb));
-    }
+__device__ __forceinline__ Half4 split4(const f32x4& x) {
+    const uint32_t h01 = pack_bf16x2(x[0], x[1]), h23 = pack_bf16x2(x[2], x[3]);
+    Half4 r;
+    r.hi = u32x2{h01, h23};
+    r.lo = u32x2{pack_bf16x2(x[0] - bf16lo(h01), x[1] - bf16hi(h01)),
+                 pack_bf16x2(x[2] - bf16lo(h23), x[3] - bf16hi(h23))};
     return r;
 }
-__device__ __forceinline__ Split4 neg(const Split4& s) {
-    Split4 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r.hi[e] = (short)(s.hi[e] ^ (short)0x8000);
-        r.lo[e] = (short)(s.lo[e] ^ (short)0x8000);
-    }
-    return r;
+// eight values (a: slots 0..3, b: slots 4..7) as one split 32-deep operand
+struct Split8 {
+    u32x4 hi, lo;
+};
+__device__ __forceinline__ Split8 split8(const f32x4& a, const f32x4& b) {
+    const Half4 x = split4(a), y = split4(b);
+    return Split8{u32x4{x.hi.x, x.hi.y, y.hi.x, y.hi.y}, u32x4{x.lo.x, x.lo.y, y.lo.x, y.lo.y}};
 }
-// a (split) times b (split): three bf16 products
-__device__ __forceinline__ f32x4 mma3(const Split4& a, const Split4& b, f32x4 c) {
-    c = mfma16(a.hi, b.hi, c);
-    c = mfma16(a.hi, b.lo, c);
-    return mfma16(a.lo, b.hi, c);
-}
-// a (split) times exact bf16 b, or exact a times split b
-__device__ __forceinline__ f32x4 mma2(const Split4& a, const s16x4& b, f32x4 c) {
-    c = mfma16(a.hi, b, c);
-    return mfma16(a.lo, b, c);
-}
-__device__ __forceinline__ f32x4 mma2(const s16x4& a, const Split4& b, f32x4 c) {
-    c = mfma16(a, b.hi, c);
-    return mfma16(a, b.lo, c);
+__device__ __forceinline__ u32x4 cat(const u32x2& a, const u32x2& b) { return u32x4{a.x, a.y, b.x, b.y}; }
+
+// 16 x 16 x 16 product of split fp32 operands (the inverse's off-diagonal blocks)
+__device__ __forceinline__ f32x4 mma3_16(const Half4& a, const Half4& b, f32x4 c) {
+    const s16x4 ah = __builtin_bit_cast(s16x4, a.hi), al = __builtin_bit_cast(s16x4, a.lo);
+    const s16x4 bh = __builtin_bit_cast(s16x4, b.hi), bl = __builtin_bit_cast(s16x4, b.lo);
+    c = mfma16(ah, bh, c);
+    c = mfma16(ah, bl, c);
+    return mfma16(al, bh, c);
 }
 
-__device__ __forceinline__ s16x4 load_bf16x4(const uint16_t* p) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-    return __builtin_bit_cast(s16x4, v);
+// A operand (rows m0 + l%16, columns k0 + 4 (l/16) ..) and B operand (rows
+// k0 + 4 (l/16) .., column n0 + l%16) of a 16 x 16 x 16 product, from a row-major
+// fp32 LDS matrix
+__device__ __forceinline__ Half4 lds_a16(const float (*m)[kC + 4], int m0, int k0, int lane) {
+    const float4 v = *reinterpret_cast<const float4*>(&m[m0 + (lane & 15)][k0 + 4 * (lane >> 4)]);
+    return split4(f32x4{v.x, v.y, v.z, v.w});
+}
+__device__ __forceinline__ Half4 lds_b16(const float (*m)[kC + 4], int k0, int n0, int lane) {
+    const int k = k0 + 4 * (lane >> 4), n = n0 + (lane & 15);
+    return split4(f32x4{m[k][n], m[k + 1][n], m[k + 2][n], m[k + 3][n]});
 }
 
-}  // namespace
-
-// Workspace of one (chunk, value head), 4-byte words: W [64][128], Pm [64][64] and
-// Tb [64][64] as bf16 hi/lo pairs, grouped four columns at a time (eight bf16:
-// the four hi, then the four lo, so one 16-byte load is an MFMA operand's split
-// pair), then gamma [64] = exp(G_t) and d [64] = exp(G_63 - G_t), fp32.
-constexpr size_t kGdnChunkFloats = (size_t)kC * kD + 2 * (size_t)kC * kC + 2 * kC;
-
-namespace {
-// Stores the split pair of x at column `col` of row `row` of a [rows][ncol] matrix
-// in the grouped hi/lo format.
-__device__ __forceinline__ void store_split(uint16_t* base, int ncol, int row, int col, float x) {
-    const uint32_t hb = f32_to_bf16(x);
-    const uint32_t lb = f32_to_bf16(x - bf16_to_f32(hb));
-    uint16_t* g = base + ((size_t)row * (ncol / 4) + col / 4) * 8 + (col & 3);
-    g[0] = (uint16_t)hb;
-    g[4] = (uint16_t)lb;
+// 4 tokens x 4 columns of bf16 (rows r[0..3], two dwords each) -> 4 columns x 4 tokens
+__device__ __forceinline__ void transpose4(const u32x2 (&r)[4], u32x2 (&c)[4]) {
+    c[0] = u32x2{(r[0].x & 0xFFFFu) | (r[1].x << 16), (r[2].x & 0xFFFFu) | (r[3].x << 16)};
+    c[1] = u32x2{(r[0].x >> 16) | (r[1].x & 0xFFFF0000u), (r[2].x >> 16) | (r[3].x & 0xFFFF0000u)};
+    c[2] = u32x2{(r[0].y & 0xFFFFu) | (r[1].y << 16), (r[2].y & 0xFFFFu) | (r[3].y << 16)};
+    c[3] = u32x2{(r[0].y >> 16) | (r[1].y & 0xFFFF0000u), (r[2].y >> 16) | (r[3].y & 0xFFFF0000u)};
 }
-__device__ __forceinline__ Split4 load_split(const uint16_t* base, int ncol, int row, int col4) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(base + ((size_t)row * (ncol / 4) + col4 / 4) * 8);
-    Split4 r;
-    r.hi = __builtin_bit_cast(s16x4, u32x2{v.x, v.y});
-    r.lo = __builtin_bit_cast(s16x4, u32x2{v.z, v.w});
-    return r;
+
+__device__ __forceinline__ float* head_block(const GdnChunkArgs& a, int c, int h) {
+    return a.ws + ((size_t)c * a.Hv + h) * kHeadWords;
 }
+__device__ __forceinline__ float* key_block(const GdnChunkArgs& a, int nch, int c, int kh) {
+    return a.ws + (size_t)nch * a.Hv * kHeadWords + ((size_t)c * a.Hk + kh) * kKeyWords;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // k_gdn_prep
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[kC][kD + 8];    // K rows (bf16)
-    __shared__ __attribute__((aligned(16))) uint16_t s_q[kC][kD + 8];    // Q rows
-    __shared__ __attribute__((aligned(16))) uint16_t s_kt[kD][kC + 8];   // K transposed
-    __shared__ __attribute__((aligned(16))) float s_a[kC][kC + 4];       // A, then Tbg
-    __shared__ float s_g[kC], s_b[kC];
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[kC][kD + 8];        // K rows
+    __shared__ __attribute__((aligned(16))) uint16_t s_qv[kD * (kC + 8)];    // Q rows [64][136], then V^T [128][72]
+    __shared__ __attribute__((aligned(16))) uint16_t s_kt[kD][kC + 8];       // K^T
+    __shared__ __attribute__((aligned(16))) float s_a[kC][kC + 4];           // A, then Tinv
+    __shared__ __attribute__((aligned(16))) float s_g[kC], s_b[kC], s_bg[kC];
+    uint16_t (*s_q)[kD + 8] = reinterpret_cast<uint16_t (*)[kD + 8]>(s_qv);
+    uint16_t (*s_vt)[kC + 8] = reinterpret_cast<uint16_t (*)[kC + 8]>(s_qv);
+
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    const int g4 = lane >> 4, ln = lane & 15;
     const int c = blockIdx.x, h = blockIdx.y;
     const int kh = h / a.rep;
+    const int nch = (a.nt + kC - 1) / kC;
     const int t0 = a.t0 + c * kC;
     const int nt = min(kC, a.t0 + a.nt - t0);
-    float* ws = a.ws + ((size_t)c * a.Hv + h) * kGdnChunkFloats;
-    uint16_t* wW = reinterpret_cast<uint16_t*>(ws);
-    uint16_t* wP = reinterpret_cast<uint16_t*>(ws + kC * kD);
-    uint16_t* wT = reinterpret_cast<uint16_t*>(ws + kC * kD + kC * kC);
-    float* wG = ws + kC * kD + 2 * kC * kC;
+    float* hb = head_block(a, c, h);
 
     // decays and write strengths; tokens past the sequence have g = 0, beta = 0
     if (wave == 0) {
@@ -147,15 +167,19 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
             const float v = __shfl_up(gv, o, kWave);
             if (lane >= o) gv += v;
         }
+        const float gam = expf(gv);
         s_g[lane] = gv;
         s_b[lane] = bv;
-        wG[lane] = expf(gv);
-        wG[kC + lane] = expf(__shfl(gv, kC - 1, kWave) - gv);
+        s_bg[lane] = bv * gam;
+        hb[kOffG + lane] = gam;
+        hb[kOffG + kC + lane] = expf(__shfl(gv, kC - 1, kWave) - gv);
     }
-    // q and k rows of the chunk (zero past the sequence); K also transposed
-    for (int i = threadIdx.x; i < kC * (kD / 8); i += blockDim.x) {
-        const int t = i / (kD / 8), j = (i - t * (kD / 8)) * 8;
-        u32x4 kk = {0u, 0u, 0u, 0u}, qq = {0u, 0u, 0u, 0u};
+    // Q and K rows (zero past the sequence)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = threadIdx.x + 256 * u;                 // token i / 16, columns 8 (i % 16) ..
+        const int t = i >> 4, j = (i & 15) * 8;
+        u32x4 kk = {0u, 0u, 0u, 0u}, qq = kk;
         if (t < nt) {
             const size_t off = ((size_t)(t0 + t) * a.Hk + kh) * kD + j;
             kk = load_u32x4(a.k + off);
@@ -163,60 +187,112 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
         }
         *reinterpret_cast<u32x4*>(&s_k[t][j]) = kk;
         *reinterpret_cast<u32x4*>(&s_q[t][j]) = qq;
-        const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+    }
+    // K^T to LDS now, V^T tiles to registers (written over Q once K Q^T is done):
+    // tile = tokens 4 tq .. +3, columns 4 cg .. +3
+    u32x2 vtile[2][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s_kt[j + 2 * e][t] = (uint16_t)(kw[e] & 0xFFFFu);
-            s_kt[j + 2 * e + 1][t] = (uint16_t)(kw[e] >> 16);
+    for (int u = 0; u < 2; ++u) {
+        const int i = threadIdx.x + 256 * u;
+        const int tq = i & 15, cg = i >> 4;
+        u32x2 kr[4], vr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * tq + r;
+            const bool ok = t < nt;
+            kr[r] = ok ? *reinterpret_cast<const u32x2*>(a.k + ((size_t)(t0 + t) * a.Hk + kh) * kD + 4 * cg)
+                       : u32x2{0u, 0u};
+            vr[r] = ok ? *reinterpret_cast<const u32x2*>(a.v + ((size_t)(t0 + t) * a.Hv + h) * kD + 4 * cg)
+                       : u32x2{0u, 0u};
         }
+        u32x2 kc[4];
+        transpose4(kr, kc);
+        transpose4(vr, vtile[u]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x2*>(&s_kt[4 * cg + d][4 * tq]) = kc[d];
     }
     __syncthreads();
 
-    // K K^T and Q K^T, rows t of this wavefront's block, blocks s <= t only
-    {
-        const int tl = lane & 15, ks = (lane >> 4) * 4;
-        f32x4 kk[4], qk[4];
+    // K^T fragments of the scan's state update (once per key head): key block jb,
+    // token group p, paired-block order
+    if (h % a.rep == 0) {
+        u32x4* kf = reinterpret_cast<u32x4*>(key_block(a, nch, c, kh));
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) { kk[sb] = f32x4{0.f, 0.f, 0.f, 0.f}; qk[sb] = kk[sb]; }
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j0 = 0; j0 < kD; j0 += 16) {
-            const s16x4 ak = load_bf16x4(&s_k[16 * wave + tl][j0 + ks]);
-            const s16x4 aq = load_bf16x4(&s_q[16 * wave + tl][j0 + ks]);
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                if (sb > wave) continue;
-                const s16x4 b = load_bf16x4(&s_k[16 * sb + tl][j0 + ks]);
-                kk[sb] = mfma16(ak, b, kk[sb]);
-                qk[sb] = mfma16(aq, b, qk[sb]);
+            for (int p = 0; p < 2; ++p) {
+                const int jb = 2 * wave + i;
+                const uint16_t* row = &s_kt[16 * jb + ln][32 * p + 4 * g4];
+                kf[(jb * 2 + p) * 64 + lane] = cat(*reinterpret_cast<const u32x2*>(row),
+                                                   *reinterpret_cast<const u32x2*>(row + 16));
             }
-        }
-        // masks and decays: A (strictly lower, times beta_t) to LDS, Pm (lower) to the workspace
+    }
+
+    // K K^T and K Q^T as transposed blocks [s block sb][t block = wave]: lane holds
+    // s = 16 sb + 4 g4 + r, t = 16 wave + ln.  A (strictly lower, times beta_t) to
+    // LDS as rows t; Pm kept for its fragments.
+    f32x4 pm[4];
+    {
+        const int t = 16 * wave + ln;
+        const float gt = s_g[t], bt = s_b[t];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
-            const int s = 16 * sb + tl;
+            f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = kk;
+            if (sb <= wave) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const u32x4 as = *reinterpret_cast<const u32x4*>(&s_k[16 * sb + ln][32 * p + 8 * g4]);
+                    const u32x4 bk = *reinterpret_cast<const u32x4*>(&s_k[t][32 * p + 8 * g4]);
+                    const u32x4 bq = *reinterpret_cast<const u32x4*>(&s_q[t][32 * p + 8 * g4]);
+                    kk = mfma32(as, bk, kk);
+                    kq = mfma32(as, bq, kq);
+                }
+            }
+            f32x4 av, pv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + ks + r;
-                const float dec = (s <= t) ? expf(s_g[t] - s_g[s]) : 0.f;
-                const float av = (sb <= wave && s < t) ? s_b[t] * dec * kk[sb][r] : 0.f;
-                const float pv = (sb <= wave) ? dec * qk[sb][r] : 0.f;
-                s_a[t][s] = av;
-                store_split(wP, kC, t, s, pv);
+                const int s = 16 * sb + 4 * g4 + r;
+                const float dec = (s <= t) ? expf(gt - s_g[s]) : 0.f;
+                av[r] = (s < t) ? bt * dec * kk[r] : 0.f;
+                pv[r] = dec * kq[r];
             }
+            pm[sb] = pv;
+            *reinterpret_cast<float4*>(&s_a[t][16 * sb + 4 * g4]) = float4{av[0], av[1], av[2], av[3]};
         }
     }
-    __syncthreads();
-
-    // Tinv = (I + A)^-1 by forward substitution: lane c holds column c
-    if (wave == 0) {
-        // four independent partial sums per row shorten the dependent chain
-        float x[kC];
+    // Pm fragments [token block wave][token group p]
+    {
+        float* pf = hb + kOffP;
 #pragma unroll
-        for (int t = 0; t < kC; ++t) {
+        for (int p = 0; p < 2; ++p) {
+            if (2 * p > wave) continue;
+            const Split8 sp = split8(pm[2 * p], pm[2 * p + 1]);
+            u32x4* f = reinterpret_cast<u32x4*>(pf + (wave * 2 + p) * kFragSplit);
+            f[lane] = sp.hi;
+            f[64 + lane] = sp.lo;
+        }
+    }
+    __syncthreads();          // A complete; Q no longer read
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = threadIdx.x + 256 * u;
+        const int tq = i & 15, cg = i >> 4;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x2*>(&s_vt[4 * cg + d][4 * tq]) = vtile[u][d];
+    }
+
+    // Tinv level 1: wavefront w inverts its diagonal block I + A_ww by forward
+    // substitution in fp32, lane c < 16 holding column c
+    if (lane < 16) {
+        const int o = 16 * wave;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
             float acc0 = (t == lane) ? 1.f : 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
 #pragma unroll
             for (int s = 0; s < t; s += 4) {
-                const float4 av = *reinterpret_cast<const float4*>(&s_a[t][s]);
+                const float4 av = *reinterpret_cast<const float4*>(&s_a[o + t][o + s]);
                 acc0 = fmaf(-av.x, x[s], acc0);
                 if (s + 1 < t) acc1 = fmaf(-av.y, x[s + 1], acc1);
                 if (s + 2 < t) acc2 = fmaf(-av.z, x[s + 2], acc2);
@@ -224,33 +300,98 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
             }
             x[t] = (acc0 + acc1) + (acc2 + acc3);
         }
-        // Tb = Tinv diag(beta) to the workspace, Tbg = Tinv diag(beta gamma) to LDS
-        // (over A, which only this wavefront has been reading)
-        const float bc = s_b[lane];
-        const float bgc = bc * expf(s_g[lane]);
 #pragma unroll
-        for (int t = 0; t < kC; ++t) {
-            store_split(wT, kC, t, lane, x[t] * bc);
-            s_a[t][lane] = x[t] * bgc;
-        }
+        for (int t = 0; t < 16; ++t) s_a[o + t][o + lane] = x[t];
     }
     __syncthreads();
 
-    // W = Tbg K: rows t of this wavefront's block, all 128 key columns
-    {
-        const int tl = lane & 15, ks = (lane >> 4) * 4;
+    // level 2: X_10 = -X_11 A_10 X_00 (wavefront 0), X_32 = -X_33 A_32 X_22 (wavefront 2)
+    if (wave == 0 || wave == 2) {
+        const int i = wave + 1, j = wave;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 r = mma3_16(lds_a16(s_a, 16 * i, 16 * j, lane), lds_b16(s_a, 16 * j, 16 * j, lane), z);
+        const f32x4 x = mma3_16(lds_a16(s_a, 16 * i, 16 * i, lane), split4(r), z);
 #pragma unroll
-        for (int jb = 0; jb < kD / 16; ++jb) {
+        for (int e = 0; e < 4; ++e) s_a[16 * i + 4 * g4 + e][16 * j + ln] = -x[e];
+    }
+    __syncthreads();
+
+    // level 3: the 32 x 32 block below the diagonal, X_ij for i = 2, 3 and j = 0, 1:
+    // Y_kj = sum_{m = 0, 1} A_km X_mj, X_ij = -sum_{k = 2..i} X_ik Y_kj
+    {
+        const int i = 2 + (wave >> 1), j = wave & 1;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 y2 = mma3_16(lds_a16(s_a, 32, 16, lane), lds_b16(s_a, 16, 16 * j, lane), z);
+        if (j == 0) y2 = mma3_16(lds_a16(s_a, 32, 0, lane), lds_b16(s_a, 0, 0, lane), y2);
+        f32x4 x = mma3_16(lds_a16(s_a, 16 * i, 32, lane), split4(y2), z);
+        if (i == 3) {
+            f32x4 y3 = mma3_16(lds_a16(s_a, 48, 16, lane), lds_b16(s_a, 16, 16 * j, lane), z);
+            if (j == 0) y3 = mma3_16(lds_a16(s_a, 48, 0, lane), lds_b16(s_a, 0, 0, lane), y3);
+            x = mma3_16(lds_a16(s_a, 48, 48, lane), split4(y3), x);
+        }
+        __syncthreads();      // every read of A_2j, A_3j done before they are overwritten
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_a[16 * i + 4 * g4 + e][16 * j + ln] = -x[e];
+    }
+    __syncthreads();          // Tinv complete (zero above the diagonal), V^T staged
+
+    // rows t = 16 wave + ln of Tb and Tbg over token groups p (natural order);
+    // Tinv is zero for s > t, so blocks 0 and 1 need group 0 only
+    const int np = wave >= 2 ? 2 : 1;
+    Split8 tbs[2], tgs[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        if (p >= np) continue;
+        const int s0 = 32 * p + 8 * g4;
+        const float* row = &s_a[16 * wave + ln][s0];
+        const float4 x0 = *reinterpret_cast<const float4*>(row), x1 = *reinterpret_cast<const float4*>(row + 4);
+        const float4 b0 = *reinterpret_cast<const float4*>(&s_b[s0]), b1 = *reinterpret_cast<const float4*>(&s_b[s0 + 4]);
+        const float4 c0 = *reinterpret_cast<const float4*>(&s_bg[s0]), c1 = *reinterpret_cast<const float4*>(&s_bg[s0 + 4]);
+        tbs[p] = split8(f32x4{x0.x * b0.x, x0.y * b0.y, x0.z * b0.z, x0.w * b0.w},
+                        f32x4{x1.x * b1.x, x1.y * b1.y, x1.z * b1.z, x1.w * b1.w});
+        tgs[p] = split8(f32x4{x0.x * c0.x, x0.y * c0.y, x0.z * c0.z, x0.w * c0.w},
+                        f32x4{x1.x * c1.x, x1.y * c1.y, x1.z * c1.z, x1.w * c1.w});
+    }
+
+    // W^T = K^T Tbg^T as blocks [key block jb][token block wave]: lane holds
+    // W[16 wave + ln][16 jb + 4 g4 + r], two blocks = one -W fragment (paired order)
+    {
+        u32x4* wf = reinterpret_cast<u32x4*>(hb + kOffW);
+#pragma unroll
+        for (int pk = 0; pk < 4; ++pk) {
+            f32x4 w2[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int jb = 2 * pk + i;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    if (p >= np) continue;
+                    const u32x4 ak = *reinterpret_cast<const u32x4*>(&s_kt[16 * jb + ln][32 * p + 8 * g4]);
+                    acc = mfma32(ak, tgs[p].hi, acc);
+                    acc = mfma32(ak, tgs[p].lo, acc);
+                }
+                w2[i] = -acc;
+            }
+            const Split8 sp = split8(w2[0], w2[1]);
+            wf[(wave * 4 + pk) * 128 + lane] = sp.hi;
+            wf[(wave * 4 + pk) * 128 + 64 + lane] = sp.lo;
+        }
+    }
+    // Vt = Tb V as blocks [token block wave][value block vb], stored in result layout
+    {
+        f32x4* vf = reinterpret_cast<f32x4*>(hb + kOffV);
+#pragma unroll
+        for (int vb = 0; vb < 8; ++vb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s0 = 0; s0 < kC; s0 += 16) {
-                const float4 t4 = *reinterpret_cast<const float4*>(&s_a[16 * wave + tl][s0 + ks]);
-                const Split4 at = split4(f32x4{t4.x, t4.y, t4.z, t4.w});
-                const s16x4 b = load_bf16x4(&s_kt[16 * jb + tl][s0 + ks]);
-                acc = mma2(at, b, acc);
+            for (int p = 0; p < 2; ++p) {
+                if (p >= np) continue;
+                const u32x4 bv = *reinterpret_cast<const u32x4*>(&s_vt[16 * vb + ln][32 * p + 8 * g4]);
+                acc = mfma32(tbs[p].hi, bv, acc);
+                acc = mfma32(tbs[p].lo, bv, acc);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) store_split(wW, kD, 16 * wave + ks + r, 16 * jb + tl, acc[r]);
+            vf[(wave * 8 + vb) * 64 + lane] = acc;
         }
     }
 }
@@ -258,193 +399,161 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
 // ---------------------------------------------------------------------------
 // k_gdn_chunk_scan
 // ---------------------------------------------------------------------------
-// Operands of one chunk for one wavefront (token rows 16 wave .. + 15), loaded
-// one chunk ahead so that their memory latency overlaps the current chunk.
-struct ChunkOperands {
-    u32x4 w[kD / 16];        // W rows, split pairs (four key columns each)
-    u32x4 p[kC / 16];        // Pm rows (blocks above the diagonal unused)
-    u32x4 tb[kC / 16];       // Tb rows
-    u32x2 q[kD / 16];        // Q rows (bf16)
-    u32x2 v;                 // this thread's share of the chunk's V rows (staged to LDS)
-    u32x4 k[4];              // this thread's share of the chunk's K (staged to LDS)
-    float g;                 // gamma (threads 0..63) or d (threads 64..127) of token threadIdx % 64
+namespace {
+// Operands of one chunk for one wavefront (token block = wave; key blocks
+// 2 wave, 2 wave + 1), loaded one chunk ahead so that their memory latency
+// overlaps the current chunk.
+struct ScanOps {
+    u32x4 wh[4], wl[4];      // -W fragments, key groups 0..3
+    u32x4 ph[2], pl[2];      // Pm fragments, token groups 0, 1 (group 1: blocks 2, 3 only)
+    u32x4 q[4];              // Q row 16 wave + l%16, key groups 0..3, paired order
+    u32x4 kt[2][2];          // K^T fragments [key block 2 wave + i][token group]
+    f32x4 vt;                // Vt block [wave][value block]
+    f32x4 gam, dec;          // gamma_t and d_t of rows 16 wave + 4 (l/16) .. + 3
+    float gend;              // gamma_63
 };
 
-__device__ __forceinline__ void load_chunk(ChunkOperands& o, const GdnChunkArgs& a, int c, int h, int kh,
-                                           int wave, int tl, int ks, int iv) {
+__device__ __forceinline__ void load_ops(ScanOps& o, const GdnChunkArgs& a, int nch, int c, int h, int kh,
+                                         int rb, int wave, int lane) {
     const int t0 = a.t0 + c * kC;
     const int nt = min(kC, a.t0 + a.nt - t0);
-    const float* ws = a.ws + ((size_t)c * a.Hv + h) * kGdnChunkFloats;
-    const uint16_t* wW = reinterpret_cast<const uint16_t*>(ws);
-    const uint16_t* wP = reinterpret_cast<const uint16_t*>(ws + kC * kD);
-    const uint16_t* wT = reinterpret_cast<const uint16_t*>(ws + kC * kD + kC * kC);
-    const float* wG = ws + kC * kD + 2 * kC * kC;
-    const int tw = 16 * wave + tl;
+    const int g4 = lane >> 4, ln = lane & 15;
+    const float* hb = head_block(a, c, h);
+    const u32x4* wf = reinterpret_cast<const u32x4*>(hb + kOffW);
 #pragma unroll
-    for (int jb = 0; jb < kD / 16; ++jb)
-        o.w[jb] = *reinterpret_cast<const u32x4*>(wW + ((size_t)tw * (kD / 4) + (16 * jb + ks) / 4) * 8);
-#pragma unroll
-    for (int sb = 0; sb < kC / 16; ++sb) {
-        const size_t gi = ((size_t)tw * (kC / 4) + (16 * sb + ks) / 4) * 8;
-        o.p[sb] = (sb <= wave) ? *reinterpret_cast<const u32x4*>(wP + gi) : u32x4{0u, 0u, 0u, 0u};
-        o.tb[sb] = *reinterpret_cast<const u32x4*>(wT + gi);
+    for (int p = 0; p < 4; ++p) {
+        o.wh[p] = wf[(wave * 4 + p) * 128 + lane];
+        o.wl[p] = wf[(wave * 4 + p) * 128 + 64 + lane];
     }
-    const bool qok = tw < nt;
-    const uint16_t* qrow = a.q + ((size_t)(t0 + (qok ? tw : 0)) * a.Hk + kh) * kD;
+    const u32x4* pf = reinterpret_cast<const u32x4*>(hb + kOffP);
+    // (every load is unconditional: token group 1 of blocks 0, 1 is never written
+    // and never used; Q rows past the sequence repeat its last row, whose outputs
+    // go to the sink)
 #pragma unroll
-    for (int jb = 0; jb < kD / 16; ++jb)
-        o.q[jb] = qok ? *reinterpret_cast<const u32x2*>(qrow + 16 * jb + ks) : u32x2{0u, 0u};
-    {
-        // V of the workgroup's 16 value rows: token threadIdx / 4, rows 4 (threadIdx % 4) .. + 3
-        const int t = threadIdx.x >> 2, m = threadIdx.x & 3;
-        o.v = (t < nt) ? *reinterpret_cast<const u32x2*>(a.v + ((size_t)(t0 + t) * a.Hv + h) * kD + (iv - tl) + 4 * m)
-                       : u32x2{0u, 0u};
+    for (int p = 0; p < 2; ++p) {
+        o.ph[p] = pf[(wave * 2 + p) * 128 + lane];
+        o.pl[p] = pf[(wave * 2 + p) * 128 + 64 + lane];
     }
+    const int tq = min(16 * wave + ln, nt - 1);
+    const uint16_t* qrow = a.q + ((size_t)(t0 + tq) * a.Hk + kh) * kD + 4 * g4;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = threadIdx.x + u * 256;           // 1024 pieces of 8 bf16: token i / 16, columns 8 (i % 16)
-        const int t = i >> 4, j = (i & 15) * 8;
-        o.k[u] = (t < nt) ? load_u32x4(a.k + ((size_t)(t0 + t) * a.Hk + kh) * kD + j) : u32x4{0u, 0u, 0u, 0u};
-    }
-    o.g = (threadIdx.x < 2 * kC) ? wG[threadIdx.x] : 0.f;
+    for (int p = 0; p < 4; ++p)
+        o.q[p] = cat(*reinterpret_cast<const u32x2*>(qrow + 32 * p), *reinterpret_cast<const u32x2*>(qrow + 32 * p + 16));
+    const u32x4* kf = reinterpret_cast<const u32x4*>(key_block(a, nch, c, kh));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) o.kt[i][p] = kf[((2 * wave + i) * 2 + p) * 64 + lane];
+    o.vt = reinterpret_cast<const f32x4*>(hb + kOffV)[(wave * 8 + rb) * 64 + lane];
+    o.gam = *reinterpret_cast<const f32x4*>(hb + kOffG + 16 * wave + 4 * g4);
+    o.dec = *reinterpret_cast<const f32x4*>(hb + kOffG + kC + 16 * wave + 4 * g4);
+    o.gend = hb[kOffG + kC - 1];
 }
+}  // namespace
 
 __global__ __launch_bounds__(256) void k_gdn_chunk_scan(GdnChunkArgs a) {
-    __shared__ __attribute__((aligned(16))) u32x4 s_s[kD / 16][kWave];     // S^T blocks, split pairs
-    __shared__ __attribute__((aligned(16))) u32x4 s_us[kC / 16][kWave];    // U blocks, split pairs
-    __shared__ __attribute__((aligned(16))) u32x4 s_du[kC / 16][kWave];    // d U blocks, split pairs
-    __shared__ __attribute__((aligned(16))) uint16_t s_kt[2][kD][kC + 4];  // K transposed, two chunks
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kRB][kC + 4]; // V rows transposed, two chunks
-    __shared__ float s_g[2][2 * kC];                                          // gamma, then d
+    __shared__ __attribute__((aligned(16))) u32x4 s_sh[4][kWave], s_sl[4][kWave];   // S^T key groups, split
+    __shared__ __attribute__((aligned(16))) u32x2 s_uh[4][kWave], s_ul[4][kWave];   // U blocks, split
+    __shared__ __attribute__((aligned(16))) u32x2 s_dh[4][kWave], s_dl[4][kWave];   // d U blocks, split
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    const int g4 = lane >> 4, ln = lane & 15;
     const int h = blockIdx.x % a.Hv;
-    const int i0 = (blockIdx.x / a.Hv) * kRB;
+    const int rb = blockIdx.x / a.Hv;
     const int kh = h / a.rep;
-    const int tl = lane & 15, ks = (lane >> 4) * 4;
-    const int iv = i0 + tl;                       // this lane's value row
-    float* state = a.state + (size_t)h * kD * kD;
-    auto split_pack = [](const f32x4& x) {
-        const Split4 sp = split4(x);
-        const u32x2 hi = __builtin_bit_cast(u32x2, sp.hi), lo = __builtin_bit_cast(u32x2, sp.lo);
-        return u32x4{hi.x, hi.y, lo.x, lo.y};
-    };
-    auto unpack = [](const u32x4& v) {
-        Split4 r;
-        r.hi = __builtin_bit_cast(s16x4, u32x2{v.x, v.y});
-        r.lo = __builtin_bit_cast(s16x4, u32x2{v.z, v.w});
-        return r;
-    };
-    auto stage = [&](const ChunkOperands& o, int buf) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = threadIdx.x + u * 256;
-            const int t = i >> 4, j = (i & 15) * 8;
-            const uint32_t kw[4] = {o.k[u].x, o.k[u].y, o.k[u].z, o.k[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s_kt[buf][j + 2 * e][t] = (uint16_t)(kw[e] & 0xFFFFu);
-                s_kt[buf][j + 2 * e + 1][t] = (uint16_t)(kw[e] >> 16);
-            }
-        }
-        {
-            const int t = threadIdx.x >> 2, m = threadIdx.x & 3;
-            s_vt[buf][4 * m][t] = (uint16_t)(o.v.x & 0xFFFFu);
-            s_vt[buf][4 * m + 1][t] = (uint16_t)(o.v.x >> 16);
-            s_vt[buf][4 * m + 2][t] = (uint16_t)(o.v.y & 0xFFFFu);
-            s_vt[buf][4 * m + 3][t] = (uint16_t)(o.v.y >> 16);
-        }
-        if (threadIdx.x < 2 * kC) s_g[buf][threadIdx.x] = o.g;
-    };
+    const int iv = kRB * rb + ln;                 // this lane's value row
+    const int nch = (a.nt + kC - 1) / kC;
+    float* state = a.state + ((size_t)h * kD + iv) * kD;
+    uint16_t* sink = reinterpret_cast<uint16_t*>(a.ws + (size_t)nch * ((size_t)a.Hv * kHeadWords + (size_t)a.Hk * kKeyWords));
 
-    // S^T blocks jb = 2 wave, 2 wave + 1: lane holds S[iv][16 jb + ks .. + 3]
+    // S^T key blocks 2 wave, 2 wave + 1: lane holds S[iv][32 wave + 16 i + 4 g4 + r]
     f32x4 sm[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int jb = 2 * wave + q;
-        const float4 v = *reinterpret_cast<const float4*>(state + (size_t)iv * kD + 16 * jb + ks);
-        sm[q] = f32x4{v.x, v.y, v.z, v.w};
-        s_s[jb][lane] = split_pack(sm[q]);
+    for (int i = 0; i < 2; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(state + 32 * wave + 16 * i + 4 * g4);
+        sm[i] = f32x4{v.x, v.y, v.z, v.w};
     }
+    auto publish = [&]() {        // this wavefront's key group as a split B operand
+        const Split8 sp = split8(sm[0], sm[1]);
+        s_sh[wave][lane] = sp.hi;
+        s_sl[wave][lane] = sp.lo;
+    };
+    publish();
 
-    const int nch = (a.nt + kC - 1) / kC;
-    ChunkOperands cur, nxt;
-    load_chunk(cur, a, 0, h, kh, wave, tl, ks, iv);
-    stage(cur, 0);
-    for (int c = 0; c < nch; ++c) {
-        const int buf = c & 1;
+    auto step = [&](const ScanOps& cur, ScanOps& nxt, int c) {
         const int t0 = a.t0 + c * kC;
         const int nt = min(kC, a.t0 + a.nt - t0);
-        if (c + 1 < nch) load_chunk(nxt, a, c + 1, h, kh, wave, tl, ks, iv);   // in flight during this chunk
-        __syncthreads();          // this chunk's K and G are staged; the state blocks are current
+        load_ops(nxt, a, nch, min(c + 1, nch - 1), h, kh, rb, wave, lane);      // in flight during this chunk
+        __syncthreads();          // the state's key groups are current
 
-        // U = Tb V - W S^T and QS = Q S^T for token rows 16 wave .. + 15, as five
-        // independent accumulation chains
-        f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = u0, u2 = u0, q0 = u0, q1 = u0;
+        // U = Vt - W S^T and QS = Q S^T for token block `wave`, five chains
+        f32x4 a1 = cur.vt, a2 = {0.f, 0.f, 0.f, 0.f}, a3 = a2, q1 = a2, q2 = a2;
 #pragma unroll
-        for (int sb = 0; sb < kC / 16; ++sb)
-            u0 = mma2(unpack(cur.tb[sb]), load_bf16x4(&s_vt[buf][tl][16 * sb + ks]), u0);
-#pragma unroll
-        for (int jb = 0; jb < kD / 16; jb += 2) {
-            const Split4 sa = unpack(s_s[jb][lane]), sb = unpack(s_s[jb + 1][lane]);
-            u1 = mma3(neg(unpack(cur.w[jb])), sa, u1);
-            u2 = mma3(neg(unpack(cur.w[jb + 1])), sb, u2);
-            q0 = mma2(__builtin_bit_cast(s16x4, cur.q[jb]), sa, q0);
-            q1 = mma2(__builtin_bit_cast(s16x4, cur.q[jb + 1]), sb, q1);
+        for (int p = 0; p < 4; ++p) {
+            const u32x4 sh = s_sh[p][lane], sl = s_sl[p][lane];
+            a1 = mfma32(cur.wh[p], sh, a1);
+            q1 = mfma32(cur.q[p], sh, q1);
+            a2 = mfma32(cur.wh[p], sl, a2);
+            q2 = mfma32(cur.q[p], sl, q2);
+            a3 = mfma32(cur.wl[p], sh, a3);
         }
-        f32x4 u, qs, du;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            u[r] = u0[r] + (u1[r] + u2[r]);
-            qs[r] = q0[r] + q1[r];
-            du[r] = u[r] * s_g[buf][kC + 16 * wave + ks + r];
-        }
-        s_us[wave][lane] = split_pack(u);
-        s_du[wave][lane] = split_pack(du);
-        __syncthreads();          // every U block written; every state block read
+        const f32x4 u = a1 + (a2 + a3), qs = q1 + q2;
+        const Half4 us = split4(u), ds = split4(u * cur.dec);
+        s_uh[wave][lane] = us.hi;
+        s_ul[wave][lane] = us.lo;
+        s_dh[wave][lane] = ds.hi;
+        s_dl[wave][lane] = ds.lo;
+        __syncthreads();          // every U block written; every key group read
 
-        // O = Gamma QS + Pm U for this wavefront's token rows
-        f32x4 o;
+        // O = Gamma QS + Pm U over token groups p <= wave / 2
+        f32x4 o1 = cur.gam * qs, o2 = {0.f, 0.f, 0.f, 0.f}, o3 = o2;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = s_g[buf][16 * wave + ks + r] * qs[r];
-#pragma unroll
-        for (int sb = 0; sb < kC / 16; ++sb)
-            if (sb <= wave) o = mma3(unpack(cur.p[sb]), unpack(s_us[sb][lane]), o);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wave + ks + r;
-            if (t < nt) a.out[((size_t)(t0 + t) * a.Hv + h) * kD + iv] = (uint16_t)f32_to_bf16(o[r]);
+        for (int p = 0; p < 2; ++p) {
+            if (2 * p > wave) continue;
+            const u32x4 uh = cat(s_uh[2 * p][lane], s_uh[2 * p + 1][lane]);
+            const u32x4 ul = cat(s_ul[2 * p][lane], s_ul[2 * p + 1][lane]);
+            o1 = mfma32(cur.ph[p], uh, o1);
+            o2 = mfma32(cur.ph[p], ul, o2);
+            o3 = mfma32(cur.pl[p], uh, o3);
         }
         // S^T <- gamma_63 S^T + K^T diag(d) U on key blocks 2 wave, 2 wave + 1
-        const float gend = s_g[buf][kC - 1];
+        f32x4 s0 = cur.gend * sm[0], s1 = cur.gend * sm[1], s0l = {0.f, 0.f, 0.f, 0.f}, s1l = s0l;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int jb = 2 * wave + q;
-            f32x4 acc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = gend * sm[q][r];
-#pragma unroll
-            for (int tb = 0; tb < kC / 16; ++tb)
-                acc = mma2(load_bf16x4(&s_kt[buf][16 * jb + tl][16 * tb + ks]), unpack(s_du[tb][lane]), acc);
-            sm[q] = acc;
-            s_s[jb][lane] = split_pack(acc);   // read after the next chunk's first barrier
+        for (int p = 0; p < 2; ++p) {
+            const u32x4 dh = cat(s_dh[2 * p][lane], s_dh[2 * p + 1][lane]);
+            const u32x4 dl = cat(s_dl[2 * p][lane], s_dl[2 * p + 1][lane]);
+            s0 = mfma32(cur.kt[0][p], dh, s0);
+            s1 = mfma32(cur.kt[1][p], dh, s1);
+            s0l = mfma32(cur.kt[0][p], dl, s0l);
+            s1l = mfma32(cur.kt[1][p], dl, s1l);
         }
-        if (c + 1 < nch) {
-            stage(nxt, buf ^ 1);               // the other buffer: last read two barriers ago
-            cur = nxt;
+        sm[0] = s0 + s0l;
+        sm[1] = s1 + s1l;
+        publish();                // read after the next chunk's first barrier
+        const f32x4 o = o1 + (o2 + o3);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * wave + 4 * g4 + r;
+            uint16_t* dst = (t < nt) ? a.out + ((size_t)(t0 + t) * a.Hv + h) * kD + iv : sink;
+            *dst = (uint16_t)f32_to_bf16(o[r]);
         }
+    };
+
+    ScanOps A, B;
+    load_ops(A, a, nch, 0, h, kh, rb, wave, lane);
+    for (int c = 0; c < nch; c += 2) {
+        step(A, B, c);
+        if (c + 1 < nch) step(B, A, c + 1);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int jb = 2 * wave + q;
-        *reinterpret_cast<float4*>(state + (size_t)iv * kD + 16 * jb + ks) =
-            float4{sm[q][0], sm[q][1], sm[q][2], sm[q][3]};
-    }
+    for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<float4*>(state + 32 * wave + 16 * i + 4 * g4) = float4{sm[i][0], sm[i][1], sm[i][2], sm[i][3]};
 }
 
-size_t gdn_chunked_workspace_floats(int T, int Hv) {
+size_t gdn_chunked_workspace_floats(int T, int Hv, int Hk) {
     const int seg = T < kGdnSegT ? T : kGdnSegT;
-    return (size_t)((seg + kC - 1) / kC) * (size_t)Hv * kGdnChunkFloats;
+    const size_t nch = (size_t)((seg + kC - 1) / kC);
+    return nch * ((size_t)Hv * kHeadWords + (size_t)Hk * kKeyWords) + kSinkWords;
 }
 
 hipError_t launch_gdn_chunked(const GdnChunkArgs& base, hipStream_t st, KernelTimer& tm) {

@@ -122,7 +122,7 @@ struct GdnArgs {
 // Chunked Gated DeltaNet scan (moe_w4_gdn_scan_chunked).  The sequence is
 // processed in segments of kGdnSegT tokens (chunks of 64), each a prep launch
 // over all its chunks and a scan launch; the state carries over in `state`.
-constexpr int kGdnSegT = 1024;
+constexpr int kGdnSegT = 2048;
 struct GdnChunkArgs {
     const uint16_t* q;       // bf16 [T][Hk][128]
     const uint16_t* k;
@@ -131,7 +131,7 @@ struct GdnChunkArgs {
     const float* beta;       // [T][Hv]
     float* state;            // [Hv][128][128]
     uint16_t* out;           // bf16 [T][Hv][128]
-    float* ws;               // per (chunk, value head): W, Pm, Tb, gamma, d of one segment
+    float* ws;               // per chunk: operand fragments of one segment
     int T, Hv, Hk, rep;
     int t0, nt;              // segment: first token, tokens
 };
@@ -172,6 +172,6 @@ hipError_t launch_block_decode(const DecodeBlockArgs& a, hipStream_t st, KernelT
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_gdn_scan(const GdnArgs& a, hipStream_t st, KernelTimer& tm);
 hipError_t launch_gdn_chunked(const GdnChunkArgs& a, hipStream_t st, KernelTimer& tm);
-size_t gdn_chunked_workspace_floats(int T, int Hv);
+size_t gdn_chunked_workspace_floats(int T, int Hv, int Hk);
 
 }  // namespace moe_w4

@@ -533,7 +533,7 @@ int gdn_dims_status(const moe_w4_gdn_dims* dims) {
 
 size_t moe_w4_gdn_chunked_workspace_bytes(const moe_w4_gdn_dims* dims) {
     if (gdn_dims_status(dims) != MOE_W4_OK) return 0;
-    return moe_w4::gdn_chunked_workspace_floats(dims->T, dims->n_v_heads) * sizeof(float);
+    return moe_w4::gdn_chunked_workspace_floats(dims->T, dims->n_v_heads, dims->n_k_heads) * sizeof(float);
 }
 
 int moe_w4_gdn_scan_chunked_timed(const moe_w4_gdn_dims* dims, const void* q, const void* k,
