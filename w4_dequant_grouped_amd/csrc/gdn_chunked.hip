@@ -51,10 +51,7 @@ constexpr int kRB = 16;           // value rows per scan workgroup
 //   Pm  fragments [token block 4][token group 2]  same format (group 1 only for blocks 2, 3)
 //   Vt  fragments [token block 4][value block 8]  64 lanes x 4 floats, result layout
 //   gamma [64], d [64]
-// then per (chunk, key head): K^T fragments [key block 8][token group 2], 64 lanes x 8 bf16,
-// and last a 64-word sink for the scan's stores of rows past the sequence (so
-// that every lane stores and the memory counters it waits on are the same on
-// every chunk).
+// then per (chunk, key head): K^T fragments [key block 8][token group 2], 64 lanes x 8 bf16.
 constexpr int kFragSplit = 512;                       // words of a split fragment
 constexpr int kOffW = 0;
 constexpr int kOffP = kOffW + 16 * kFragSplit;
@@ -62,7 +59,6 @@ constexpr int kOffV = kOffP + 8 * kFragSplit;
 constexpr int kOffG = kOffV + 32 * 256;
 constexpr int kHeadWords = kOffG + 2 * kC;            // 20608
 constexpr int kKeyWords = 16 * 256;                   // 4096
-constexpr int kSinkWords = 64;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -401,8 +397,8 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 // Operands of one chunk for one wavefront (token block = wave; key blocks
-// 2 wave, 2 wave + 1), loaded one chunk ahead so that their memory latency
-// overlaps the current chunk.
+// 2 wave, 2 wave + 1), loaded two chunks ahead so that their memory latency
+// (the prep kernel's output, mostly out of the L2) overlaps two chunks of work.
 struct ScanOps {
     u32x4 wh[4], wl[4];      // -W fragments, key groups 0..3
     u32x4 ph[2], pl[2];      // Pm fragments, token groups 0, 1 (group 1: blocks 2, 3 only)
@@ -413,41 +409,66 @@ struct ScanOps {
     float gend;              // gamma_63
 };
 
-__device__ __forceinline__ void load_ops(ScanOps& o, const GdnChunkArgs& a, int nch, int c, int h, int kh,
-                                         int rb, int wave, int lane) {
-    const int t0 = a.t0 + c * kC;
-    const int nt = min(kC, a.t0 + a.nt - t0);
-    const int g4 = lane >> 4, ln = lane & 15;
-    const float* hb = head_block(a, c, h);
-    const u32x4* wf = reinterpret_cast<const u32x4*>(hb + kOffW);
+// Buffer resources of the segment and this lane's fixed byte offsets.  Chunk-
+// dependent parts of workspace addresses go to the scalar offset.  Q and the
+// output keep the whole offset in the lane's register, which the range check
+// covers: a raw buffer access at or past num_records reads zero and stores
+// nothing, and that handles the rows past the sequence in the last chunk.
+struct ScanMem {
+    __amdgpu_buffer_rsrc_t ws, q, out;
+    int vw, vp, vq, vk, vv, vg;          // -W, Pm, Q, K^T, Vt, gamma
+    int vo[4];                           // output rows 16 wave + 4 (l/16) + r
+    int head_base;                       // this head's block within a chunk (the lane offsets include it)
+    int head_stride, key_base, key_stride, q_stride, o_stride;   // bytes
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, int v, int s) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0);
+}
+__device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, int v, int s) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, v, s, 0);
+}
+
+// Part 1: the -W fragments; part 2: Pm and Q; part 3: K^T, Vt and the decays.
+// The scan issues the three parts in different phases of a chunk, so that no
+// phase waits behind the whole set of loads.
+template <int Part>
+__device__ __forceinline__ void load_ops(ScanOps& o, const ScanMem& m, int c) {
+    const int hoff = c * m.head_stride;
+    if constexpr (Part == 1) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        o.wh[p] = wf[(wave * 4 + p) * 128 + lane];
-        o.wl[p] = wf[(wave * 4 + p) * 128 + 64 + lane];
+        for (int p = 0; p < 4; ++p) {
+            o.wh[p] = ld16(m.ws, m.vw, hoff + 4 * kOffW + 2048 * p);
+            o.wl[p] = ld16(m.ws, m.vw + 1024, hoff + 4 * kOffW + 2048 * p);
+        }
     }
-    const u32x4* pf = reinterpret_cast<const u32x4*>(hb + kOffP);
-    // (every load is unconditional: token group 1 of blocks 0, 1 is never written
-    // and never used; Q rows past the sequence repeat its last row, whose outputs
-    // go to the sink)
+    if constexpr (Part == 2) {
+        // token group 1 of blocks 0, 1 is never written and never used
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        o.ph[p] = pf[(wave * 2 + p) * 128 + lane];
-        o.pl[p] = pf[(wave * 2 + p) * 128 + 64 + lane];
+        for (int p = 0; p < 2; ++p) {
+            o.ph[p] = ld16(m.ws, m.vp, hoff + 4 * kOffP + 2048 * p);
+            o.pl[p] = ld16(m.ws, m.vp + 1024, hoff + 4 * kOffP + 2048 * p);
+        }
+        const int qoff = c * kC * m.q_stride;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) o.q[p] = cat(ld8(m.q, m.vq + qoff + 64 * p, 0), ld8(m.q, m.vq + qoff + 64 * p + 32, 0));
     }
-    const int tq = min(16 * wave + ln, nt - 1);
-    const uint16_t* qrow = a.q + ((size_t)(t0 + tq) * a.Hk + kh) * kD + 4 * g4;
+    if constexpr (Part == 3) {
+        const int koff = m.key_base + c * m.key_stride;
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-        o.q[p] = cat(*reinterpret_cast<const u32x2*>(qrow + 32 * p), *reinterpret_cast<const u32x2*>(qrow + 32 * p + 16));
-    const u32x4* kf = reinterpret_cast<const u32x4*>(key_block(a, nch, c, kh));
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int p = 0; p < 2; ++p) o.kt[i][p] = kf[((2 * wave + i) * 2 + p) * 64 + lane];
-    o.vt = reinterpret_cast<const f32x4*>(hb + kOffV)[(wave * 8 + rb) * 64 + lane];
-    o.gam = *reinterpret_cast<const f32x4*>(hb + kOffG + 16 * wave + 4 * g4);
-    o.dec = *reinterpret_cast<const f32x4*>(hb + kOffG + kC + 16 * wave + 4 * g4);
-    o.gend = hb[kOffG + kC - 1];
+            for (int p = 0; p < 2; ++p) o.kt[i][p] = ld16(m.ws, m.vk, koff + 1024 * (2 * i + p));
+        o.vt = __builtin_bit_cast(f32x4, ld16(m.ws, m.vv, hoff + 4 * kOffV));
+        o.gam = __builtin_bit_cast(f32x4, ld16(m.ws, m.vg, hoff + 4 * kOffG));
+        o.dec = __builtin_bit_cast(f32x4, ld16(m.ws, m.vg, hoff + 4 * (kOffG + kC)));
+        o.gend = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               m.ws, 0, m.head_base + hoff + 4 * (kOffG + kC - 1), 0));
+    }
 }
 }  // namespace
 
@@ -464,7 +485,26 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_scan(GdnChunkArgs a) {
     const int iv = kRB * rb + ln;                 // this lane's value row
     const int nch = (a.nt + kC - 1) / kC;
     float* state = a.state + ((size_t)h * kD + iv) * kD;
-    uint16_t* sink = reinterpret_cast<uint16_t*>(a.ws + (size_t)nch * ((size_t)a.Hv * kHeadWords + (size_t)a.Hk * kKeyWords));
+
+    ScanMem m;
+    m.head_stride = a.Hv * kHeadWords * 4;
+    m.key_stride = a.Hk * kKeyWords * 4;
+    m.key_base = nch * m.head_stride + kh * kKeyWords * 4;
+    m.q_stride = a.Hk * kD * 2;
+    m.o_stride = a.Hv * kD * 2;
+    m.ws = make_rsrc(a.ws, (uint32_t)nch * (uint32_t)(m.head_stride + m.key_stride));
+    m.q = make_rsrc(a.q + (size_t)a.t0 * a.Hk * kD, (uint32_t)a.nt * m.q_stride);
+    m.out = make_rsrc(a.out + (size_t)a.t0 * a.Hv * kD, (uint32_t)a.nt * m.o_stride);
+    const int hb0 = h * kHeadWords * 4;
+    m.head_base = hb0;
+    m.vw = hb0 + (wave * 4 * 128 + lane) * 16;
+    m.vp = hb0 + (wave * 2 * 128 + lane) * 16;
+    m.vq = (16 * wave + ln) * m.q_stride + kh * kD * 2 + 8 * g4;
+    m.vk = (4 * wave * 64 + lane) * 16;
+    m.vv = hb0 + ((wave * 8 + rb) * 64 + lane) * 16;
+    m.vg = hb0 + (16 * wave + 4 * g4) * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m.vo[r] = (16 * wave + 4 * g4 + r) * m.o_stride + h * kD * 2 + 2 * iv;
 
     // S^T key blocks 2 wave, 2 wave + 1: lane holds S[iv][32 wave + 16 i + 4 g4 + r]
     f32x4 sm[2];
@@ -481,70 +521,74 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_scan(GdnChunkArgs a) {
     publish();
 
     auto step = [&](const ScanOps& cur, ScanOps& nxt, int c) {
-        const int t0 = a.t0 + c * kC;
-        const int nt = min(kC, a.t0 + a.nt - t0);
-        load_ops(nxt, a, nch, min(c + 1, nch - 1), h, kh, rb, wave, lane);      // in flight during this chunk
+        const int cn = min(c + 2, nch - 1);       // operands in flight for two chunks
+        load_ops<1>(nxt, m, cn);
         __syncthreads();          // the state's key groups are current
 
-        // U = Vt - W S^T and QS = Q S^T for token block `wave`, five chains
-        f32x4 a1 = cur.vt, a2 = {0.f, 0.f, 0.f, 0.f}, a3 = a2, q1 = a2, q2 = a2;
+        // U = Vt - W S^T and QS = Q S^T for token block `wave`
+        f32x4 u = cur.vt, qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const u32x4 sh = s_sh[p][lane], sl = s_sl[p][lane];
-            a1 = mfma32(cur.wh[p], sh, a1);
-            q1 = mfma32(cur.q[p], sh, q1);
-            a2 = mfma32(cur.wh[p], sl, a2);
-            q2 = mfma32(cur.q[p], sl, q2);
-            a3 = mfma32(cur.wl[p], sh, a3);
+            u = mfma32(cur.wh[p], sh, u);
+            qs = mfma32(cur.q[p], sh, qs);
+            u = mfma32(cur.wh[p], sl, u);
+            qs = mfma32(cur.q[p], sl, qs);
+            u = mfma32(cur.wl[p], sh, u);
         }
-        const f32x4 u = a1 + (a2 + a3), qs = q1 + q2;
+        load_ops<2>(nxt, m, cn);
         const Half4 us = split4(u), ds = split4(u * cur.dec);
         s_uh[wave][lane] = us.hi;
         s_ul[wave][lane] = us.lo;
         s_dh[wave][lane] = ds.hi;
         s_dl[wave][lane] = ds.lo;
         __syncthreads();          // every U block written; every key group read
+        load_ops<3>(nxt, m, cn);
 
-        // O = Gamma QS + Pm U over token groups p <= wave / 2
-        f32x4 o1 = cur.gam * qs, o2 = {0.f, 0.f, 0.f, 0.f}, o3 = o2;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            if (2 * p > wave) continue;
-            const u32x4 uh = cat(s_uh[2 * p][lane], s_uh[2 * p + 1][lane]);
-            const u32x4 ul = cat(s_ul[2 * p][lane], s_ul[2 * p + 1][lane]);
-            o1 = mfma32(cur.ph[p], uh, o1);
-            o2 = mfma32(cur.ph[p], ul, o2);
-            o3 = mfma32(cur.pl[p], uh, o3);
-        }
+        // O = Gamma QS + Pm U over token groups p <= wave / 2, and
         // S^T <- gamma_63 S^T + K^T diag(d) U on key blocks 2 wave, 2 wave + 1
-        f32x4 s0 = cur.gend * sm[0], s1 = cur.gend * sm[1], s0l = {0.f, 0.f, 0.f, 0.f}, s1l = s0l;
+        f32x4 o = cur.gam * qs, s0 = cur.gend * sm[0], s1 = cur.gend * sm[1];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const u32x4 dh = cat(s_dh[2 * p][lane], s_dh[2 * p + 1][lane]);
             const u32x4 dl = cat(s_dl[2 * p][lane], s_dl[2 * p + 1][lane]);
             s0 = mfma32(cur.kt[0][p], dh, s0);
             s1 = mfma32(cur.kt[1][p], dh, s1);
-            s0l = mfma32(cur.kt[0][p], dl, s0l);
-            s1l = mfma32(cur.kt[1][p], dl, s1l);
+            s0 = mfma32(cur.kt[0][p], dl, s0);
+            s1 = mfma32(cur.kt[1][p], dl, s1);
+            if (2 * p > wave) continue;
+            const u32x4 uh = cat(s_uh[2 * p][lane], s_uh[2 * p + 1][lane]);
+            const u32x4 ul = cat(s_ul[2 * p][lane], s_ul[2 * p + 1][lane]);
+            o = mfma32(cur.ph[p], uh, o);
+            o = mfma32(cur.ph[p], ul, o);
+            o = mfma32(cur.pl[p], uh, o);
         }
-        sm[0] = s0 + s0l;
-        sm[1] = s1 + s1l;
+        sm[0] = s0;
+        sm[1] = s1;
         publish();                // read after the next chunk's first barrier
-        const f32x4 o = o1 + (o2 + o3);
+        const int ooff = c * kC * m.o_stride;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wave + 4 * g4 + r;
-            uint16_t* dst = (t < nt) ? a.out + ((size_t)(t0 + t) * a.Hv + h) * kD + iv : sink;
-            *dst = (uint16_t)f32_to_bf16(o[r]);
-        }
+        for (int r = 0; r < 4; ++r)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16(o[r]), m.out, m.vo[r] + ooff, 0, 0);
     };
 
-    ScanOps A, B;
-    load_ops(A, a, nch, 0, h, kh, rb, wave, lane);
-    for (int c = 0; c < nch; c += 2) {
-        step(A, B, c);
-        if (c + 1 < nch) step(B, A, c + 1);
+    // three operand sets in rotation; the loop body has no conditional step, so
+    // every wait on the memory counter it compiles to is exact
+    ScanOps A, B, C;
+    load_ops<1>(A, m, 0);
+    load_ops<2>(A, m, 0);
+    load_ops<3>(A, m, 0);
+    load_ops<1>(B, m, min(1, nch - 1));
+    load_ops<2>(B, m, min(1, nch - 1));
+    load_ops<3>(B, m, min(1, nch - 1));
+    int c = 0;
+    for (; c + 3 <= nch; c += 3) {
+        step(A, C, c);
+        step(B, A, c + 1);
+        step(C, B, c + 2);
     }
+    if (c < nch) step(A, C, c);
+    if (c + 1 < nch) step(B, A, c + 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         *reinterpret_cast<float4*>(state + 32 * wave + 16 * i + 4 * g4) = float4{sm[i][0], sm[i][1], sm[i][2], sm[i][3]};
@@ -553,7 +597,7 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_scan(GdnChunkArgs a) {
 size_t gdn_chunked_workspace_floats(int T, int Hv, int Hk) {
     const int seg = T < kGdnSegT ? T : kGdnSegT;
     const size_t nch = (size_t)((seg + kC - 1) / kC);
-    return nch * ((size_t)Hv * kHeadWords + (size_t)Hk * kKeyWords) + kSinkWords;
+    return nch * ((size_t)Hv * kHeadWords + (size_t)Hk * kKeyWords);
 }
 
 hipError_t launch_gdn_chunked(const GdnChunkArgs& base, hipStream_t st, KernelTimer& tm) {
