@@ -183,8 +183,8 @@ def test_chunked_workspace_size_and_graph_replays():
     """The workspace the library asks for (one 2048-token segment at most), and
     three graph replays of a chunked call equal to the eager call bit for bit."""
     # per chunk: 20608 words per value head (-W, Pm and Vt fragments, gamma, d) and
-    # 4096 per key head (K^T fragments)
-    per_chunk = (32 * 20608 + 16 * 4096) * 4
+    # 8192 per key head (K^T and Q fragments)
+    per_chunk = (32 * 20608 + 16 * 8192) * 4
     assert B.moe_w4_gdn_chunked_workspace_bytes(1, 32, 16) == per_chunk
     assert B.moe_w4_gdn_chunked_workspace_bytes(5000, 32, 16) == 32 * per_chunk
     x = SG.draw_gdn(SG.GdnShape(T=200), 901).to("cuda")

@@ -44,21 +44,25 @@ namespace {
 
 constexpr int kC = 64;            // tokens per chunk
 constexpr int kD = 128;           // head dimension
-constexpr int kRB = 16;           // value rows per scan workgroup
+constexpr int kRB = 16;           // value rows per scan wavefront
+constexpr int kSub = 1;           // value-row blocks per scan workgroup (four wavefronts each)
+constexpr int kAhead = 2;         // chunks between an operand load and its use
 
 // Workspace, in 4-byte words.  Per (chunk, value head):
 //   -W  fragments [token block 4][key group 4]    2048 B each: 64 lanes x 16 B hi, then lo
 //   Pm  fragments [token block 4][token group 2]  same format (group 1 only for blocks 2, 3)
 //   Vt  fragments [token block 4][value block 8]  64 lanes x 4 floats, result layout
 //   gamma [64], d [64]
-// then per (chunk, key head): K^T fragments [key block 8][token group 2], 64 lanes x 8 bf16.
+// then per (chunk, key head): K^T fragments [key block 8][token group 2] and Q
+// fragments [token block 4][key group 4], 64 lanes x 8 bf16 each.
 constexpr int kFragSplit = 512;                       // words of a split fragment
 constexpr int kOffW = 0;
 constexpr int kOffP = kOffW + 16 * kFragSplit;
 constexpr int kOffV = kOffP + 8 * kFragSplit;
 constexpr int kOffG = kOffV + 32 * 256;
 constexpr int kHeadWords = kOffG + 2 * kC;            // 20608
-constexpr int kKeyWords = 16 * 256;                   // 4096
+constexpr int kOffQ = 16 * 256;                       // Q fragments within a key block
+constexpr int kKeyWords = 2 * 16 * 256;               // 8192
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -209,8 +213,9 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
     }
     __syncthreads();
 
-    // K^T fragments of the scan's state update (once per key head): key block jb,
-    // token group p, paired-block order
+    // K^T fragments of the scan's state update (key block jb, token group p) and
+    // Q fragments of its Q S^T (token block = wave, key group p), paired-block
+    // order, once per key head
     if (h % a.rep == 0) {
         u32x4* kf = reinterpret_cast<u32x4*>(key_block(a, nch, c, kh));
 #pragma unroll
@@ -222,6 +227,13 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
                 kf[(jb * 2 + p) * 64 + lane] = cat(*reinterpret_cast<const u32x2*>(row),
                                                    *reinterpret_cast<const u32x2*>(row + 16));
             }
+        u32x4* qf = reinterpret_cast<u32x4*>(key_block(a, nch, c, kh) + kOffQ);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint16_t* row = &s_q[16 * wave + ln][32 * p + 4 * g4];
+            qf[(wave * 4 + p) * 64 + lane] = cat(*reinterpret_cast<const u32x2*>(row),
+                                                 *reinterpret_cast<const u32x2*>(row + 16));
+        }
     }
 
     // K K^T and K Q^T as transposed blocks [s block sb][t block = wave]: lane holds
@@ -397,8 +409,8 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 // Operands of one chunk for one wavefront (token block = wave; key blocks
-// 2 wave, 2 wave + 1), loaded two chunks ahead so that their memory latency
-// (the prep kernel's output, mostly out of the L2) overlaps two chunks of work.
+// 2 wave, 2 wave + 1), loaded kAhead chunks ahead so that their memory latency
+// (the prep kernel's output, mostly out of the L2) overlaps the work between.
 struct ScanOps {
     u32x4 wh[4], wl[4];      // -W fragments, key groups 0..3
     u32x4 ph[2], pl[2];      // Pm fragments, token groups 0, 1 (group 1: blocks 2, 3 only)
@@ -410,16 +422,17 @@ struct ScanOps {
 };
 
 // Buffer resources of the segment and this lane's fixed byte offsets.  Chunk-
-// dependent parts of workspace addresses go to the scalar offset.  Q and the
-// output keep the whole offset in the lane's register, which the range check
-// covers: a raw buffer access at or past num_records reads zero and stores
-// nothing, and that handles the rows past the sequence in the last chunk.
+// dependent parts of workspace addresses go to the scalar offset.  The output
+// keeps the whole offset in the lane's register, which the range check covers: a
+// raw buffer store at or past num_records stores nothing, and that drops the
+// rows past the sequence in the last chunk.
 struct ScanMem {
-    __amdgpu_buffer_rsrc_t ws, q, out;
+    __amdgpu_buffer_rsrc_t ws, out;
+    const float* wsp;                    // the workspace again, for the one scalar read
     int vw, vp, vq, vk, vv, vg;          // -W, Pm, Q, K^T, Vt, gamma
     int vo[4];                           // output rows 16 wave + 4 (l/16) + r
     int head_base;                       // this head's block within a chunk (the lane offsets include it)
-    int head_stride, key_base, key_stride, q_stride, o_stride;   // bytes
+    int head_stride, key_base, key_stride, o_stride;   // bytes
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -433,54 +446,63 @@ __device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, int v, int s) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, v, s, 0);
 }
 
-// Part 1: the -W fragments; part 2: Pm and Q; part 3: K^T, Vt and the decays.
-// The scan issues the three parts in different phases of a chunk, so that no
-// phase waits behind the whole set of loads.
-template <int Part>
-__device__ __forceinline__ void load_ops(ScanOps& o, const ScanMem& m, int c) {
+// Loads of one chunk's operands in pieces; the scan issues them in three groups,
+// one per phase of a chunk.
+__device__ __forceinline__ void load_w(ScanOps& o, const ScanMem& m, int c, int p) {
+    const int off = c * m.head_stride + 4 * kOffW + 2048 * p;
+    o.wh[p] = ld16(m.ws, m.vw, off);
+    o.wl[p] = ld16(m.ws, m.vw + 1024, off);
+}
+__device__ __forceinline__ void load_q(ScanOps& o, const ScanMem& m, int c, int p) {
+    o.q[p] = ld16(m.ws, m.vq, m.key_base + c * m.key_stride + 4 * kOffQ + 1024 * p);
+}
+__device__ __forceinline__ void load_pm(ScanOps& o, const ScanMem& m, int c, int p) {
+    const int off = c * m.head_stride + 4 * kOffP + 2048 * p;
+    o.ph[p] = ld16(m.ws, m.vp, off);
+    o.pl[p] = ld16(m.ws, m.vp + 1024, off);
+}
+__device__ __forceinline__ void load_kt(ScanOps& o, const ScanMem& m, int c, int i) {
+    const int off = m.key_base + c * m.key_stride + 2048 * i;
+    o.kt[i][0] = ld16(m.ws, m.vk, off);
+    o.kt[i][1] = ld16(m.ws, m.vk, off + 1024);
+}
+__device__ __forceinline__ void load_misc(ScanOps& o, const ScanMem& m, int c) {
     const int hoff = c * m.head_stride;
-    if constexpr (Part == 1) {
+    o.vt = __builtin_bit_cast(f32x4, ld16(m.ws, m.vv, hoff + 4 * kOffV));
+    o.gam = __builtin_bit_cast(f32x4, ld16(m.ws, m.vg, hoff + 4 * kOffG));
+    o.dec = __builtin_bit_cast(f32x4, ld16(m.ws, m.vg, hoff + 4 * (kOffG + kC)));
+    // gamma_63 is the same for every lane: a scalar read, outside the vector
+    // memory counter (two chunks of vector loads already fill most of its range)
+    o.gend = m.wsp[(m.head_base + hoff) / 4 + kOffG + kC - 1];
+}
+__device__ __forceinline__ void load_ops(ScanOps& o, const ScanMem& m, int c) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            o.wh[p] = ld16(m.ws, m.vw, hoff + 4 * kOffW + 2048 * p);
-            o.wl[p] = ld16(m.ws, m.vw + 1024, hoff + 4 * kOffW + 2048 * p);
-        }
+    for (int p = 0; p < 4; ++p) {
+        load_w(o, m, c, p);
+        load_q(o, m, c, p);
     }
-    if constexpr (Part == 2) {
-        // token group 1 of blocks 0, 1 is never written and never used
+    load_pm(o, m, c, 0);
+    load_pm(o, m, c, 1);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            o.ph[p] = ld16(m.ws, m.vp, hoff + 4 * kOffP + 2048 * p);
-            o.pl[p] = ld16(m.ws, m.vp + 1024, hoff + 4 * kOffP + 2048 * p);
-        }
-        const int qoff = c * kC * m.q_stride;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) o.q[p] = cat(ld8(m.q, m.vq + qoff + 64 * p, 0), ld8(m.q, m.vq + qoff + 64 * p + 32, 0));
-    }
-    if constexpr (Part == 3) {
-        const int koff = m.key_base + c * m.key_stride;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int p = 0; p < 2; ++p) o.kt[i][p] = ld16(m.ws, m.vk, koff + 1024 * (2 * i + p));
-        o.vt = __builtin_bit_cast(f32x4, ld16(m.ws, m.vv, hoff + 4 * kOffV));
-        o.gam = __builtin_bit_cast(f32x4, ld16(m.ws, m.vg, hoff + 4 * kOffG));
-        o.dec = __builtin_bit_cast(f32x4, ld16(m.ws, m.vg, hoff + 4 * (kOffG + kC)));
-        o.gend = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                               m.ws, 0, m.head_base + hoff + 4 * (kOffG + kC - 1), 0));
-    }
+    for (int i = 0; i < 2; ++i) load_kt(o, m, c, i);
+    load_misc(o, m, c);
 }
 }  // namespace
 
-__global__ __launch_bounds__(256) void k_gdn_chunk_scan(GdnChunkArgs a) {
-    __shared__ __attribute__((aligned(16))) u32x4 s_sh[4][kWave], s_sl[4][kWave];   // S^T key groups, split
-    __shared__ __attribute__((aligned(16))) u32x2 s_uh[4][kWave], s_ul[4][kWave];   // U blocks, split
-    __shared__ __attribute__((aligned(16))) u32x2 s_dh[4][kWave], s_dl[4][kWave];   // d U blocks, split
+// Wavefront w + 4 sub takes token block w (and key blocks 2w, 2w + 1) of
+// value-row block kSub (workgroup / Hv) + sub.  One row block per workgroup
+// measured fastest: the operand fetch of a CU is limited by the requests it can
+// keep in flight, and a second row block doubles them without sharing them.
+__global__ __launch_bounds__(256 * kSub) void k_gdn_chunk_scan(GdnChunkArgs a) {
+    __shared__ __attribute__((aligned(16))) u32x4 s_sh[kSub][4][kWave], s_sl[kSub][4][kWave];   // S^T key groups, split
+    __shared__ __attribute__((aligned(16))) u32x2 s_uh[kSub][4][kWave], s_ul[kSub][4][kWave];   // U blocks, split
+    __shared__ __attribute__((aligned(16))) u32x2 s_dh[kSub][4][kWave], s_dl[kSub][4][kWave];   // d U blocks, split
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = (threadIdx.x / kWave) & 3;
+    const int sub = threadIdx.x / (4 * kWave);
     const int g4 = lane >> 4, ln = lane & 15;
     const int h = blockIdx.x % a.Hv;
-    const int rb = blockIdx.x / a.Hv;
+    const int rb = kSub * (blockIdx.x / a.Hv) + sub;
     const int kh = h / a.rep;
     const int iv = kRB * rb + ln;                 // this lane's value row
     const int nch = (a.nt + kC - 1) / kC;
@@ -490,16 +512,15 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_scan(GdnChunkArgs a) {
     m.head_stride = a.Hv * kHeadWords * 4;
     m.key_stride = a.Hk * kKeyWords * 4;
     m.key_base = nch * m.head_stride + kh * kKeyWords * 4;
-    m.q_stride = a.Hk * kD * 2;
     m.o_stride = a.Hv * kD * 2;
     m.ws = make_rsrc(a.ws, (uint32_t)nch * (uint32_t)(m.head_stride + m.key_stride));
-    m.q = make_rsrc(a.q + (size_t)a.t0 * a.Hk * kD, (uint32_t)a.nt * m.q_stride);
+    m.wsp = a.ws;
     m.out = make_rsrc(a.out + (size_t)a.t0 * a.Hv * kD, (uint32_t)a.nt * m.o_stride);
     const int hb0 = h * kHeadWords * 4;
     m.head_base = hb0;
     m.vw = hb0 + (wave * 4 * 128 + lane) * 16;
     m.vp = hb0 + (wave * 2 * 128 + lane) * 16;
-    m.vq = (16 * wave + ln) * m.q_stride + kh * kD * 2 + 8 * g4;
+    m.vq = (4 * wave * 64 + lane) * 16;
     m.vk = (4 * wave * 64 + lane) * 16;
     m.vv = hb0 + ((wave * 8 + rb) * 64 + lane) * 16;
     m.vg = hb0 + (16 * wave + 4 * g4) * 4;
@@ -515,53 +536,63 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_scan(GdnChunkArgs a) {
     }
     auto publish = [&]() {        // this wavefront's key group as a split B operand
         const Split8 sp = split8(sm[0], sm[1]);
-        s_sh[wave][lane] = sp.hi;
-        s_sl[wave][lane] = sp.lo;
+        s_sh[sub][wave][lane] = sp.hi;
+        s_sl[sub][wave][lane] = sp.lo;
     };
     publish();
 
     auto step = [&](const ScanOps& cur, ScanOps& nxt, int c) {
-        const int cn = min(c + 2, nch - 1);       // operands in flight for two chunks
-        load_ops<1>(nxt, m, cn);
+        const int cn = min(c + kAhead, nch - 1);  // operands in flight for kAhead chunks
+#pragma unroll
+        for (int p = 0; p < 4; ++p) load_w(nxt, m, cn, p);
         __syncthreads();          // the state's key groups are current
 
         // U = Vt - W S^T and QS = Q S^T for token block `wave`
         f32x4 u = cur.vt, qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const u32x4 sh = s_sh[p][lane], sl = s_sl[p][lane];
+            const u32x4 sh = s_sh[sub][p][lane], sl = s_sl[sub][p][lane];
             u = mfma32(cur.wh[p], sh, u);
             qs = mfma32(cur.q[p], sh, qs);
             u = mfma32(cur.wh[p], sl, u);
             qs = mfma32(cur.q[p], sl, qs);
             u = mfma32(cur.wl[p], sh, u);
         }
-        load_ops<2>(nxt, m, cn);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) load_q(nxt, m, cn, p);
+        // (token group 1 of Pm is used, and written, for token blocks 2, 3 only;
+        // the other wavefronts load it too, as a conditional load would make
+        // the compiler's waits on the memory counter conservative)
+        load_pm(nxt, m, cn, 0);
+        load_pm(nxt, m, cn, 1);
         const Half4 us = split4(u), ds = split4(u * cur.dec);
-        s_uh[wave][lane] = us.hi;
-        s_ul[wave][lane] = us.lo;
-        s_dh[wave][lane] = ds.hi;
-        s_dl[wave][lane] = ds.lo;
+        s_uh[sub][wave][lane] = us.hi;
+        s_ul[sub][wave][lane] = us.lo;
+        s_dh[sub][wave][lane] = ds.hi;
+        s_dl[sub][wave][lane] = ds.lo;
         __syncthreads();          // every U block written; every key group read
-        load_ops<3>(nxt, m, cn);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) load_kt(nxt, m, cn, i);
+        load_misc(nxt, m, cn);
 
         // O = Gamma QS + Pm U over token groups p <= wave / 2, and
         // S^T <- gamma_63 S^T + K^T diag(d) U on key blocks 2 wave, 2 wave + 1
         f32x4 o = cur.gam * qs, s0 = cur.gend * sm[0], s1 = cur.gend * sm[1];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const u32x4 dh = cat(s_dh[2 * p][lane], s_dh[2 * p + 1][lane]);
-            const u32x4 dl = cat(s_dl[2 * p][lane], s_dl[2 * p + 1][lane]);
+            const u32x4 dh = cat(s_dh[sub][2 * p][lane], s_dh[sub][2 * p + 1][lane]);
+            const u32x4 dl = cat(s_dl[sub][2 * p][lane], s_dl[sub][2 * p + 1][lane]);
             s0 = mfma32(cur.kt[0][p], dh, s0);
             s1 = mfma32(cur.kt[1][p], dh, s1);
             s0 = mfma32(cur.kt[0][p], dl, s0);
             s1 = mfma32(cur.kt[1][p], dl, s1);
-            if (2 * p > wave) continue;
-            const u32x4 uh = cat(s_uh[2 * p][lane], s_uh[2 * p + 1][lane]);
-            const u32x4 ul = cat(s_ul[2 * p][lane], s_ul[2 * p + 1][lane]);
-            o = mfma32(cur.ph[p], uh, o);
-            o = mfma32(cur.ph[p], ul, o);
-            o = mfma32(cur.pl[p], uh, o);
+            if (2 * p <= wave) {
+                const u32x4 uh = cat(s_uh[sub][2 * p][lane], s_uh[sub][2 * p + 1][lane]);
+                const u32x4 ul = cat(s_ul[sub][2 * p][lane], s_ul[sub][2 * p + 1][lane]);
+                o = mfma32(cur.ph[p], uh, o);
+                o = mfma32(cur.ph[p], ul, o);
+                o = mfma32(cur.pl[p], uh, o);
+            }
         }
         sm[0] = s0;
         sm[1] = s1;
@@ -572,23 +603,33 @@ __global__ __launch_bounds__(256) void k_gdn_chunk_scan(GdnChunkArgs a) {
             __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16(o[r]), m.out, m.vo[r] + ooff, 0, 0);
     };
 
-    // three operand sets in rotation; the loop body has no conditional step, so
-    // every wait on the memory counter it compiles to is exact
-    ScanOps A, B, C;
-    load_ops<1>(A, m, 0);
-    load_ops<2>(A, m, 0);
-    load_ops<3>(A, m, 0);
-    load_ops<1>(B, m, min(1, nch - 1));
-    load_ops<2>(B, m, min(1, nch - 1));
-    load_ops<3>(B, m, min(1, nch - 1));
+    // kAhead + 1 operand sets in rotation; the loop body has no conditional step,
+    // so every wait on the memory counter it compiles to is exact
     int c = 0;
-    for (; c + 3 <= nch; c += 3) {
-        step(A, C, c);
-        step(B, A, c + 1);
-        step(C, B, c + 2);
+    if constexpr (kAhead == 1) {
+        ScanOps A, B;
+        load_ops(A, m, 0);
+        for (; c + 2 <= nch; c += 2) {
+            step(A, B, c);
+            step(B, A, c + 1);
+        }
+        if (c < nch) step(A, B, c);
+    } else {
+        ScanOps A, B, C;
+        load_ops(A, m, 0);
+        load_ops(B, m, min(1, nch - 1));
+        // Drain the two chunks loaded here before the loop.  Without it the
+        // compiler merges this path's pending loads into the loop header and
+        // waits there for nearly every load of the previous chunk on each pass.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        for (; c + 3 <= nch; c += 3) {
+            step(A, C, c);
+            step(B, A, c + 1);
+            step(C, B, c + 2);
+        }
+        if (c < nch) step(A, C, c);
+        if (c + 1 < nch) step(B, A, c + 1);
     }
-    if (c < nch) step(A, C, c);
-    if (c + 1 < nch) step(B, A, c + 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         *reinterpret_cast<float4*>(state + 32 * wave + 16 * i + 4 * g4) = float4{sm[i][0], sm[i][1], sm[i][2], sm[i][3]};
@@ -612,7 +653,7 @@ hipError_t launch_gdn_chunked(const GdnChunkArgs& base, hipStream_t st, KernelTi
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         tm.before();
-        tm.launch(k_gdn_chunk_scan, dim3(a.Hv * (kD / kRB)), dim3(256), 0, st, a);
+        tm.launch(k_gdn_chunk_scan, dim3(a.Hv * (kD / kRB / kSub)), dim3(256 * kSub), 0, st, a);
         tm.after();
         err = hipGetLastError();
         if (err != hipSuccess) return err;
