@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_qv[kD * (kC + 8)];    // Q rows [64][136], then V^T [128][72]
     __shared__ __attribute__((aligned(16))) uint16_t s_kt[kD][kC + 8];       // K^T
     __shared__ __attribute__((aligned(16))) float s_a[kC][kC + 4];           // A, then Tinv
-    __shared__ __attribute__((aligned(16))) float s_g[kC], s_b[kC], s_bg[kC];
+    __shared__ __attribute__((aligned(16))) float s_g[kC], s_b[kC], s_bg[kC];   // s_g: G log2(e)
     uint16_t (*s_q)[kD + 8] = reinterpret_cast<uint16_t (*)[kD + 8]>(s_qv);
     uint16_t (*s_vt)[kC + 8] = reinterpret_cast<uint16_t (*)[kC + 8]>(s_qv);
 
@@ -167,49 +167,51 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
             const float v = __shfl_up(gv, o, kWave);
             if (lane >= o) gv += v;
         }
-        const float gam = expf(gv);
-        s_g[lane] = gv;
+        // decays as 2^(G log2 e) on the hardware exp2 (about one ulp, as expf)
+        const float g2 = gv * 1.4426950408889634f;
+        const float gam = __builtin_amdgcn_exp2f(g2);
+        s_g[lane] = g2;
         s_b[lane] = bv;
         s_bg[lane] = bv * gam;
         hb[kOffG + lane] = gam;
-        hb[kOffG + kC + lane] = expf(__shfl(gv, kC - 1, kWave) - gv);
+        hb[kOffG + kC + lane] = __builtin_amdgcn_exp2f(__shfl(g2, kC - 1, kWave) - g2);
     }
-    // Q and K rows (zero past the sequence)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = threadIdx.x + 256 * u;                 // token i / 16, columns 8 (i % 16) ..
-        const int t = i >> 4, j = (i & 15) * 8;
-        u32x4 kk = {0u, 0u, 0u, 0u}, qq = kk;
-        if (t < nt) {
-            const size_t off = ((size_t)(t0 + t) * a.Hk + kh) * kD + j;
-            kk = load_u32x4(a.k + off);
-            qq = load_u32x4(a.q + off);
-        }
-        *reinterpret_cast<u32x4*>(&s_k[t][j]) = kk;
-        *reinterpret_cast<u32x4*>(&s_q[t][j]) = qq;
-    }
-    // K^T to LDS now, V^T tiles to registers (written over Q once K Q^T is done):
-    // tile = tokens 4 tq .. +3, columns 4 cg .. +3
-    u32x2 vtile[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = threadIdx.x + 256 * u;
-        const int tq = i & 15, cg = i >> 4;
-        u32x2 kr[4], vr[4];
+    // K, Q and V of the chunk (zero past the sequence): each thread one unit of
+    // tokens 4 tq .. +3 and columns 8 cg .. +7, loaded once.  K rows and K^T and
+    // Q rows go to LDS; V^T stays in registers until K Q^T is done with Q's LDS.
+    u32x2 vtile[8];
+    {
+        const int tq = threadIdx.x & 15, cg = threadIdx.x >> 4;
+        u32x4 kr[4], qr[4], vr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * tq + r;
             const bool ok = t < nt;
-            kr[r] = ok ? *reinterpret_cast<const u32x2*>(a.k + ((size_t)(t0 + t) * a.Hk + kh) * kD + 4 * cg)
-                       : u32x2{0u, 0u};
-            vr[r] = ok ? *reinterpret_cast<const u32x2*>(a.v + ((size_t)(t0 + t) * a.Hv + h) * kD + 4 * cg)
-                       : u32x2{0u, 0u};
+            const size_t ko = ((size_t)(t0 + t) * a.Hk + kh) * kD + 8 * cg;
+            kr[r] = ok ? load_u32x4(a.k + ko) : u32x4{0u, 0u, 0u, 0u};
+            qr[r] = ok ? load_u32x4(a.q + ko) : u32x4{0u, 0u, 0u, 0u};
+            vr[r] = ok ? load_u32x4(a.v + ((size_t)(t0 + t) * a.Hv + h) * kD + 8 * cg) : u32x4{0u, 0u, 0u, 0u};
         }
-        u32x2 kc[4];
-        transpose4(kr, kc);
-        transpose4(vr, vtile[u]);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x2*>(&s_kt[4 * cg + d][4 * tq]) = kc[d];
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<u32x4*>(&s_k[4 * tq + r][8 * cg]) = kr[r];
+            *reinterpret_cast<u32x4*>(&s_q[4 * tq + r][8 * cg]) = qr[r];
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {          // columns 8 cg + 4 hf .. + 3
+            const u32x2 kh2[4] = {u32x2{kr[0][2 * hf], kr[0][2 * hf + 1]}, u32x2{kr[1][2 * hf], kr[1][2 * hf + 1]},
+                                  u32x2{kr[2][2 * hf], kr[2][2 * hf + 1]}, u32x2{kr[3][2 * hf], kr[3][2 * hf + 1]}};
+            const u32x2 vh2[4] = {u32x2{vr[0][2 * hf], vr[0][2 * hf + 1]}, u32x2{vr[1][2 * hf], vr[1][2 * hf + 1]},
+                                  u32x2{vr[2][2 * hf], vr[2][2 * hf + 1]}, u32x2{vr[3][2 * hf], vr[3][2 * hf + 1]}};
+            u32x2 kc[4], vc[4];
+            transpose4(kh2, kc);
+            transpose4(vh2, vc);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                *reinterpret_cast<u32x2*>(&s_kt[8 * cg + 4 * hf + d][4 * tq]) = kc[d];
+                vtile[4 * hf + d] = vc[d];
+            }
+        }
     }
     __syncthreads();
 
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = 16 * sb + 4 * g4 + r;
-                const float dec = (s <= t) ? expf(gt - s_g[s]) : 0.f;
+                const float dec = (s <= t) ? __builtin_amdgcn_exp2f(gt - s_g[s]) : 0.f;
                 av[r] = (s < t) ? bt * dec * kk[r] : 0.f;
                 pv[r] = dec * kq[r];
             }
@@ -282,12 +284,10 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
     }
     __syncthreads();          // A complete; Q no longer read
 
+    {
+        const int tq = threadIdx.x & 15, cg = threadIdx.x >> 4;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = threadIdx.x + 256 * u;
-        const int tq = i & 15, cg = i >> 4;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x2*>(&s_vt[4 * cg + d][4 * tq]) = vtile[u][d];
+        for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x2*>(&s_vt[8 * cg + d][4 * tq]) = vtile[d];
     }
 
     // Tinv level 1: wavefront w inverts its diagonal block I + A_ww by forward
