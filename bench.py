@@ -27,8 +27,9 @@ Other modes (their own JSON line):
                 key/value heads, head dim 128, 64-token blocks) at 32K, 64K and
                 128K tokens of context, 10 caches in rotation
   --gdn         the Gated DeltaNet scan (32 value heads over 16 query/key heads,
-                dimension 128): prefill T=512 and T=2048, and T=1 decode steps
-                over 30 layer states in rotation
+                dimension 128): prefill T=512 and T=2048 on the chunked MFMA form
+                (the register-resident scan timed beside it), and T=1 decode
+                steps of the register scan over 30 layer states in rotation
 """
 from __future__ import annotations
 
@@ -659,10 +660,31 @@ def run_attn(args, ev):
     return rows
 
 
+def gdn_chunked_scan_bytes(shape) -> int:
+    """Bytes the chunked scan kernel streams per launch: the operand fragments the
+    prep kernel wrote (per chunk and value head: -W 32 KiB, the six Pm fragments
+    on or below the diagonal 12 KiB, Vt 32 KiB, the decays 512 B; per chunk and
+    key head: K^T and Q fragments 32 KiB), the outputs, and the state in and out."""
+    T, Hv, Hk, d = shape.T, shape.n_v_heads, shape.n_k_heads, shape.dim
+    nch = (T + 63) // 64
+    return nch * (Hv * (32768 + 12288 + 32768 + 512) + Hk * 32768) + T * Hv * d * 2 + 2 * Hv * d * d * 4
+
+
+def gdn_prep_bytes(shape) -> int:
+    """Bytes the chunked form's prep kernel moves per launch: q, k, v, the decays
+    and write strengths in, the operand fragments out."""
+    T, Hv, Hk, d = shape.T, shape.n_v_heads, shape.n_k_heads, shape.dim
+    nch = (T + 63) // 64
+    return 2 * T * Hk * d * 2 + T * Hv * d * 2 + 2 * T * Hv * 4 + \
+        nch * (Hv * (32768 + 12288 + 32768 + 512) + Hk * 32768)
+
+
 def run_gdn(args, ev):
-    """Gated DeltaNet scan: prefill scans (T=512, 2048) over 4 layers in rotation, and
-    T=1 decode steps over 30 layer states in rotation (a step is the 30 scans,
-    captured as a HIP graph and checked against the eager calls)."""
+    """Gated DeltaNet scan: prefill scans (T=512, 2048) over 4 layers in rotation on
+    the chunked MFMA form (the register-resident scan timed on the same inputs),
+    and T=1 decode steps of the register scan over 30 layer states in rotation (a
+    step is the 30 scans).  Each is captured as a HIP graph and checked against
+    the eager calls."""
     import torch
     from w4_dequant_grouped_amd import moe_w4 as B
     from w4_dequant_grouped_amd import synth_gdn as SG
@@ -676,65 +698,102 @@ def run_gdn(args, ev):
         xs = [SG.draw_gdn(shape, seed + 100 * l, device="cuda") for l in range(L)]
         outs = [torch.empty_like(x.v) for x in xs]
         states = [x.state.clone() for x in xs]
+        ws = torch.empty(max(B.moe_w4_gdn_chunked_workspace_bytes(shape.T, shape.n_v_heads, shape.n_k_heads), 16),
+                         dtype=torch.uint8, device="cuda")
 
-        def body():
-            for x, o, st in zip(xs, outs, states):
-                B.moe_w4_gdn_scan(x.q, x.k, x.v, x.g, x.beta, st, o)
+        def scan(chunked, x, st, o, events=None):
+            if chunked:
+                return B.moe_w4_gdn_scan_chunked(x.q, x.k, x.v, x.g, x.beta, st, o, ws, events=events)
+            return B.moe_w4_gdn_scan(x.q, x.k, x.v, x.g, x.beta, st, o, events=events)
 
-        body()
-        torch.cuda.synchronize()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
+        def measure(chunked):
+            def body():
+                for x, o, st in zip(xs, outs, states):
+                    scan(chunked, x, st, o)
+
             body()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+            torch.cuda.synchronize()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                body()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                body()
+            # a replay must equal the eager calls from the same states
+            snap = [st.clone() for st in states]
             body()
-        # a replay must equal the eager calls from the same states
-        snap = [st.clone() for st in states]
-        body()
-        torch.cuda.synchronize()
-        ref = [o.clone() for o in outs] + [st.clone() for st in states]
-        for st, s0 in zip(states, snap):
-            st.copy_(s0)
-        g.replay()
-        torch.cuda.synchronize()
-        if not all(torch.equal(a, b) for a, b in zip(outs + states, ref)):
-            raise RuntimeError("Gated DeltaNet graph replay differs from the eager calls")
-        steps = args.steps if name == "decode" else max(5, args.steps // 10)
-        elapsed = time_steps(lambda i=0: g.replay(), steps, args.warmup)
-        us = 1e6 * elapsed / (steps * L)
-        evs = []
-        for r in range(3):
-            for x, o, st in zip(xs, outs, states):
-                e = ev.create(2)
-                assert B.moe_w4_gdn_scan(x.q, x.k, x.v, x.g, x.beta, st, o, events=e) == 1
-                evs.append(e)
-        torch.cuda.synchronize()
-        k_us = 1e3 * sum(ev.elapsed_ms(e[0], e[1]) for e in evs) / len(evs)
-        for e in evs:
-            ev.destroy(e)
+            torch.cuda.synchronize()
+            ref = [o.clone() for o in outs] + [st.clone() for st in states]
+            for st, s0 in zip(states, snap):
+                st.copy_(s0)
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(outs + states, ref)):
+                raise RuntimeError("Gated DeltaNet graph replay differs from the eager calls")
+            steps = args.steps if name == "decode" else max(5, args.steps // 10)
+            elapsed = time_steps(lambda i=0: g.replay(), steps, args.warmup)
+            us = 1e6 * elapsed / (steps * L)
+            # per-kernel durations: kernel i of each call (prep, scan per segment)
+            per = {}
+            for r in range(3):
+                for x, o, st in zip(xs, outs, states):
+                    e = ev.create(16)
+                    n = scan(chunked, x, st, o, events=e)
+                    torch.cuda.synchronize()
+                    for i in range(n):
+                        per.setdefault(i, []).append(1e3 * ev.elapsed_ms(e[2 * i], e[2 * i + 1]))
+                    ev.destroy(e)
+            del g
+            return us, {i: sum(v) / len(v) for i, v in per.items()}
+
         nbytes, flops = SG.gdn_bytes(shape), SG.gdn_flops(shape)
-        ent = {"T": shape.T, "layers": L, "us_per_layer": round(us, 3),
-               "tokens_per_s": round(shape.T / (us * 1e-6), 1), "alg_MB": round(nbytes / 1e6, 3),
-               "alg_GFLOP": round(flops / 1e9, 3), "kernel_us": round(k_us, 3)}
         if name == "decode":
+            us, per = measure(False)
+            k_us = per[0]
             ach = nbytes / (k_us * 1e-6) / 1e9
+            ent = {"T": shape.T, "layers": L, "path": "register scan", "us_per_layer": round(us, 3),
+                   "tokens_per_s": round(shape.T / (us * 1e-6), 1), "alg_MB": round(nbytes / 1e6, 3),
+                   "alg_GFLOP": round(flops / 1e9, 3), "kernel_us": round(k_us, 3)}
             ent["roofline"] = {"bound": "hbm", "kernel": "gdn_scan", "achieved": round(ach, 1),
                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                                "traffic": traffic_from_profiles("gdn_scan", name),
                                "alg_bytes_per_launch": int(nbytes), "avg_launch_us": round(k_us, 3)}
         else:
-            ach = flops / (k_us * 1e-6) / 1e12
-            ent["roofline"] = {"bound": "alu", "kernel": "gdn_scan", "achieved": round(ach, 2),
-                               "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": round(ach / VALU_FP32_PEAK_TFLOPS, 4),
-                               "traffic": traffic_from_profiles("gdn_scan", name),
-                               "alg_flops_per_launch": int(flops), "avg_launch_us": round(k_us, 3)}
+            r_us, r_per = measure(False)
+            c_us, c_per = measure(True)
+            nseg = len(c_per) // 2
+            prep_us = sum(c_per[2 * i] for i in range(nseg)) / nseg
+            scan_us = sum(c_per[2 * i + 1] for i in range(nseg)) / nseg
+            sb, pb = gdn_chunked_scan_bytes(shape), gdn_prep_bytes(shape)
+            ent = {"T": shape.T, "layers": L, "path": "chunked MFMA form (prep + chunk scan)",
+                   "us_per_layer": round(c_us, 3), "tokens_per_s": round(shape.T / (c_us * 1e-6), 1),
+                   "register_us_per_layer": round(r_us, 3),
+                   "register_tokens_per_s": round(shape.T / (r_us * 1e-6), 1),
+                   "speedup_vs_register": round(r_us / c_us, 2),
+                   "alg_MB": round(nbytes / 1e6, 3), "alg_GFLOP": round(flops / 1e9, 3),
+                   "kernels_us": {"gdn_prep": round(prep_us, 2), "gdn_chunk_scan": round(scan_us, 2),
+                                  "launches_per_kind": nseg}}
+            ach = sb / (scan_us * 1e-6) / 1e9
+            ent["roofline"] = {"bound": "hbm", "kernel": "gdn_chunk_scan", "achieved": round(ach, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                               "traffic": traffic_from_profiles("gdn_chunk_scan", name),
+                               "alg_bytes_per_launch": int(sb), "avg_launch_us": round(scan_us, 3)}
+            pach = pb / (prep_us * 1e-6) / 1e9
+            ent["prep_roofline"] = {"bound": "hbm", "kernel": "gdn_prep", "achieved": round(pach, 1),
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pach / HBM_PEAK_GBS, 4),
+                                    "traffic": traffic_from_profiles("gdn_prep", name),
+                                    "alg_bytes_per_launch": int(pb), "avg_launch_us": round(prep_us, 3)}
+            rk = r_per[0]
+            rach = flops / (rk * 1e-6) / 1e12
+            ent["register_roofline"] = {"bound": "alu", "kernel": "gdn_scan", "achieved": round(rach, 2),
+                                        "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(rach / VALU_FP32_PEAK_TFLOPS, 4),
+                                        "alg_flops_per_launch": int(flops), "avg_launch_us": round(rk, 3)}
         res[name] = ent
-        del xs, outs, states, g
+        del xs, outs, states, ws
         torch.cuda.empty_cache()
     return res
 
