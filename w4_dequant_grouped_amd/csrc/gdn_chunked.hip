@@ -138,13 +138,20 @@ __device__ __forceinline__ float* key_block(const GdnChunkArgs& a, int nch, int 
 // k_gdn_prep
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[kC][kD + 8];        // K rows
-    __shared__ __attribute__((aligned(16))) uint16_t s_qv[kD * (kC + 8)];    // Q rows [64][136], then V^T [128][72]
-    __shared__ __attribute__((aligned(16))) uint16_t s_kt[kD][kC + 8];       // K^T
-    __shared__ __attribute__((aligned(16))) float s_a[kC][kC + 4];           // A, then Tinv
+    // Two LDS regions, each reused across the phases, so that four workgroups fit
+    // a CU and a segment's workgroups are resident together:
+    //   region 1: K rows [64][136] bf16 -> A, then Tinv, [64][68] fp32 -> V^T [128][72] bf16
+    //   region 2: Q rows [64][136] bf16 -> K^T [128][72] bf16
+    constexpr int kRegion = kD * (kC + 8) * 2;                               // the largest use, 18 KiB
+    __shared__ __attribute__((aligned(16))) unsigned char s_r1[kRegion], s_r2[kRegion];
     __shared__ __attribute__((aligned(16))) float s_g[kC], s_b[kC], s_bg[kC];   // s_g: G log2(e)
-    uint16_t (*s_q)[kD + 8] = reinterpret_cast<uint16_t (*)[kD + 8]>(s_qv);
-    uint16_t (*s_vt)[kC + 8] = reinterpret_cast<uint16_t (*)[kC + 8]>(s_qv);
+    uint16_t (*s_k)[kD + 8] = reinterpret_cast<uint16_t (*)[kD + 8]>(s_r1);
+    float (*s_a)[kC + 4] = reinterpret_cast<float (*)[kC + 4]>(s_r1);
+    uint16_t (*s_vt)[kC + 8] = reinterpret_cast<uint16_t (*)[kC + 8]>(s_r1);
+    uint16_t (*s_q)[kD + 8] = reinterpret_cast<uint16_t (*)[kD + 8]>(s_r2);
+    uint16_t (*s_kt)[kC + 8] = reinterpret_cast<uint16_t (*)[kC + 8]>(s_r2);
+    static_assert(sizeof(uint16_t) * kC * (kD + 8) <= kRegion && sizeof(float) * kC * (kC + 4) <= kRegion,
+                  "LDS regions");
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -177,11 +184,11 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
         hb[kOffG + kC + lane] = __builtin_amdgcn_exp2f(__shfl(g2, kC - 1, kWave) - g2);
     }
     // K, Q and V of the chunk (zero past the sequence): each thread one unit of
-    // tokens 4 tq .. +3 and columns 8 cg .. +7, loaded once.  K rows and K^T and
-    // Q rows go to LDS; V^T stays in registers until K Q^T is done with Q's LDS.
-    u32x2 vtile[8];
+    // tokens 4 tq .. +3 and columns 8 cg .. +7, loaded once.  K and Q rows go to
+    // LDS; K^T and V^T wait in registers for their regions.
+    const int tq = threadIdx.x & 15, cg = threadIdx.x >> 4;
+    u32x2 ktile[8], vtile[8];
     {
-        const int tq = threadIdx.x & 15, cg = threadIdx.x >> 4;
         u32x4 kr[4], qr[4], vr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -208,27 +215,16 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
             transpose4(vh2, vc);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                *reinterpret_cast<u32x2*>(&s_kt[8 * cg + 4 * hf + d][4 * tq]) = kc[d];
+                ktile[4 * hf + d] = kc[d];
                 vtile[4 * hf + d] = vc[d];
             }
         }
     }
     __syncthreads();
 
-    // K^T fragments of the scan's state update (key block jb, token group p) and
-    // Q fragments of its Q S^T (token block = wave, key group p), paired-block
-    // order, once per key head
+    // Q fragments of the scan's Q S^T (token block = wave, key group p), paired-
+    // block order, once per key head
     if (h % a.rep == 0) {
-        u32x4* kf = reinterpret_cast<u32x4*>(key_block(a, nch, c, kh));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int jb = 2 * wave + i;
-                const uint16_t* row = &s_kt[16 * jb + ln][32 * p + 4 * g4];
-                kf[(jb * 2 + p) * 64 + lane] = cat(*reinterpret_cast<const u32x2*>(row),
-                                                   *reinterpret_cast<const u32x2*>(row + 16));
-            }
         u32x4* qf = reinterpret_cast<u32x4*>(key_block(a, nch, c, kh) + kOffQ);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -239,9 +235,9 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
     }
 
     // K K^T and K Q^T as transposed blocks [s block sb][t block = wave]: lane holds
-    // s = 16 sb + 4 g4 + r, t = 16 wave + ln.  A (strictly lower, times beta_t) to
-    // LDS as rows t; Pm kept for its fragments.
-    f32x4 pm[4];
+    // s = 16 sb + 4 g4 + r, t = 16 wave + ln.  A (strictly lower, times beta_t) and
+    // Pm stay in registers until K's and Q's regions are free.
+    f32x4 pm[4], am[4];
     {
         const int t = 16 * wave + ln;
         const float gt = s_g[t], bt = s_b[t];
@@ -267,7 +263,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
                 pv[r] = dec * kq[r];
             }
             pm[sb] = pv;
-            *reinterpret_cast<float4*>(&s_a[t][16 * sb + 4 * g4]) = float4{av[0], av[1], av[2], av[3]};
+            am[sb] = av;
         }
     }
     // Pm fragments [token block wave][token group p]
@@ -282,12 +278,27 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
             f[64 + lane] = sp.lo;
         }
     }
-    __syncthreads();          // A complete; Q no longer read
-
-    {
-        const int tq = threadIdx.x & 15, cg = threadIdx.x >> 4;
+    __syncthreads();          // K and Q rows no longer read: A and K^T take their regions
 #pragma unroll
-        for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x2*>(&s_vt[8 * cg + d][4 * tq]) = vtile[d];
+    for (int sb = 0; sb < 4; ++sb)
+        *reinterpret_cast<f32x4*>(&s_a[16 * wave + ln][16 * sb + 4 * g4]) = am[sb];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x2*>(&s_kt[8 * cg + d][4 * tq]) = ktile[d];
+    __syncthreads();
+
+    // K^T fragments of the scan's state update (key block jb, token group p),
+    // paired-block order, once per key head
+    if (h % a.rep == 0) {
+        u32x4* kf = reinterpret_cast<u32x4*>(key_block(a, nch, c, kh));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int jb = 2 * wave + i;
+                const uint16_t* row = &s_kt[16 * jb + ln][32 * p + 4 * g4];
+                kf[(jb * 2 + p) * 64 + lane] = cat(*reinterpret_cast<const u32x2*>(row),
+                                                   *reinterpret_cast<const u32x2*>(row + 16));
+            }
     }
 
     // Tinv level 1: wavefront w inverts its diagonal block I + A_ww by forward
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) s_a[16 * i + 4 * g4 + e][16 * j + ln] = -x[e];
     }
-    __syncthreads();          // Tinv complete (zero above the diagonal), V^T staged
+    __syncthreads();          // Tinv complete (zero above the diagonal)
 
     // rows t = 16 wave + ln of Tb and Tbg over token groups p (natural order);
     // Tinv is zero for s > t, so blocks 0 and 1 need group 0 only
@@ -360,6 +371,10 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnChunkArgs a) {
         tgs[p] = split8(f32x4{x0.x * c0.x, x0.y * c0.y, x0.z * c0.z, x0.w * c0.w},
                         f32x4{x1.x * c1.x, x1.y * c1.y, x1.z * c1.z, x1.w * c1.w});
     }
+    __syncthreads();          // Tinv no longer read: V^T takes its region
+#pragma unroll
+    for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x2*>(&s_vt[8 * cg + d][4 * tq]) = vtile[d];
+    __syncthreads();
 
     // W^T = K^T Tbg^T as blocks [key block jb][token block wave]: lane holds
     // W[16 wave + ln][16 jb + 4 g4 + r], two blocks = one -W fragment (paired order)
