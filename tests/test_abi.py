@@ -265,6 +265,46 @@ def test_gdn_rejects_bad_arguments(lib):
     assert _gdn(lib, _gdims(), out=FAKE + 2) == ERR_ALIGN
 
 
+def _gdn_chunked(lib, dims, ws=FAKE + 8192, ws_bytes=1 << 40, q=FAKE, state=FAKE, out=FAKE + 4096):
+    return lib.moe_w4_gdn_scan_chunked(ctypes.byref(dims) if dims is not None else None, q, FAKE, FAKE, FAKE,
+                                       FAKE, state, out, ws, ws_bytes, None)
+
+
+def test_gdn_chunked_workspace_bytes(lib):
+    """One 2048-token segment at most: per 64-token chunk 82,432 bytes per value head
+    (-W, Pm and Vt operand fragments, the decays) and 32,768 per key head (K^T and Q
+    fragments); zero for invalid dims."""
+    def wsb(**kw):
+        return lib.moe_w4_gdn_chunked_workspace_bytes(ctypes.byref(_gdims(**kw)))
+    per_chunk = 32 * 82432 + 16 * 32768
+    assert wsb(T=1) == per_chunk
+    assert wsb(T=64) == per_chunk
+    assert wsb(T=65) == 2 * per_chunk
+    assert wsb(T=2048) == 32 * per_chunk
+    assert wsb(T=B.MOE_W4_GDN_MAX_T) == 32 * per_chunk
+    assert wsb(T=100, n_v_heads=8, n_k_heads=2) == 2 * (8 * 82432 + 2 * 32768)
+    assert wsb(T=0) == 0
+    assert wsb(n_k_heads=5) == 0
+    assert wsb(dim=64) == 0
+    assert lib.moe_w4_gdn_chunked_workspace_bytes(None) == 0
+
+
+def test_gdn_chunked_rejects_bad_arguments(lib):
+    need = lib.moe_w4_gdn_chunked_workspace_bytes(ctypes.byref(_gdims()))
+    assert _gdn_chunked(lib, None) == ERR_NULL
+    assert _gdn_chunked(lib, _gdims(flags=1)) == ERR_FLAGS
+    assert _gdn_chunked(lib, _gdims(T=B.MOE_W4_GDN_MAX_T + 1)) == ERR_DIMS
+    assert _gdn_chunked(lib, _gdims(n_k_heads=3)) == ERR_DIMS
+    assert _gdn_chunked(lib, _gdims(dim=64)) == ERR_GROUP
+    assert _gdn_chunked(lib, _gdims(T=0), ws=None, ws_bytes=0) == OK      # nothing to do
+    assert _gdn_chunked(lib, _gdims(), ws=None) == ERR_NULL
+    assert _gdn_chunked(lib, _gdims(), q=None) == ERR_NULL
+    assert _gdn_chunked(lib, _gdims(), ws=FAKE + 8) == ERR_ALIGN
+    assert _gdn_chunked(lib, _gdims(), state=FAKE + 4) == ERR_ALIGN
+    assert _gdn_chunked(lib, _gdims(), ws_bytes=need - 1) == ERR_WS
+    assert _gdn_chunked(lib, _gdims(), ws_bytes=0) == ERR_WS
+
+
 def test_size_limits_match_the_headers():
     for header, name, value in (("moe_w4_attn.h", "MOE_W4_ATTN_MAX_CTX", B.MOE_W4_ATTN_MAX_CTX),
                                 ("moe_w4_gdn.h", "MOE_W4_GDN_MAX_T", B.MOE_W4_GDN_MAX_T)):
