@@ -15,7 +15,7 @@
 // operands of v_dot2_f32_bf16 with two bit operations per pair and no
 // conversion; the expanded weights never exist.
 //
-//   k_decode_gateup: (slot, 16 rows of I) per workgroup -> h = silu(g) * u (bf16)
+//   k_decode_gateup: (slot, 8 rows of I) per workgroup -> h = silu(g) * u (bf16)
 //   k_decode_down:   8 output rows per workgroup, every slot -> out (bf16)
 // A slot is the shared expert (first: it needs no routing, so its workgroups
 // start streaming at once) or an expert with a non-empty segment (ascending id).
@@ -140,10 +140,14 @@ __device__ __forceinline__ Slot find_slot(const int32_t* __restrict__ offsets, i
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU
 // ---------------------------------------------------------------------------
-// Weight rows per wavefront: 4 for up to four token rows, 2 beyond (the
-// accumulators of every token stay in registers).
+// Weight rows per wavefront: 2 for every row count.  A decode gate/up wavefront
+// is one memory round trip plus its dot products and one wavefront reduction
+// per row; two rows halve that tail against four, with twice the workgroups
+// (measured per layer-call: T=1 21.1 -> 18.7 us, T=2 28.2 -> 25.1, T=4
+// 44.7 -> 42.6; one row was slower again at T=1, 20.2 us, with every extra
+// workgroup repeating the top-k).
 template <int TMAX>
-constexpr int gu_rows_per_wave() { return TMAX <= 4 ? 4 : 2; }
+constexpr int gu_rows_per_wave() { return 2; }
 template <int TMAX>
 constexpr int gu_rows_per_block() { return 4 * gu_rows_per_wave<TMAX>(); }
 
@@ -520,11 +524,12 @@ static hipError_t decode_t(const ForwardArgs& a, hipStream_t st, KernelTimer& tm
 // Launch 1: router logits (a wavefront per expert) and the shared expert's
 //   gate/up -- both need only x, so their bytes stream together.
 // Launch 2: every workgroup reads the T x E logits and repeats the (cheap)
-//   top-k and grouping in LDS; workgroup (0, 0) writes the routing outputs.
-//   Workgroup (s, y) then runs rows 16y .. 16y+15 of gate/up of the s-th
-//   selected expert (ascending id).  There is no "last workgroup" hand-off
-//   inside the router: the kernel boundary is the only grid-wide dependency
-//   between the logits and the expert weights.
+//   top-k; the workgroup of the last column writes the routing outputs and the
+//   slot table and runs no expert rows.  Workgroup (s, y) runs rows
+//   8y .. 8y+7 of gate/up of the s-th selected expert (ascending id); at T = 1
+//   each wavefront selects on its own and needs no grouping.  There is no
+//   "last workgroup" hand-off inside the router: the kernel boundary is the
+//   only grid-wide dependency between the logits and the expert weights.
 // Launch 3: k_decode_down over the shared expert and the selected experts.
 
 template <int TMAX>
