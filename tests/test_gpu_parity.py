@@ -353,6 +353,31 @@ def test_boundary_ties_go_to_the_lower_expert(T):
         check_output(out, y, what=f"ties T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 2, 16])
+def test_six_way_tie_across_the_top12_boundary(T):
+    """top-12 of 64 experts: nine far above, six with identical router rows and
+    biases spread over several lane groups, the rest far below.  Only the three
+    lowest-id tied experts may be chosen, which the selection can settle only at
+    full key depth."""
+    shape = S(T=T, H=256, I=128, E=64, top_k=12)
+    layer = synth.draw_layer(shape, 90 + T)
+    tied = [12, 20, 33, 47, 58, 61]
+    for e in tied[1:]:
+        layer.router_w[e] = layer.router_w[tied[0]]
+    bias = torch.full((64,), -40.0, dtype=torch.float32)
+    bias[:9] = 40.0
+    bias[tied] = 10.0
+    layer.router_b = bias
+    x = synth.draw_x(T, 256, 90 + T)
+    ref = O.route(x, layer.router_w, layer.router_b, 12)
+    assert (ref.ids == np.array(list(range(9)) + tied[:3])).all()
+    lg = layer.to("cuda")
+    for split in (False, True):
+        r, out = run_block(lg, x.cuda(), shape, split=split)
+        check_routing(r, ref, f"6-way tie T={T} {'split' if split else 'block'}")
+        check_output(out, O.forward_grouped(x, layer, ref, shape.group), what=f"6-way tie T={T}")
+
+
 # --- largest sizes the ABI accepts ------------------------------------------------------
 
 @pytest.mark.parametrize("T", [2, 64])

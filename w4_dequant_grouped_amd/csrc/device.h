@@ -165,28 +165,21 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 
-// Maximum of a 64-bit key over the wavefront, returned in every lane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-    auto step = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
-    auto mv = [](uint64_t a, auto ctrl) {
-        constexpr int c = decltype(ctrl)::value;
-        const int lo = dpp_i<c>((int)(uint32_t)a);
-        const int hi = dpp_i<c>((int)(uint32_t)(a >> 32));
-        return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-    };
-    k = step(k, mv(k, std::integral_constant<int, kDppXor1>{}));
-    k = step(k, mv(k, std::integral_constant<int, kDppXor2>{}));
-    k = step(k, mv(k, std::integral_constant<int, kDppHalfMirror>{}));
-    k = step(k, mv(k, std::integral_constant<int, kDppMirror>{}));
-    uint64_t r = 0;
-#pragma unroll
-    for (int row = 0; row < 4; ++row) {
-        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, row * 16);
-        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), row * 16);
-        r = step(r, ((uint64_t)hi << 32) | lo);
-    }
-    return r;
+// Maximum and minimum of an unsigned 32-bit value over the wavefront, returned
+// (uniform) in every lane.
+template <bool kMax>
+__device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t v) {
+    auto pick = [](uint32_t a, uint32_t b) { return kMax ? (a > b ? a : b) : (a < b ? a : b); };
+    v = pick(v, (uint32_t)dpp_i<kDppXor1>((int)v));
+    v = pick(v, (uint32_t)dpp_i<kDppXor2>((int)v));
+    v = pick(v, (uint32_t)dpp_i<kDppHalfMirror>((int)v));
+    v = pick(v, (uint32_t)dpp_i<kDppMirror>((int)v));
+    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+    return pick(pick(r0, r1), pick(r2, r3));
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_extreme_u32<true>(v); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_extreme_u32<false>(v); }
 
 // --- memory -------------------------------------------------------------------
 

@@ -32,12 +32,19 @@ __device__ __forceinline__ int bits_below(uint64_t mask) {
 // vals[j] is the logit of expert e = lane + 64 j.  Chooses the k largest (ties
 // to the lower expert) and writes them in ascending expert order to ids_out and
 // w_out (and ids_lds when given), with the renormalised softmax weights
-// exp(l - lmax) / (sum over the chosen).  No k sequential arg-max rounds: a
-// bitwise binary search on the order keys finds the k-th largest key theta (32
-// steps of one compare and one ballot count each); the entries above theta and
-// the lowest-id entries equal to theta are chosen, and every chosen entry's rank
-// in ascending expert order comes from the ballot masks, which are also
-// returned in masks_out[j] (bit l: expert 64 j + l chosen) when given.
+// exp(l - lmax) / (sum over the chosen).  No k sequential arg-max rounds: the
+// k-th largest order key theta is found by bisection, each probe c costing one
+// compare and one ballot count per register, f(c) = #{valid keys >= c}.  The
+// bracket starts at [lo, hi]: hi is the largest key; lo is the smallest of the
+// maxima of 8 disjoint lane groups (16 when k > 8), which are that many distinct
+// entries, so f(lo) >= k.  The probes keep f(lo) >= k and theta <= hi, and stop
+// early when f(c) == k: then no key lies in [c, theta), so the keys >= c are
+// exactly the chosen ones.  For logits of a continuous distribution the bracket
+// narrows to the gap between the k-th and (k+1)-th largest within a handful of
+// probes (at most 32 in any case).  The entries above theta and the lowest-id
+// entries equal to theta are chosen, and every chosen entry's rank in ascending
+// expert order comes from the ballot masks, which are also returned in
+// masks_out[j] (bit l: expert 64 j + l chosen) when given.
 template <int EPL>
 __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E, int k, int lane,
                                                  int32_t* __restrict__ ids_out,
@@ -45,17 +52,33 @@ __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E
                                                  int32_t* ids_lds = nullptr,
                                                  uint64_t* masks_out = nullptr) {
     uint32_t key[EPL];
+    uint32_t g = 0u;                       // invalid entries hold key 0
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) key[j] = (lane + kWave * j < E) ? order_key(vals[j]) : 0u;
-    // theta: the largest value with #{key >= theta} >= k
-    uint32_t theta = 0u;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t c = theta | (1u << b);
+    for (int j = 0; j < EPL; ++j) {
+        key[j] = (lane + kWave * j < E) ? order_key(vals[j]) : 0u;
+        g = key[j] > g ? key[j] : g;
+    }
+    // group maxima: 4 lanes (16 groups) or 8 lanes (8 groups); a group without a
+    // valid entry has maximum 0, which makes lo = 0 and f(0) = E >= k
+    auto gmax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    g = gmax(g, (uint32_t)dpp_i<kDppXor1>((int)g));
+    g = gmax(g, (uint32_t)dpp_i<kDppXor2>((int)g));
+    if (k <= 8) g = gmax(g, (uint32_t)dpp_i<kDppHalfMirror>((int)g));
+    const uint32_t top = wave_max_u32(g);
+    uint32_t lo = wave_min_u32(g), hi = top;
+    while (lo < hi) {
+        const uint32_t c = lo + ((hi - lo) >> 1) + 1u;   // lo < c <= hi
         int n = 0;
 #pragma unroll
         for (int j = 0; j < EPL; ++j) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[j] >= c));
-        if (n >= k) theta = c;
+        if (n < k) {
+            hi = c - 1u;
+        } else {
+            lo = c;
+            if (n == k) break;
+        }
     }
+    const uint32_t theta = lo;
     // chosen: key > theta, then key == theta in ascending expert order until k
     int above = 0;
 #pragma unroll
@@ -71,12 +94,9 @@ __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E
         sel[j] = (valid && key[j] > theta) || (eq && eq_before + bits_below(m) < need);
         eq_before += __builtin_popcountll(m);
     }
-    // weights: exp(l - lmax) over the chosen (the largest logit is always chosen)
-    uint32_t kmax = 0u;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) kmax = (sel[j] && key[j] > kmax) ? key[j] : kmax;
-    kmax = (uint32_t)(wave_max_u64((uint64_t)kmax));
-    const float vmax = order_key_inverse(kmax);
+    // weights: exp(l - lmax) over the chosen (an entry with the largest key is
+    // always chosen)
+    const float vmax = order_key_inverse(top);
     float p[EPL];
     float local = 0.f;
 #pragma unroll
