@@ -98,20 +98,17 @@ __device__ __forceinline__ void build_slots(const int32_t* __restrict__ offsets,
     if (lane == 0) *s_n = min(base + a.total, kMaxSlots);
 }
 
-// Slot list from a table written by the routing kernel: [0] = n, then (expert,
-// first h row, rows) for each selected expert in ascending id.  One round trip.
-__device__ __forceinline__ void read_slot_table(const int32_t* __restrict__ table, int T, int k,
-                                                int has_shared, Slot* s_slots, int* s_n, int lane) {
-    const int base = has_shared ? 1 : 0;
-    const int n = min(max(table[0], 0), min(T * k, kMaxSlots - base));
-    if (has_shared && lane == 0) s_slots[0] = Slot{-1, T * k, T};
-    for (int i = lane; i < n; i += kWave) {
-        const int e = table[1 + 3 * i];
-        const int off = min(max(table[2 + 3 * i], 0), T * k);
-        const int cnt = min(max(table[3 + 3 * i], 0), min(T, T * k - off));
-        s_slots[base + i] = Slot{e, off, cnt};
-    }
-    if (lane == 0) *s_n = base + n;
+// Slot table written by the routing kernel of the decode block (1 + 5 T k
+// words): [0] = n; (expert, first h row, rows) of the i-th selected expert in
+// ascending id at 1 + 3 i, i < n; (token, weight bits) of routed h row p at
+// slot_rows_at(T, k) + 2 p, p < T k.  Every read is clamped to the ranges the
+// kernels assume.
+__device__ __forceinline__ int slot_rows_at(int T, int k) { return 1 + 3 * T * k; }
+__device__ __forceinline__ int slot_count(const int32_t* __restrict__ table, int T, int k, int base) {
+    return min(max(table[0], 0), min(T * k, kMaxSlots - base));
+}
+__device__ __forceinline__ int slot_expert(const int32_t* __restrict__ table, int i, int E) {
+    return min(max(table[1 + 3 * i], 0), E - 1);
 }
 
 // The idx-th non-empty expert (ascending id), found by one wavefront;
@@ -367,6 +364,7 @@ constexpr int kDnRowsPerWave = 2;
 constexpr int kDnRowsPerBlock = 4 * kDnRowsPerWave;
 constexpr int kDnUnroll = 4;     // (slot, 32-code chunk) items per lane in one batch of loads
 constexpr int kDnLdsI = 512;     // h is staged in LDS when I <= this
+constexpr int kDnThreads = 256;  // threads per down workgroup
 
 // h rows of T <= TMAX tokens: T*k routed + T shared, k <= 16
 template <int TMAX>
@@ -384,11 +382,14 @@ struct DnBatch {
 // threads), the slot list (wavefront 0) and each h row's token and weight
 // (wavefront 1) go to LDS in parallel, so that no batch of weight loads waits
 // on a dependent global read, and the next batch is in flight while the
-// current one is used.  HLDS: h staged in LDS (I <= kDnLdsI), else read from
-// global memory.  A compile-time choice: a global read inside the item loop
-// would make every iteration wait for the next batch's loads too.
-template <int TMAX, bool HLDS>
-__global__ __launch_bounds__(256) void k_decode_down(
+// current one is used.  Given the routing kernel's slot table, the first
+// batch's experts are read from it directly and its weight loads are issued
+// before that staging, and the rows' tokens and weights come from the table in
+// one round trip.  HLDS: h staged in LDS (I <= kDnLdsI), else read from global
+// memory.  A compile-time choice: a global read inside the item loop would make
+// every iteration wait for the next batch's loads too.
+template <int TMAX, bool HLDS, bool kTable>
+__global__ __launch_bounds__(kDnThreads) void k_decode_down(
     int T, int H, int I, int E, int k, W4Set routed, W4Set shared, int has_shared,
     const float* __restrict__ topk_w, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const uint16_t* __restrict__ h,
@@ -402,43 +403,23 @@ __global__ __launch_bounds__(256) void k_decode_down(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int hrows = T * k + T;
-    if constexpr (HLDS) {
-        const int n16 = hrows * I / 8;
-        for (int i = threadIdx.x; i < n16; i += blockDim.x)
-            reinterpret_cast<u32x4*>(s_h)[i] = reinterpret_cast<const u32x4*>(h)[i];
-    }
-    if (wave == 0) {
-        if (slot_table) read_slot_table(slot_table, T, k, has_shared, s_slots, &s_n, lane);
-        else build_slots(offsets, E, T, k, has_shared, s_slots, &s_n, lane);
-    } else if (wave == 1) {
-        for (int r = lane; r < hrows; r += kWave) {
-            int t;
-            float w;
-            if (r >= T * k) { t = r - T * k; w = 1.0f; }
-            else { const int f = min(max(perm[r], 0), T * k - 1); t = f / k; w = topk_w[f]; }
-            s_rt[r] = t;
-            s_rw[r] = w;
-        }
-    }
-    __syncthreads();
-    const int nslots = s_n;
+    const int base = has_shared ? 1 : 0;
     const int n0 = blockIdx.x * kDnRowsPerBlock + wave * kDnRowsPerWave;
     const int cpr = I / 32;            // 32-code chunks per down row
     const int ngroups = I / kGroup;
-    const int nitems = nslots * cpr;
     constexpr int kStep = kWave * kDnUnroll;
-    // items past the end load slot 0, chunk 0 again (in bounds, never used)
-    auto load = [&](DnBatch& B, int base) {
+    // ex[u]: expert of item u's slot, negative for the shared expert; items past
+    // the end load chunk 0 of an in-bounds expert (never used)
+    auto load = [&](DnBatch& B, int first, int nitems, const int (&ex)[kDnUnroll]) {
 #pragma unroll
         for (int u = 0; u < kDnUnroll; ++u) {
-            const int idx = base + u * kWave + lane;
+            const int idx = first + u * kWave + lane;
             const bool ok = idx < nitems;
             const int a = ok ? idx / cpr : 0;
             B.slot[u] = ok ? a : -1;
             B.cc[u] = ok ? idx - a * cpr : 0;
-            const Slot sl = s_slots[a];
-            const bool is_shared = sl.e < 0;
-            const int e = is_shared ? 0 : sl.e;
+            const bool is_shared = ex[u] < 0;
+            const int e = is_shared ? 0 : ex[u];
             const W4 D = is_shared ? shared.down : routed.down;
 #pragma unroll
             for (int r = 0; r < kDnRowsPerWave; ++r) {
@@ -450,15 +431,121 @@ __global__ __launch_bounds__(256) void k_decode_down(
             }
         }
     };
+    auto load_lds = [&](DnBatch& B, int first, int nitems) {
+        int ex[kDnUnroll];
+#pragma unroll
+        for (int u = 0; u < kDnUnroll; ++u) {
+            const int idx = first + u * kWave + lane;
+            ex[u] = s_slots[idx < nitems ? idx / cpr : 0].e;
+        }
+        load(B, first, nitems, ex);
+    };
+    DnBatch cur, nxt;
+    // h: all of this thread's loads first (unconditional, index clamped; T >= 1
+    // here, so h is not empty), the LDS writes later: one round trip
+    constexpr int kPer = HLDS ? (HR * kDnLdsI / 8 + kDnThreads - 1) / kDnThreads : 1;
+    const int n16 = hrows * I / 8;
+    u32x4 hv[kPer];
+    auto load_h = [&]() {
+#pragma unroll
+        for (int q = 0; q < kPer; ++q)
+            hv[q] = reinterpret_cast<const u32x4*>(h)[min((int)threadIdx.x + q * kDnThreads, n16 - 1)];
+    };
+    auto store_h = [&]() {
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int i = threadIdx.x + q * kDnThreads;
+            if (i < n16) reinterpret_cast<u32x4*>(s_h)[i] = hv[q];
+        }
+    };
+    int nitems;
+    if constexpr (kTable) {
+        // Straight-line, every read issued before any wait that the weights
+        // would hold up (loads complete in issue order): the table entries of
+        // the first batch's items, of every slot and of every routed h row (one
+        // lane each, T k <= 64), the count; then the first batch's weights; then
+        // h; then the LDS writes.
+        static_assert(TMAX * kMaxTopK + TMAX <= kWave, "one lane per slot and per h row");
+        int ex[kDnUnroll];
+#pragma unroll
+        for (int u = 0; u < kDnUnroll; ++u) {
+            const int a = (u * kWave + lane) / cpr;
+            ex[u] = slot_table[1 + 3 * min(max(a - base, 0), T * k - 1)];
+        }
+        // lane i reads words 3 i .. 3 i + 3: slot i, and in lane 0 the count (a
+        // vector read, so that no scalar wait comes before the other reads)
+        const int i = min(lane, T * k - 1);
+        int c0 = slot_table[3 * i];
+        int se = slot_table[1 + 3 * i], so = slot_table[2 + 3 * i], sc = slot_table[3 + 3 * i];
+        int rt = slot_table[slot_rows_at(T, k) + 2 * i];
+        int rw = slot_table[slot_rows_at(T, k) + 2 * i + 1];
+        // an empty asm that takes every table value: all the reads above are
+        // issued before it and no use of one is moved above it (one wait)
+        static_assert(kDnUnroll == 4, "operands below");
+        asm volatile("" : "+v"(c0), "+v"(se), "+v"(so), "+v"(sc), "+v"(rt), "+v"(rw),
+                          "+v"(ex[0]), "+v"(ex[1]), "+v"(ex[2]), "+v"(ex[3]));
+        const int nsel = min(max(__builtin_amdgcn_readfirstlane(c0), 0), min(T * k, kMaxSlots - base));
+        nitems = (base + nsel) * cpr;
+#pragma unroll
+        for (int u = 0; u < kDnUnroll; ++u) {
+            const int a = (u * kWave + lane) / cpr;
+            ex[u] = a < base ? -1 : min(max(ex[u], 0), E - 1);
+        }
+        load(cur, 0, nitems, ex);
+        if constexpr (HLDS) {
+            load_h();
+            store_h();
+        }
+        if (wave == 0) {
+            if (has_shared && lane == 0) s_slots[0] = Slot{-1, T * k, T};
+            if (lane < nsel) {
+                const int off = min(max(so, 0), T * k);
+                s_slots[base + lane] = Slot{min(max(se, 0), E - 1), off, min(max(sc, 0), min(T, T * k - off))};
+            }
+            if (lane == 0) s_n = base + nsel;
+        } else if (wave == 1 && lane < hrows) {
+            const bool routed_row = lane < T * k;
+            s_rt[lane] = routed_row ? min(max(rt, 0), T - 1) : lane - T * k;
+            s_rw[lane] = routed_row ? __int_as_float(rw) : 1.0f;
+        }
+        __syncthreads();
+    } else {
+        if constexpr (HLDS) {
+            load_h();
+            store_h();
+        }
+        if (wave == 0) {
+            build_slots(offsets, E, T, k, has_shared, s_slots, &s_n, lane);
+        } else if (wave == 1) {
+            for (int r = lane; r < hrows; r += kWave) {
+                int t;
+                float w;
+                if (r >= T * k) {
+                    t = r - T * k;
+                    w = 1.0f;
+                } else {
+                    const int f = min(max(perm[r], 0), T * k - 1);
+                    t = f / k;
+                    w = topk_w[f];
+                }
+                s_rt[r] = t;
+                s_rw[r] = w;
+            }
+        }
+        __syncthreads();
+        nitems = s_n * cpr;
+        load_lds(cur, 0, nitems);
+    }
     float acc[kDnRowsPerWave][TMAX];
 #pragma unroll
     for (int r = 0; r < kDnRowsPerWave; ++r)
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) acc[r][t] = 0.f;
-    DnBatch cur, nxt;
-    load(cur, 0);
-    for (int base = 0; base < nitems; base += kStep) {
-        load(nxt, base + kStep);                 // next batch in flight during this one
+    for (int first = 0; first < nitems; first += kStep) {
+        // next batch in flight during this one; none past the end (its loads
+        // would still be waited for before the kernel's last instructions)
+        const bool more = first + kStep < nitems;
+        if (more) load_lds(nxt, first + kStep, nitems);
 #pragma unroll
         for (int u = 0; u < kDnUnroll; ++u) {
             if (cur.slot[u] < 0) continue;
@@ -488,6 +575,7 @@ __global__ __launch_bounds__(256) void k_decode_down(
                 }
             }
         }
+        if (!more) break;
         cur = nxt;
     }
 #pragma unroll
@@ -511,8 +599,8 @@ static hipError_t decode_t(const ForwardArgs& a, hipStream_t st, KernelTimer& tm
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    tm.launch(a.I <= kDnLdsI ? k_decode_down<TMAX, true> : k_decode_down<TMAX, false>,
-              dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T, a.H, a.I, a.E, a.k, a.routed,
+    tm.launch(a.I <= kDnLdsI ? k_decode_down<TMAX, true, false> : k_decode_down<TMAX, false, false>,
+              dim3(a.H / kDnRowsPerBlock), dim3(kDnThreads), 0, st, a.T, a.H, a.I, a.E, a.k, a.routed,
               a.shared, a.has_shared, a.topk_w, a.offsets, a.perm, a.ws_h, a.out, nullptr);
     tm.after();
     return hipGetLastError();
@@ -607,14 +695,13 @@ __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) 
             // among the chosen, so no grouping is needed.  Each wavefront selects on
             // its own (no barrier) and streams its expert's rows as soon as it knows it.
             __shared__ int32_t s_idw[4][kMaxTopK];
-            __shared__ float s_ww[4][kMaxTopK];
             float vals[EPL];
 #pragma unroll
             for (int j = 0; j < EPL; ++j) {
                 const int e = lane + kWave * j;
                 vals[j] = (e < E) ? a.logits[e] : -INFINITY;
             }
-            wave_topk_select<EPL>(vals, E, k, lane, s_idw[wave], s_ww[wave]);
+            wave_topk_select<EPL>(vals, E, k, lane, s_idw[wave], nullptr);   // ids only
             const int slot = blockIdx.x;               // grid.x = min(E, k) + 1: slot < k
             const int e = s_idw[wave][slot];
             const int tok1[1] = {0};
@@ -632,8 +719,11 @@ __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) 
             const int e = lane + kWave * j;
             vals[j] = (e < E) ? a.logits[t * E + e] : -INFINITY;
         }
+        // the writer also keeps the weights in LDS for the row table; the other
+        // workgroups need only the selection masks
         wave_topk_select<EPL>(vals, E, k, lane, writer ? a.ids + t * k : s_ids + t * k,
-                              writer ? a.tw + t * k : s_w + t * k, nullptr, &s_mask[t][0]);
+                              writer ? a.tw + t * k : nullptr, nullptr, writer ? s_w + t * k : nullptr,
+                              &s_mask[t][0]);
     }
     __syncthreads();
     // grouping by wavefront 0 from the selection masks: lane l handles experts
@@ -684,7 +774,12 @@ __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) 
                     if ((mk[t][j] >> lane) & 1ull) {
                         const int p = below + before;
                         s_ptok[p] = t;
-                        if (writer) a.perm[p] = t * k + pre[t][j] + bits_below(mk[t][j]);
+                        if (writer) {
+                            const int f = t * k + pre[t][j] + bits_below(mk[t][j]);
+                            a.perm[p] = f;
+                            a.slots[slot_rows_at(T, k) + 2 * p] = t;
+                            a.slots[slot_rows_at(T, k) + 2 * p + 1] = __float_as_int(s_w[f]);
+                        }
                         ++before;
                     }
                 }
@@ -734,8 +829,8 @@ static hipError_t block_decode_t(const DecodeBlockArgs& a, hipStream_t st, Kerne
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    tm.launch(a.I <= kDnLdsI ? k_decode_down<TMAX, true> : k_decode_down<TMAX, false>,
-              dim3(a.H / kDnRowsPerBlock), dim3(256), 0, st, a.T, a.H, a.I, a.E, a.k, a.routed,
+    tm.launch(a.I <= kDnLdsI ? k_decode_down<TMAX, true, true> : k_decode_down<TMAX, false, true>,
+              dim3(a.H / kDnRowsPerBlock), dim3(kDnThreads), 0, st, a.T, a.H, a.I, a.E, a.k, a.routed,
               a.shared, a.has_shared, a.tw, a.offsets, a.perm, a.h, a.out, a.slots);
     tm.after();
     return hipGetLastError();

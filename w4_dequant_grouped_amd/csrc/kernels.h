@@ -86,7 +86,7 @@ struct DecodeBlockArgs {     // route + forward of decode rows (T <= kDecodeMaxT
     uint16_t* out;           // [T][H] bf16
     float* logits;           // [T][E] workspace
     uint16_t* h;             // [T*k + T][I] bf16 workspace
-    int32_t* slots;          // [1 + 3 T k] workspace: selected experts for the down kernel
+    int32_t* slots;          // [1 + 5 T k] workspace: selected experts and h rows for the down kernel
 };
 
 // Decode attention over a paged KV cache (moe_w4_attn_decode).

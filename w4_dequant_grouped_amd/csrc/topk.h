@@ -44,12 +44,15 @@ __device__ __forceinline__ int bits_below(uint64_t mask) {
 // probes (at most 32 in any case).  The entries above theta and the lowest-id
 // entries equal to theta are chosen, and every chosen entry's rank in ascending
 // expert order comes from the ballot masks, which are also returned in
-// masks_out[j] (bit l: expert 64 j + l chosen) when given.
+// masks_out[j] (bit l: expert 64 j + l chosen) when given.  With w_out null the
+// weights are neither computed nor written (ids only); ids_lds and w_lds receive
+// second copies of the ids and weights when given.
 template <int EPL>
 __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E, int k, int lane,
                                                  int32_t* __restrict__ ids_out,
                                                  float* __restrict__ w_out,
                                                  int32_t* ids_lds = nullptr,
+                                                 float* w_lds = nullptr,
                                                  uint64_t* masks_out = nullptr) {
     uint32_t key[EPL];
     uint32_t g = 0u;                       // invalid entries hold key 0
@@ -96,15 +99,18 @@ __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E
     }
     // weights: exp(l - lmax) over the chosen (an entry with the largest key is
     // always chosen)
-    const float vmax = order_key_inverse(top);
     float p[EPL];
-    float local = 0.f;
+    float inv = 0.f;
+    if (w_out) {
+        const float vmax = order_key_inverse(top);
+        float local = 0.f;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-        p[j] = sel[j] ? expf(vals[j] - vmax) : 0.f;
-        local += p[j];
+        for (int j = 0; j < EPL; ++j) {
+            p[j] = sel[j] ? expf(vals[j] - vmax) : 0.f;
+            local += p[j];
+        }
+        inv = 1.0f / wave_sum(local);
     }
-    const float inv = 1.0f / wave_sum(local);
     int before = 0;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
@@ -112,8 +118,11 @@ __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E
         if (sel[j]) {
             const int rank = before + bits_below(m);
             ids_out[rank] = lane + kWave * j;
-            w_out[rank] = p[j] * inv;
             if (ids_lds) ids_lds[rank] = lane + kWave * j;
+            if (w_out) {
+                w_out[rank] = p[j] * inv;
+                if (w_lds) w_lds[rank] = p[j] * inv;
+            }
         }
         if (masks_out && lane == 0) masks_out[j] = m;   // chosen experts 64 j .. 64 j + 63
         before += __builtin_popcountll(m);
