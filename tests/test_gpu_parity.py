@@ -15,8 +15,8 @@ from oracle import moe_w4_oracle as O
 from w4_dequant_grouped_amd import moe_w4 as B
 from w4_dequant_grouped_amd import synth
 
-from parity_util import (check_output, check_routing, full_check, make_inputs, note, run_block,
-                         sampled_rows)
+from parity_util import (GAP, check_output, check_routing, full_check, make_inputs, note,
+                         run_block, sampled_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -132,6 +132,25 @@ def full_layer():
 def test_decode_full_size(full_layer, T):
     shape = S(T=T, H=2048, I=512, E=256, top_k=8)
     full_check(shape, 100 + T, layer=full_layer, what=f"decode full T={T}")
+
+
+def test_two_equal_rows_share_every_expert(full_layer):
+    """T=2 with both token rows equal: both tokens pick the same eight experts, so
+    every routed slot of the single-call decode block holds two h rows, and the down
+    kernel takes both rows' tokens and weights from the slot table.  Routing
+    bit-exact, both output rows within the tolerance (block and split calls)."""
+    shape = S(T=2, H=2048, I=512, E=256, top_k=8)
+    x1, _ = O.gap_conditioned_x(lambda rd: synth.draw_x(1, shape.H, 96, redraws=rd), 1,
+                                full_layer.router_w, full_layer.router_b, shape.top_k, GAP)
+    x = torch.cat([x1, x1], 0)
+    ref = O.route(x, full_layer.router_w, full_layer.router_b, shape.top_k)
+    assert (ref.ids[0] == ref.ids[1]).all() and (ref.counts[ref.counts > 0] == 2).all()
+    lg = full_layer.to("cuda")
+    y = O.forward_grouped(x, full_layer, ref, shape.group)
+    for split in (False, True):
+        r, out = run_block(lg, x.cuda(), shape, split=split)
+        check_routing(r, ref, f"equal rows {'split' if split else 'block'}")
+        check_output(out, y, what=f"equal rows {'split' if split else 'block'}")
 
 
 @pytest.mark.parametrize("T,flags", [(1, B.MOE_W4_FORWARD_GROUPED), (4, B.MOE_W4_FORWARD_GROUPED),
