@@ -208,7 +208,9 @@ def step_percentiles(step_fn, n):
 
 def measure_ceilings():
     """Secondary denominators measured on this GPU: a plain device copy (bytes read
-    plus written per second) and a large bf16 GEMM through torch (hipBLASLt)."""
+    plus written per second), a plain read (row sums over the same buffer, the
+    fastest of the torch reductions measured: the weight streams of the MoE kernels
+    only read) and a large bf16 GEMM through torch (hipBLASLt)."""
     import torch
     n = 1 << 28                                   # 1 GiB of fp32
     src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -222,7 +224,17 @@ def measure_ceilings():
     b.record()
     torch.cuda.synchronize()
     copy_gbps = 10 * 2 * 4 * n / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src, dst
+    del dst
+    rows = src.view(-1, 4096)
+    for _ in range(2):
+        s = rows.sum(1)
+    a.record()
+    for _ in range(10):
+        s = rows.sum(1)
+    b.record()
+    torch.cuda.synchronize()
+    read_gbps = 10 * 4 * n / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, rows, s
     m = 8192
     g = torch.Generator(device="cuda").manual_seed(5)
     x = torch.randn((m, m), generator=g, device="cuda").to(torch.bfloat16)
@@ -237,8 +249,10 @@ def measure_ceilings():
     gemm_tflops = 10 * 2.0 * m ** 3 / (a.elapsed_time(b) * 1e-3) / 1e12
     del x, w, y
     torch.cuda.empty_cache()
-    return {"copy_GBps": round(copy_gbps, 1), "bf16_gemm_TFLOPs": round(gemm_tflops, 1),
+    return {"copy_GBps": round(copy_gbps, 1), "read_GBps": round(read_gbps, 1),
+            "bf16_gemm_TFLOPs": round(gemm_tflops, 1),
             "copy": "1 GiB fp32 device copy (read + write bytes)",
+            "read": "row sums (4096 floats a row) over the same 1 GiB fp32 buffer (bytes read)",
             "gemm": f"{m}x{m}x{m} bf16 matmul (torch / hipBLASLt)"}
 
 
@@ -1046,6 +1060,10 @@ def main():
     line["ceilings"] = ceil
     rf = line["roofline"]
     rf["frac_of_measured_copy"] = round(rf["achieved"] / ceil["copy_GBps"], 4)
+    rf["frac_of_measured_read"] = round(rf["achieved"] / ceil["read_GBps"], 4)
+    if "prefill_T512" in line:
+        p5 = line["prefill_T512"]["roofline"]
+        p5["frac_of_measured_read"] = round(p5["achieved"] / ceil["read_GBps"], 4)
     if "prefill" in line:
         pr = line["prefill"]["roofline"]
         pr["frac_of_measured_gemm"] = round(pr["achieved"] / ceil["bf16_gemm_TFLOPs"], 4)
