@@ -198,7 +198,7 @@ int moe_w4_forward(const moe_w4_dims* dims, const void* x,
  * moe_w4_route() followed by moe_w4_forward() in one call, with the same
  * arguments, outputs and errors as the pair: every argument is validated before
  * anything is enqueued.  The routing outputs are written as moe_w4_route()
- * writes them.  For T <= 2 the work is scheduled as three kernels instead of the
+ * writes them.  For T <= 4 the work is scheduled as three kernels instead of the
  * pair's: (1) router logits together with the shared expert's gate/up, which
  * need only x; (2) top-k and grouping repeated by every workgroup from the
  * logits, followed by the selected experts' gate/up; (3) down and the weighted

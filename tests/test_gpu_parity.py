@@ -399,10 +399,12 @@ def test_six_way_tie_across_the_top12_boundary(T):
 
 # --- largest sizes the ABI accepts ------------------------------------------------------
 
-@pytest.mark.parametrize("T", [2, 64])
+@pytest.mark.parametrize("T", [2, 4, 64])
 def test_max_experts_and_top_k(T):
     """E = 1024 experts (the largest accepted) with top-16: the 16-per-lane top-k,
-    1025 segments in the grouped tile list, and the single-call decode block."""
+    1025 segments in the grouped tile list, and the single-call decode block (at
+    T=4 its 64 selected slots and 68 h rows take the down kernel's slot table in
+    two passes of 64 lanes)."""
     full_check(S(T=T, H=256, I=128, E=1024, top_k=16), 70 + T, what=f"E=1024 top16 T={T}")
 
 

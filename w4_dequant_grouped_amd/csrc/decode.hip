@@ -463,27 +463,41 @@ __global__ __launch_bounds__(kDnThreads) void k_decode_down(
         // Straight-line, every read issued before any wait that the weights
         // would hold up (loads complete in issue order): the table entries of
         // the first batch's items, of every slot and of every routed h row (one
-        // lane each, T k <= 64), the count; then the first batch's weights; then
-        // h; then the LDS writes.
-        static_assert(TMAX * kMaxTopK + TMAX <= kWave, "one lane per slot and per h row");
+        // lane each per pass of 64), the count; then the first batch's weights;
+        // then h; then the LDS writes.
+        constexpr int kP = (TMAX * kMaxTopK + TMAX + kWave - 1) / kWave;   // passes of 64 slots or rows
+        static_assert(kP <= 2, "table reads below");
         int ex[kDnUnroll];
 #pragma unroll
         for (int u = 0; u < kDnUnroll; ++u) {
             const int a = (u * kWave + lane) / cpr;
             ex[u] = slot_table[1 + 3 * min(max(a - base, 0), T * k - 1)];
         }
-        // lane i reads words 3 i .. 3 i + 3: slot i, and in lane 0 the count (a
-        // vector read, so that no scalar wait comes before the other reads)
-        const int i = min(lane, T * k - 1);
-        int c0 = slot_table[3 * i];
-        int se = slot_table[1 + 3 * i], so = slot_table[2 + 3 * i], sc = slot_table[3 + 3 * i];
-        int rt = slot_table[slot_rows_at(T, k) + 2 * i];
-        int rw = slot_table[slot_rows_at(T, k) + 2 * i + 1];
+        // lane i of pass p reads words 3 i .. 3 i + 3 for slot i = 64 p + lane
+        // (clamped into the table), and in pass 0 lane 0 the count (a vector
+        // read, so that no scalar wait comes before the other reads)
+        int c0 = 0, se[kP], so[kP], sc[kP], rt[kP], rw[kP];
+#pragma unroll
+        for (int p = 0; p < kP; ++p) {
+            const int i = min(kWave * p + lane, T * k - 1);
+            if (p == 0) c0 = slot_table[3 * i];
+            se[p] = slot_table[1 + 3 * i];
+            so[p] = slot_table[2 + 3 * i];
+            sc[p] = slot_table[3 + 3 * i];
+            rt[p] = slot_table[slot_rows_at(T, k) + 2 * i];
+            rw[p] = slot_table[slot_rows_at(T, k) + 2 * i + 1];
+        }
         // an empty asm that takes every table value: all the reads above are
         // issued before it and no use of one is moved above it (one wait)
         static_assert(kDnUnroll == 4, "operands below");
-        asm volatile("" : "+v"(c0), "+v"(se), "+v"(so), "+v"(sc), "+v"(rt), "+v"(rw),
-                          "+v"(ex[0]), "+v"(ex[1]), "+v"(ex[2]), "+v"(ex[3]));
+        if constexpr (kP == 1) {
+            asm volatile("" : "+v"(c0), "+v"(se[0]), "+v"(so[0]), "+v"(sc[0]), "+v"(rt[0]), "+v"(rw[0]),
+                              "+v"(ex[0]), "+v"(ex[1]), "+v"(ex[2]), "+v"(ex[3]));
+        } else {
+            asm volatile("" : "+v"(c0), "+v"(se[0]), "+v"(so[0]), "+v"(sc[0]), "+v"(rt[0]), "+v"(rw[0]),
+                              "+v"(se[kP - 1]), "+v"(so[kP - 1]), "+v"(sc[kP - 1]), "+v"(rt[kP - 1]),
+                              "+v"(rw[kP - 1]), "+v"(ex[0]), "+v"(ex[1]), "+v"(ex[2]), "+v"(ex[3]));
+        }
         const int nsel = min(max(__builtin_amdgcn_readfirstlane(c0), 0), min(T * k, kMaxSlots - base));
         nitems = (base + nsel) * cpr;
 #pragma unroll
@@ -498,15 +512,25 @@ __global__ __launch_bounds__(kDnThreads) void k_decode_down(
         }
         if (wave == 0) {
             if (has_shared && lane == 0) s_slots[0] = Slot{-1, T * k, T};
-            if (lane < nsel) {
-                const int off = min(max(so, 0), T * k);
-                s_slots[base + lane] = Slot{min(max(se, 0), E - 1), off, min(max(sc, 0), min(T, T * k - off))};
+#pragma unroll
+            for (int p = 0; p < kP; ++p) {
+                const int i = kWave * p + lane;
+                if (i < nsel) {
+                    const int off = min(max(so[p], 0), T * k);
+                    s_slots[base + i] = Slot{min(max(se[p], 0), E - 1), off, min(max(sc[p], 0), min(T, T * k - off))};
+                }
             }
             if (lane == 0) s_n = base + nsel;
-        } else if (wave == 1 && lane < hrows) {
-            const bool routed_row = lane < T * k;
-            s_rt[lane] = routed_row ? min(max(rt, 0), T - 1) : lane - T * k;
-            s_rw[lane] = routed_row ? __int_as_float(rw) : 1.0f;
+        } else if (wave == 1) {
+#pragma unroll
+            for (int p = 0; p < kP; ++p) {
+                const int r = kWave * p + lane;
+                if (r < hrows) {
+                    const bool routed_row = r < T * k;
+                    s_rt[r] = routed_row ? min(max(rt[p], 0), T - 1) : r - T * k;
+                    s_rw[r] = routed_row ? __int_as_float(rw[p]) : 1.0f;
+                }
+            }
         }
         __syncthreads();
     } else {
@@ -844,10 +868,12 @@ static hipError_t block_decode_e(const DecodeBlockArgs& a, hipStream_t st, Kerne
 }
 
 hipError_t launch_block_decode(const DecodeBlockArgs& a, hipStream_t st, KernelTimer& tm) {
-    static_assert(kBlockDecodeMaxT == 2, "instantiations below");
+    static_assert(kBlockDecodeMaxT == 4, "instantiations below");
     switch (a.T) {
         case 1: return block_decode_e<1>(a, st, tm);
         case 2: return block_decode_e<2>(a, st, tm);
+        case 3: return block_decode_e<3>(a, st, tm);
+        case 4: return block_decode_e<4>(a, st, tm);
         default: return hipErrorInvalidValue;     // the host serves larger T by route + forward
     }
 }
