@@ -717,17 +717,16 @@ __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) 
         if (!writer) {
             // One row: every selected expert has exactly one h row, the rank of its id
             // among the chosen, so no grouping is needed.  Each wavefront selects on
-            // its own (no barrier) and streams its expert's rows as soon as it knows it.
-            __shared__ int32_t s_idw[4][kMaxTopK];
+            // its own (no barrier, no LDS) and streams its expert's rows as soon as it
+            // knows it.
             float vals[EPL];
 #pragma unroll
             for (int j = 0; j < EPL; ++j) {
                 const int e = lane + kWave * j;
                 vals[j] = (e < E) ? a.logits[e] : -INFINITY;
             }
-            wave_topk_select<EPL>(vals, E, k, lane, s_idw[wave], nullptr);   // ids only
             const int slot = blockIdx.x;               // grid.x = min(E, k) + 1: slot < k
-            const int e = s_idw[wave][slot];
+            const int e = wave_topk_nth<EPL>(vals, E, k, lane, slot);
             const int tok1[1] = {0};
             const int n0 = blockIdx.y * gu_rows_per_block<1>() + wave * gu_rows_per_wave<1>();
             gateup_rows<1>(a.x, a.H, a.I, a.routed.gate, a.routed.up, e, n0, 1, tok1, slot, a.h, lane, wave);
