@@ -17,6 +17,8 @@
 //
 //   k_decode_gateup: (slot, 8 rows of I) per workgroup -> h = silu(g) * u (bf16)
 //   k_decode_down:   8 output rows per workgroup, every slot -> out (bf16)
+// and the single-call block for T <= 4 (route + forward in three launches,
+// described above k_decode_logits_shared).
 // A slot is the shared expert (first: it needs no routing, so its workgroups
 // start streaming at once) or an expert with a non-empty segment (ascending id).
 // Both kernels read the routing from the device; the grid depends only on T.
@@ -699,7 +701,6 @@ __global__ __launch_bounds__(256) void k_decode_logits_shared(DecodeBlockArgs a)
 template <int TMAX, int EPL>
 __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) {
     constexpr int N = TMAX * kMaxTopK;            // (token, slot) entries at most
-    __shared__ int32_t s_ids[N];
     __shared__ float s_w[N];
     __shared__ uint64_t s_mask[TMAX][EPL];        // chosen experts of each token
     __shared__ int s_ptok[N];
@@ -744,7 +745,7 @@ __global__ __launch_bounds__(256) void k_decode_route_gateup(DecodeBlockArgs a) 
         }
         // the writer also keeps the weights in LDS for the row table; the other
         // workgroups need only the selection masks
-        wave_topk_select<EPL>(vals, E, k, lane, writer ? a.ids + t * k : s_ids + t * k,
+        wave_topk_select<EPL>(vals, E, k, lane, writer ? a.ids + t * k : nullptr,
                               writer ? a.tw + t * k : nullptr, nullptr, writer ? s_w + t * k : nullptr,
                               &s_mask[t][0]);
     }

@@ -238,14 +238,19 @@ __device__ __forceinline__ void report_exit(uint32_t* ctl, int exit_word, uint32
 
 // ---------------------------------------------------------------------------
 // The K-loop of one tile, software-pipelined through LDS.
-//   Every operand byte of a K chunk -- the kBM activation rows (A), the
-//   wavefront's packed weight rows (B codes) and their group scale/bias words --
-//   is copied global -> LDS by the direct global_load_lds path, issued through
-//   inline assembly, into one of two stages: while chunk c is multiplied from
-//   one stage, chunk c+1 is copied into the other.  The loop holds no load the
-//   compiler tracks, and its only waits on the copies are explicit.  A rows are
-//   gathered by token on the fly and stored XOR-swizzled by row, which keeps the
-//   MFMA operand reads conflict-free.
+//   The operand bytes of a K chunk -- the kBM activation rows (A) and the
+//   wavefront's packed weight rows (B codes) -- are copied global -> LDS by the
+//   direct global_load_lds path, issued through inline assembly, into one of two
+//   stages: while chunk c is multiplied from one stage, chunk c+1 is copied into
+//   the other.  The copies' only waits are explicit.  A rows are gathered by
+//   token on the fly and stored XOR-swizzled by row, which keeps the MFMA operand
+//   reads conflict-free.  The group scale/bias words travel in registers instead:
+//   each lane loads the words of its (array, row) for four chunks with one
+//   16-byte load and hands each chunk's word to the lanes that need it with
+//   ds_bpermute.  (Copied to LDS one word per lane and chunk, as before, those
+//   loads were a quarter of a chunk's copy instructions and most of its memory
+//   requests, 64 scattered 4-byte reads; a timing copy without them was 14%
+//   faster on gate/up at 512 tokens.)
 // ---------------------------------------------------------------------------
 constexpr int kARow = kKC * 2;                     // bytes of one A row per chunk (256)
 constexpr int kABuf = kBM * kARow;                 // A bytes per stage (16 KiB)
@@ -253,22 +258,20 @@ constexpr int kBRowBytes = kKC / 2;                // packed codes of a weight r
 constexpr int kBBlk = 16 * kBRowBytes;             // codes of one 16-row block (1 KiB)
 constexpr int kBlkPerWave = 2;                     // (matrix, 16-row block) pairs per wavefront
 constexpr int kBBuf = kWaves * kBlkPerWave * kBBlk;    // B code bytes per stage (8 KiB)
-constexpr int kSBWave = kWave * 4;                 // scale/bias words of a wavefront (256 B)
-constexpr int kSBBuf = kWaves * kSBWave;           // per stage (1 KiB)
-constexpr int kStageBytes = kABuf + kBBuf + kSBBuf;
-constexpr int kStages = 2;                         // 50 KiB: three workgroups share a CU's 160 KiB
+constexpr int kStageBytes = kABuf + kBBuf;
+constexpr int kStages = 2;                         // 48 KiB: three workgroups share a CU's 160 KiB
 constexpr int kDmaPerWave = kBM / kWaves / 4;      // A copies per wavefront in a full tile (4 rows, 1 KiB each)
 
 // Per-tile copy addressing.  The bases are wave-uniform (SGPRs, advanced per
 // chunk with scalar adds); the lane offsets are computed once per tile, so a
-// copy costs no vector arithmetic except the scale/bias address (+4 B a chunk).
+// copy costs no vector arithmetic.
 template <int NMAT, int NBW>
 struct TileSrc {
     uint64_t a_base;                 // A operand (x for gate/up, the segment's h rows for down)
     uint32_t a_off[kDmaPerWave];     // lane's byte offset of its row piece in each A copy
     uint64_t b_base[NMAT][NBW];      // codes of the first row of each (matrix, 16-row block)
     uint32_t b_off;                  // lane's byte offset within a block's chunk
-    uint64_t sb_addr;                // lane's scale/bias word of chunk 0
+    uint64_t sb_addr;                // the scale/bias words of the lane's (array, row), chunk 0 first
     int K;
 };
 
@@ -276,9 +279,6 @@ struct TileSrc {
 __device__ __forceinline__ uint32_t off_a(int st) { return (uint32_t)(st * kStageBytes); }
 __device__ __forceinline__ uint32_t off_b(int st, int wave) {
     return (uint32_t)(st * kStageBytes + kABuf + wave * kBlkPerWave * kBBlk);
-}
-__device__ __forceinline__ uint32_t off_sb(int st, int wave) {
-    return (uint32_t)(st * kStageBytes + kABuf + kBBuf + wave * kSBWave);
 }
 
 // Lane offsets of the A copies: copy i of wavefront w moves the four rows of
@@ -304,10 +304,10 @@ __device__ __forceinline__ void a_offsets(uint32_t (&off)[kDmaPerWave], int wave
 //    (16 bytes) of row r = L>>2 (64 B per row) with quarter (L&3) ^ ((r>>2)&3)
 //    of the row's 64 code bytes of the chunk; the XOR spreads the 16 rows'
 //    reads of one quarter over the LDS banks;
-//  * scale/bias: one dword copy; lane L copies the word holding the chunk's two
-//    groups (even group in the low half) of row L&15, from the scales (bit 4 of
-//    L clear) or biases, of pair p = L>>5.  The word is 4-byte aligned because
-//    K/64 is even and the arrays are 4-byte aligned.
+//  * scale/bias: lane L owns row L&15 of pair p = L>>5, in the scales (bit 4 of
+//    L clear) or the biases; the row's word of chunk c holds the chunk's two
+//    groups (even group in the low half) at sb_addr + 4 c.  Every word is 4-byte
+//    aligned because K/64 is even and the arrays are 4-byte aligned.
 template <int NMAT, int NBW>
 __device__ __forceinline__ void b_addressing(TileSrc<NMAT, NBW>& t, const W4 (&mat)[NMAT],
                                              const uint32_t (&rowblk)[NBW], int K, int lane) {
@@ -351,13 +351,29 @@ __device__ __forceinline__ void issue_chunk(uint32_t ring, int wave, const TileS
         for (int nb = 0; nb < NBW; ++nb)
             dma16_to_lds(t.b_base[m][nb] + (uint64_t)c * (kKC / 2), t.b_off,
                          ring + off_b(st, wave) + (m * NBW + nb) * kBBlk);
-    dma4_to_lds(reinterpret_cast<const void*>(t.sb_addr + (uint64_t)c * 4u), ring + off_sb(st, wave));
+}
+
+// The lane's scale/bias words of chunks 4 b .. 4 b + 3 (one 16-byte load, 4-byte
+// aligned); for a last block of fewer chunks, dword loads that stay inside the
+// row (the words past its last chunk are never used).
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ u32x4 load_sb_block(uint64_t sb_addr, int b, int nch) {
+    // a global (not flat) pointer: a flat load would also count against the LDS
+    // wait counter
+    const __attribute__((address_space(1))) uint32_t* p =
+        reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(sb_addr) + 4 * b;
+    if (4 * b + 4 <= nch) {
+        const u32x4_a4 v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4_a4*>(p);
+        return u32x4{v.x, v.y, v.z, v.w};
+    }
+    const int last = nch - 1 - 4 * b;
+    return u32x4{p[0], p[min(1, last)], p[min(2, last)], p[min(3, last)]};
 }
 
 
-// Operands of one K chunk that are read from LDS before the chunk's MFMA work:
-// the wavefront's packed codes and scale/bias words, and the A fragments of the
-// first MFMA step.  They are read right after the barrier that publishes the
+// Operands of one K chunk that are read before the chunk's MFMA work: the
+// wavefront's packed codes and the A fragments of the first MFMA step from LDS,
+// and the scale/bias words from the lanes that hold them.  They are read right after the barrier that publishes the
 // chunk, ahead of the next chunk's copy instructions, so their LDS latency
 // overlaps the copy issue instead of stalling the first dequantisation.
 template <int NMAT, int NBW, int MB>
@@ -378,18 +394,19 @@ __device__ __forceinline__ void read_a_step(bf16x8 (&a)[MB], const uint8_t* s_a,
         a[mb] = *reinterpret_cast<const bf16x8*>(s_a + (mb * 16 + arow) * kARow + col);
 }
 
+// `mine` is this lane's scale/bias word of the chunk; the scale and bias of row
+// arow of pair p are the words of lanes 32 p + arow and 32 p + 16 + arow.
 template <int NMAT, int NBW, int MB>
 __device__ __forceinline__ void read_chunk_ops(ChunkOps<NMAT, NBW, MB>& o, const uint8_t* s_a,
-                                               const uint8_t* s_b, const uint8_t* s_sb, int lane) {
+                                               const uint8_t* s_b, uint32_t mine, int lane) {
     const int arow = lane & 15;
-    const uint32_t* sb = reinterpret_cast<const uint32_t*>(s_sb);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
             const int p = m * NBW + nb;
-            o.sw[m][nb] = sb[p * 32 + arow];
-            o.bw[m][nb] = sb[p * 32 + 16 + arow];
+            o.sw[m][nb] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (p * 32 + arow), (int)mine);
+            o.bw[m][nb] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (p * 32 + 16 + arow), (int)mine);
             o.codes[m][nb] = *reinterpret_cast<const u32x4*>(
                 s_b + p * kBBlk + arow * kBRowBytes + (((lane >> 4) ^ (arow >> 2)) & 3) * 16);
         }
@@ -443,18 +460,26 @@ __device__ __forceinline__ void mma_chunk(ChunkOps<NMAT, NBW, MB>& o, const uint
 // K-loop over the two-stage ring.  Iteration c waits for this wavefront's copies
 // (vmcnt 0), then a barrier makes every wavefront's part of chunk c visible and
 // frees the stage read in iteration c-1, which receives chunk c+1 while chunk c
-// is multiplied.  The chunk's first operands are read from LDS before the copies
-// of chunk c+1 are issued.  The loop is unrolled by two so that each stage's LDS
-// offsets are compile-time constants.  Nothing is copied past the end of K.
+// is multiplied.  The chunk's first operands are read before the copies of chunk
+// c+1 are issued.  The loop is unrolled by two so that each stage's LDS offsets
+// are compile-time constants.  Nothing is copied past the end of K.  sbc holds
+// the lane's scale/bias words of the current block of four chunks; at the first
+// chunk of a block it takes sbn, and the next block's load goes out (its result
+// is waited for with the copies of the next iteration).
 template <int NMAT, int NBW, int MB, int ST>
 __device__ __forceinline__ void kloop_step(uint8_t* s_stage, uint32_t ring, int wave, int lane,
                                            const TileSrc<NMAT, NBW>& t, int c, int nch,
-                                           f32x4 (&acc)[MB][NMAT][NBW]) {
+                                           u32x4& sbc, u32x4& sbn, f32x4 (&acc)[MB][NMAT][NBW]) {
     wait_vmcnt<0>();
     __syncthreads();           // chunk c visible to all; the other stage is free
+    if (ST == 0 && (c & 3) == 0) {
+        sbc = sbn;
+        if (c + 4 < nch) sbn = load_sb_block(t.sb_addr, c / 4 + 1, nch);
+    }
+    // c & 1 == ST
+    const uint32_t mine = (c & 2) ? sbc[ST + 2] : sbc[ST];
     ChunkOps<NMAT, NBW, MB> o;
-    read_chunk_ops<NMAT, NBW, MB>(o, s_stage + off_a(ST), s_stage + off_b(ST, wave),
-                                  s_stage + off_sb(ST, wave), lane);
+    read_chunk_ops<NMAT, NBW, MB>(o, s_stage + off_a(ST), s_stage + off_b(ST, wave), mine, lane);
     if (c + 1 < nch) issue_chunk<MB>(ring, wave, t, c + 1);
     mma_chunk<NMAT, NBW, MB>(o, s_stage + off_a(ST), lane, acc);
 }
@@ -466,10 +491,11 @@ __device__ __forceinline__ void tile_kloop(uint8_t* s_stage, int wave, int lane,
     static_assert(kStages == 2, "the loop below alternates two stages");
     const int nch = t.K / kKC;
     const uint32_t ring = lds_addr(s_stage);
+    u32x4 sbc, sbn = load_sb_block(t.sb_addr, 0, nch);
     issue_chunk<MB>(ring, wave, t, 0);
     for (int c = 0; c < nch; c += 2) {
-        kloop_step<NMAT, NBW, MB, 0>(s_stage, ring, wave, lane, t, c, nch, acc);
-        if (c + 1 < nch) kloop_step<NMAT, NBW, MB, 1>(s_stage, ring, wave, lane, t, c + 1, nch, acc);
+        kloop_step<NMAT, NBW, MB, 0>(s_stage, ring, wave, lane, t, c, nch, sbc, sbn, acc);
+        if (c + 1 < nch) kloop_step<NMAT, NBW, MB, 1>(s_stage, ring, wave, lane, t, c + 1, nch, sbc, sbn, acc);
     }
     __syncthreads();           // both stages free for the next tile
 }

@@ -142,8 +142,9 @@ __device__ __forceinline__ uint32_t wave_topk_choose(const uint32_t (&key)[EPL],
 // largest key is always chosen, so lmax is the bracket's top.  Every chosen
 // entry's rank in ascending expert order comes from the ballot masks, which are
 // also returned in masks_out[j] (bit l: expert 64 j + l chosen) when given.  With
-// w_out null the weights are neither computed nor written (ids only); ids_lds
-// and w_lds receive second copies of the ids and weights when given.
+// w_out null the weights are neither computed nor written (ids only), and with
+// ids_out null the ids are not written either; ids_lds and w_lds receive second
+// copies of the ids and weights when given.
 template <int EPL>
 __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E, int k, int lane,
                                                  int32_t* __restrict__ ids_out,
@@ -173,7 +174,7 @@ __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E
     for (int j = 0; j < EPL; ++j) {
         if (sel[j]) {
             const int rank = before + bits_below(chosen[j]);
-            ids_out[rank] = lane + kWave * j;
+            if (ids_out) ids_out[rank] = lane + kWave * j;
             if (ids_lds) ids_lds[rank] = lane + kWave * j;
             if (w_out) {
                 w_out[rank] = p[j] * inv;
