@@ -75,6 +75,14 @@ def test_tile_counts_not_powers_of_two(T):
     full_check(S(T=T, H=768, I=384, E=12, top_k=3), 90 + T, what=f"H=768 I=384 T={T}")
 
 
+@pytest.mark.parametrize("T", [3, 9, 200])
+def test_long_rows(T):
+    # H=4352, I=640: gate/up rows of 34 K-chunks (eight full four-chunk blocks of
+    # scale/bias words, then a block of two), down rows of 5 (one block, then one);
+    # H/8 = 544 takes the tiled router's fallback logits kernel
+    full_check(S(T=T, H=4352, I=640, E=8, top_k=2), 95 + T, what=f"H=4352 I=640 T={T}")
+
+
 def test_one_expert_takes_every_token():
     shape = S(T=700, H=256, I=128, E=8, top_k=2)
     layer = synth.draw_layer(shape, 62)
