@@ -11,10 +11,12 @@
 //    grid streams a slice of the router weight (reading W_r is a large share of
 //    a decode step's bytes, so it is spread over many CUs); the last workgroup to
 //    finish (ticket counter in the workspace control block) selects and groups.
-//  * large T (prefill): exact three-way bf16 split of W_r -> logits on bf16
-//    MFMA -> per-token top-k (wavefront per token) -> per-expert kernel that
-//    derives its own offset and writes its permutation segment in token order
-//    (no atomics, no histogram shared between workgroups).
+//  * large T (prefill): logits on bf16 MFMA from an exact three-way bf16 split
+//    of W_r (made inside the logits kernel, or by a kernel of its own for the
+//    fallback logits kernel) -> per-token top-k (wavefront per token) ->
+//    per-expert kernel that derives its own offset and writes its permutation
+//    segment in token order (no atomics, no histogram shared between
+//    workgroups).
 #include "device.h"
 #include "kernels.h"
 #include "lds_copy.h"
@@ -281,14 +283,19 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(
 
 // Partial logits over one eighth of H for a tile of 128 tokens x 64 experts, with
 // both operands staged in LDS (used when H/8 is a multiple of 64).  Each 64-k
-// chunk of the 128 activation rows and of the 3 x 64 weight-plane rows is copied
-// global -> LDS by global_load_lds (eight rows of 128 contiguous bytes per
-// instruction, so each instruction reads whole cache lines of eight rows), into
-// one of two stages while the other is multiplied.  Wavefront (i, j) computes
-// tokens 64i..64i+63 x experts 32j..32j+31 (four by two 16x16 blocks, three
-// planes each): per 32-k step, 10 LDS operand reads feed 24 MFMAs.  A row r of a
-// stage holds its 8 pieces of 16 bytes with logical piece p at p ^ ((r>>1)&7),
-// so the 16 rows of an operand read hit 16 distinct 4-bank groups.
+// chunk of the 128 activation rows is copied global -> LDS by global_load_lds
+// (eight rows of 128 contiguous bytes per instruction, so each instruction reads
+// whole cache lines of eight rows); the chunk's 64 x 64 fp32 router weights are
+// loaded by the threads (64 contiguous bytes each) and split in registers into
+// the three bf16 planes hi + mid + lo, which they write to LDS -- the same split
+// as k_router_split, done per workgroup instead of by a kernel of its own.  Two
+// stages: while chunk c is multiplied, chunk c+1's rows are copied and its
+// weights loaded, and the weights are split into the other stage after the
+// MFMAs.  Wavefront (i, j) computes tokens 64i..64i+63 x experts 32j..32j+31
+// (four by two 16x16 blocks, three planes each): per 32-k step, 10 LDS operand
+// reads feed 24 MFMAs.  A row r of a stage holds its 8 pieces of 16 bytes with
+// logical piece p at p ^ ((r>>1)&7), so the 16 rows of an operand read hit 16
+// distinct 4-bank groups.
 constexpr int kRlTok = 128;                  // tokens per workgroup
 constexpr int kRlExp = 64;                   // experts per workgroup
 constexpr int kRlKC = 64;                    // k per chunk
@@ -298,12 +305,11 @@ constexpr int kRlBRows = 3 * kRlExp;         // weight-plane rows per stage
 constexpr int kRlStage = (kRlARows + kRlBRows) * kRlRow;    // 40 KiB
 constexpr int kRlRowsPerCopy = 64 * 16 / kRlRow;            // 8 rows per copy instruction
 constexpr int kRlACopies = kRlARows / kRlRowsPerCopy / 4;   // per wavefront (4)
-constexpr int kRlBCopies = kRlBRows / kRlRowsPerCopy / 4;   // per wavefront (6)
 
 __device__ __forceinline__ int rl_swz(int r) { return (r >> 1) & 7; }
 
 __global__ __launch_bounds__(256, 2) void k_router_logits_lds(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes, int T, int H, int E,
+    const uint16_t* __restrict__ x, const float* __restrict__ Wr, int T, int H, int E,
     float* __restrict__ partial) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[2 * kRlStage];
     const int lane = threadIdx.x & (kWave - 1);
@@ -313,39 +319,58 @@ __global__ __launch_bounds__(256, 2) void k_router_logits_lds(
     const int e0 = blockIdx.x * kRlExp;
     const int ks = H / kRouterKSplit;          // a multiple of kRlKC here
     const int kbeg = blockIdx.z * ks;
-    const size_t plane = (size_t)E * H;
     const uint32_t ring = lds_addr(s_stage);
 
-    // copy addressing: lane L fills position L&7 of stage row 8q + (L>>3) of copy q
-    // with its logical piece; rows past T or E re-read the last valid row
+    // activation copies: lane L fills position L&7 of stage row 8q + (L>>3) of copy
+    // q with its logical piece; rows past T re-read the last valid row
     const uint64_t xbase = uniform64((uint64_t)(x + kbeg));
-    const uint64_t wbase = uniform64((uint64_t)(planes + kbeg));
     uint32_t a_off[kRlACopies];
-    uint64_t b_off[kRlBCopies];
 #pragma unroll
     for (int i = 0; i < kRlACopies; ++i) {
         const int row = (wave * kRlACopies + i) * kRlRowsPerCopy + (lane >> 3);
         const int logical = (lane & 7) ^ rl_swz(row);
         a_off[i] = (uint32_t)min(tbase + row, T - 1) * (uint32_t)(H * 2) + (uint32_t)logical * 16u;
     }
-#pragma unroll
-    for (int i = 0; i < kRlBCopies; ++i) {
-        const int row = (wave * kRlBCopies + i) * kRlRowsPerCopy + (lane >> 3);
-        const int p = row / kRlExp, e = min(e0 + row % kRlExp, E - 1);
-        const int logical = (lane & 7) ^ rl_swz(row);
-        b_off[i] = ((uint64_t)p * plane + (uint64_t)e * H) * 2 + (uint64_t)logical * 16u;
-    }
-    auto issue = [&](int c, int st) {
+    auto issue_a = [&](int c, int st) {
         const uint32_t sa = ring + st * kRlStage;
         const uint64_t xa = xbase + (uint64_t)c * kRlRow;
 #pragma unroll
         for (int i = 0; i < kRlACopies; ++i)
             dma16_to_lds(xa, a_off[i], sa + (wave * kRlACopies + i) * kRlRowsPerCopy * kRlRow);
-        const uint32_t sb = sa + kRlARows * kRlRow;
+    };
+    // weights: thread t owns expert row wr = t/4 (past E: the last expert) and k
+    // 16 wq .. 16 wq + 15 of each chunk, i.e. logical pieces 2 wq and 2 wq + 1 of
+    // that row in each plane
+    const int wr = threadIdx.x >> 2, wq = threadIdx.x & 3;
+    const float* wsrc = Wr + (size_t)min(e0 + wr, E - 1) * H + kbeg + 16 * wq;
+    auto load_w = [&](int c, float4 (&w)[4]) {
 #pragma unroll
-        for (int i = 0; i < kRlBCopies; ++i)
-            dma16v_to_lds(reinterpret_cast<const void*>(wbase + b_off[i] + (uint64_t)c * kRlRow),
-                          sb + (wave * kRlBCopies + i) * kRlRowsPerCopy * kRlRow);
+        for (int q = 0; q < 4; ++q) w[q] = *reinterpret_cast<const float4*>(wsrc + c * kRlKC + 4 * q);
+    };
+    auto store_w = [&](const float4 (&w)[4], int st) {
+        const float v[16] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w,
+                             w[2].x, w[2].y, w[2].z, w[2].w, w[3].x, w[3].y, w[3].z, w[3].w};
+        uint32_t hi[8], mid[8], lo[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            // w = hi + mid + lo exactly (see k_router_split)
+            hi[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+            const float r0 = v[2 * q] - bf16lo(hi[q]), r1 = v[2 * q + 1] - bf16hi(hi[q]);
+            mid[q] = pack_bf16x2(r0, r1);
+            lo[q] = pack_bf16x2(r0 - bf16lo(mid[q]), r1 - bf16hi(mid[q]));
+        }
+        uint8_t* sb = s_stage + st * kRlStage + kRlARows * kRlRow;
+        const int sw = rl_swz(wr);               // the same for the row in every plane
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int piece = ((2 * wq + h) ^ sw) * 16;
+            *reinterpret_cast<u32x4*>(sb + (0 * kRlExp + wr) * kRlRow + piece) =
+                u32x4{hi[4 * h], hi[4 * h + 1], hi[4 * h + 2], hi[4 * h + 3]};
+            *reinterpret_cast<u32x4*>(sb + (1 * kRlExp + wr) * kRlRow + piece) =
+                u32x4{mid[4 * h], mid[4 * h + 1], mid[4 * h + 2], mid[4 * h + 3]};
+            *reinterpret_cast<u32x4*>(sb + (2 * kRlExp + wr) * kRlRow + piece) =
+                u32x4{lo[4 * h], lo[4 * h + 1], lo[4 * h + 2], lo[4 * h + 3]};
+        }
     };
 
     f32x4 acc[4][2];
@@ -355,12 +380,19 @@ __global__ __launch_bounds__(256, 2) void k_router_logits_lds(
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int r16 = lane & 15, g = lane >> 4;
     const int nch = ks / kRlKC;
-    issue(0, 0);
+    float4 w[4];
+    issue_a(0, 0);
+    load_w(0, w);
+    store_w(w, 0);
     for (int c = 0; c < nch; ++c) {
         const int st = c & 1;
         wait_vmcnt<0>();
         __syncthreads();       // chunk c visible to all; the other stage is free
-        if (c + 1 < nch) issue(c + 1, st ^ 1);
+        const bool more = c + 1 < nch;
+        if (more) {
+            issue_a(c + 1, st ^ 1);
+            load_w(c + 1, w);
+        }
         const uint8_t* sa = s_stage + st * kRlStage;
         const uint8_t* sb = sa + kRlARows * kRlRow;
 #pragma unroll
@@ -385,6 +417,7 @@ __global__ __launch_bounds__(256, 2) void k_router_logits_lds(
                         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[nb][p], acc[mb][nb],
                                                                              0, 0, 0);
         }
+        if (more) store_w(w, st ^ 1);   // the stage read in iteration c-1, free since the barrier
     }
     float* out = partial + (size_t)blockIdx.z * T * E;
 #pragma unroll
@@ -554,23 +587,29 @@ hipError_t launch_route_small(const RouteArgs& a, hipStream_t st, KernelTimer& t
 }
 
 hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& tm) {
-    const long n = (long)a.E * a.H;
-    tm.before();
-    tm.launch(k_router_split, dim3((unsigned)min((n / 4 + 255) / 256, 1024L)), dim3(256), 0, st,
-                       a.Wr, n, a.ws_planes);
-    tm.after();
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    tm.before();
-    if ((a.H / kRouterKSplit) % kRlKC == 0)
+    hipError_t err;
+    if ((a.H / kRouterKSplit) % kRlKC == 0) {
+        // three launches: the logits kernel splits W_r itself
+        tm.before();
         tm.launch(k_router_logits_lds,
                   dim3((a.E + kRlExp - 1) / kRlExp, (a.T + kRlTok - 1) / kRlTok, kRouterKSplit),
-                  dim3(256), 0, st, a.x, a.ws_planes, a.T, a.H, a.E, a.ws_logits);
-    else
+                  dim3(256), 0, st, a.x, a.Wr, a.T, a.H, a.E, a.ws_logits);
+        tm.after();
+    } else {
+        // four launches: the weight planes first, for the fallback logits kernel
+        const long n = (long)a.E * a.H;
+        tm.before();
+        tm.launch(k_router_split, dim3((unsigned)min((n / 4 + 255) / 256, 1024L)), dim3(256), 0, st,
+                  a.Wr, n, a.ws_planes);
+        tm.after();
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        tm.before();
         tm.launch(k_router_logits_mfma,
                   dim3((a.E + kLgExp - 1) / kLgExp, (a.T + kLgTok - 1) / kLgTok, kRouterKSplit),
                   dim3(256), 0, st, a.x, a.ws_planes, a.T, a.H, a.E, a.ws_logits);
-    tm.after();
+        tm.after();
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
