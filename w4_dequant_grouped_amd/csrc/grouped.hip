@@ -334,8 +334,8 @@ __device__ __forceinline__ void b_addressing(TileSrc<NMAT, NBW>& t, const W4 (&m
 }
 
 // Copies of chunk c into stage c mod kStages: the wavefront's MB A copies (row
-// groups of the tile's row blocks only), then B codes, then scale/bias -- the
-// same count for every wavefront.
+// groups of the tile's row blocks only), then its B code blocks -- the same
+// count for every wavefront.
 template <int MB, int NMAT, int NBW>
 __device__ __forceinline__ void issue_chunk(uint32_t ring, int wave, const TileSrc<NMAT, NBW>& t, int c) {
     const int st = c % kStages;

@@ -40,7 +40,7 @@ struct RouteArgs {
     int32_t* perm;
     float* ws_logits;        // [T][E]
     uint32_t* ws_ticket;     // control block (zero between calls)
-    uint16_t* ws_planes;     // [3][E][H] bf16 split of the router weight (large T)
+    uint16_t* ws_planes;     // [3][E][H] bf16 split of the router weight (large T, fallback logits kernel)
 };
 
 struct ForwardArgs {
