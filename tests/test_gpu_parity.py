@@ -75,6 +75,14 @@ def test_tile_counts_not_powers_of_two(T):
     full_check(S(T=T, H=768, I=384, E=12, top_k=3), 90 + T, what=f"H=768 I=384 T={T}")
 
 
+@pytest.mark.parametrize("T", [9, 130])
+def test_partial_expert_tile(T):
+    # E=100 at H=512: the tiled router's LDS logits kernel (H/8 = 64) with a second
+    # tile of 36 experts (its weight rows past E clamped), two registers of logits per
+    # lane in the top-k
+    full_check(S(T=T, H=512, I=256, E=100, top_k=6), 105 + T, what=f"E=100 T={T}")
+
+
 @pytest.mark.parametrize("T", [3, 9, 200])
 def test_long_rows(T):
     # H=4352, I=640: gate/up rows of 34 K-chunks (eight full four-chunk blocks of
