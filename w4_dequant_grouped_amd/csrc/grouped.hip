@@ -195,23 +195,16 @@ __device__ __forceinline__ int grab_tile(uint32_t* qb, int n_mt, int NT, int& q,
     return -1;
 }
 
-// Tile scheduling state of a workgroup (meaningful in thread 0 only).  While a
-// tile is processed, the next entry of the current queue is already being
-// taken; its result is needed only when the tile is done.  `ran` counts the
-// tiles the workgroup ran.
+// Tile scheduling state of a workgroup (meaningful in thread 0 only).  A tile
+// is taken only once the workgroup is free to run it: an entry taken while the
+// previous tile still runs would be held back for a whole tile time, and near
+// the end of the list other workgroups would find the queues empty and leave
+// while such entries wait.  `ran` counts the tiles the workgroup ran.
 struct TileQueue {
     int q;               // current queue
     uint32_t empty;      // queues found empty
-    uint32_t taken;      // entry taken from queue q for the next tile
-    bool pending;
     uint32_t ran;
-    __device__ __forceinline__ void prefetch(uint32_t* qb) {
-        pending = !(empty & (1u << q));
-        if (pending) taken = queue_take(qb, q);
-    }
     __device__ __forceinline__ int next(uint32_t* qb, int n_mt, int NT) {
-        if (pending && taken < (uint32_t)queue_len(q, n_mt, NT)) return queue_start(q, n_mt, NT) + (int)taken;
-        if (pending) empty |= 1u << q;
         return grab_tile(qb, n_mt, NT, q, empty);
     }
 };
@@ -603,10 +596,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
     const int NT = I / BN;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = (int)uniform32(threadIdx.x / kWave);
-    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false, 0u};    // thread 0's scheduling state
+    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u};    // thread 0's scheduling state
     uint32_t* const qb = ctl + kCtlQueueGateUp;
 
-    if (threadIdx.x == 0) s_next = grab_tile(qb, n_mt, NT, tq.q, tq.empty);
+    if (threadIdx.x == 0) s_next = tq.next(qb, n_mt, NT);
     __syncthreads();
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
         int seg, mt, nt;
@@ -617,7 +610,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
         for (int r = threadIdx.x; r < c.rows; r += kThreads)
             s_tok[r] = c.shared ? (c.m0 + r) : min(max(perm[c.hbase + c.m0 + r], 0), T * k - 1) / k;
         __syncthreads();
-        if (threadIdx.x == 0) { tq.prefetch(qb); ++tq.ran; }
+        if (threadIdx.x == 0) ++tq.ran;
         const int nbase = nt * BN + wave * 16 * NBW;
 
         TileSrc<2, NBW> ts;
@@ -666,10 +659,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
     const int NT = H / BN;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = (int)uniform32(threadIdx.x / kWave);
-    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u, false, 0u};    // thread 0's scheduling state
+    TileQueue tq{(int)(blockIdx.x & 7), 0u, 0u};    // thread 0's scheduling state
     uint32_t* const qb = ctl + kCtlQueueDown;
 
-    if (threadIdx.x == 0) s_next = grab_tile(qb, n_mt, NT, tq.q, tq.empty);
+    if (threadIdx.x == 0) s_next = tq.next(qb, n_mt, NT);
     __syncthreads();
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
         int seg, mt, nt;
@@ -686,7 +679,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
             }
         }
         __syncthreads();
-        if (threadIdx.x == 0) { tq.prefetch(qb); ++tq.ran; }
+        if (threadIdx.x == 0) ++tq.ran;
         const int nbase = nt * BN + wave * 16 * NBW;
         TileSrc<1, NBW> ts;
         ts.a_base = uniform64((uint64_t)(h + (size_t)(c.hbase + c.m0) * I));
