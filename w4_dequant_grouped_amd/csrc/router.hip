@@ -468,10 +468,11 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ p
 // e.  Each workgroup reads all ids (T*k ints, L2-resident) and needs nothing
 // from the others: no histogram, no atomics.  Thread tid owns a contiguous run
 // of the flattened (t, j) entries, read kGroupBatch x 4 at a time with every
-// load of a batch issued together (once to count, once more, from L2, to write
-// its part of the permutation).  1024 threads keep each thread's run short (at
-// T = 16384 two batches per pass instead of eight), since the kernel is bound by
-// its dependent batches of loads.
+// load of a batch issued together, once to count and, if the run spans more
+// than one batch, once more from L2 to write its part of the permutation (a
+// run of one batch, T * k <= 65536, stays in registers between the passes).
+// 1024 threads keep each thread's run short (at T = 16384 two batches per pass
+// instead of eight), since the kernel is bound by its dependent batches of loads.
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupBatch = 16;          // int4 loads per thread issued together
 
@@ -502,8 +503,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_router_group(const int32_t* _
     const int per4 = (n4 + kGroupThreads - 1) / kGroupThreads;
     const int q0 = min(tid * per4, n4), q1 = min(q0 + per4, n4);
     int below = 0, hits = 0;
+    int4 w[kGroupBatch];                 // the last batch read; the whole run when it fits one
     for (int qb = q0; qb < q1; qb += kGroupBatch) {
-        int4 w[kGroupBatch];
 #pragma unroll
         for (int u = 0; u < kGroupBatch; ++u) {
             w[u] = int4{0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
@@ -543,12 +544,14 @@ __global__ __launch_bounds__(kGroupThreads) void k_router_group(const int32_t* _
         if (e == E - 1) offsets[E] = n;
     }
     if (hits == 0) return;
+    const bool one_batch = q1 - q0 <= kGroupBatch;
     for (int qb = q0; qb < q1; qb += kGroupBatch) {
-        int4 w[kGroupBatch];
+        if (!one_batch) {
 #pragma unroll
-        for (int u = 0; u < kGroupBatch; ++u) {
-            w[u] = int4{0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
-            if (qb + u < q1) group_load(ids, n, qb + u, w[u]);
+            for (int u = 0; u < kGroupBatch; ++u) {
+                w[u] = int4{0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
+                if (qb + u < q1) group_load(ids, n, qb + u, w[u]);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kGroupBatch; ++u) {
