@@ -41,6 +41,7 @@ struct RouteArgs {
     float* ws_logits;        // [T][E]
     uint32_t* ws_ticket;     // control block (zero between calls)
     uint16_t* ws_planes;     // [3][E][H] bf16 split of the router weight (large T, fallback logits kernel)
+    uint8_t* ws_ids8;        // [T*k] the chosen ids as bytes, padded to 16 (large T, E <= 256)
 };
 
 struct ForwardArgs {

@@ -32,7 +32,7 @@ static_assert(MOE_W4_GEMV_MAX_T == moe_w4::kDecodeMaxT, "GEMV kernels are built 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t logits, planes, h, y, total;
+    size_t logits, planes, ids8, h, y, total;
 };
 
 bool dims_ok(const moe_w4_dims* d, int* status) {
@@ -62,6 +62,8 @@ Layout layout(const moe_w4_dims* d) {
     off = align_up(off + T * E * sizeof(float) * (d->T > moe_w4::kSmallRouteMaxT ? moe_w4::kRouterKSplit : 1));
     L.planes = off;
     if (d->T > moe_w4::kSmallRouteMaxT) off = align_up(off + 3 * E * (size_t)d->H * 2);
+    L.ids8 = off;     // large T: the chosen ids as bytes for the grouping kernel
+    if (d->T > moe_w4::kSmallRouteMaxT) off = align_up(off + T * (size_t)d->top_k);
     L.h = off;
     off = align_up(off + (T * (size_t)d->top_k + T) * (size_t)d->I * 2);
     L.y = off;        // grouped path: per-(token, slot) output rows; decode block: slot table
@@ -161,6 +163,7 @@ hipError_t run_route(const moe_w4_dims* dims, const void* x, const float* router
     a.ws_ticket = reinterpret_cast<uint32_t*>(ws);
     a.ws_logits = reinterpret_cast<float*>(ws + L.logits);
     a.ws_planes = reinterpret_cast<uint16_t*>(ws + L.planes);
+    a.ws_ids8 = ws + L.ids8;
     return (a.T <= moe_w4::kSmallRouteMaxT) ? moe_w4::launch_route_small(a, stream, tm)
                                             : moe_w4::launch_route_large(a, stream, tm);
 }

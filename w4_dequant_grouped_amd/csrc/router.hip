@@ -440,7 +440,7 @@ template <int EPL>
 __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ partial,
                                                      const float* __restrict__ br, int T, int E,
                                                      int k, int32_t* __restrict__ ids,
-                                                     float* __restrict__ tw) {
+                                                     float* __restrict__ tw, uint8_t* __restrict__ ids8) {
     const int lane = threadIdx.x & (kWave - 1);
     const int t = blockIdx.x * 4 + (threadIdx.x / kWave);
     if (t >= T) return;
@@ -459,7 +459,8 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ p
         }
         vals[j] = v;
     }
-    wave_topk_select<EPL>(vals, E, k, lane, ids + (size_t)t * k, tw + (size_t)t * k);
+    wave_topk_select<EPL>(vals, E, k, lane, ids + (size_t)t * k, tw + (size_t)t * k, nullptr, nullptr,
+                          nullptr, ids8 ? ids8 + (size_t)t * k : nullptr);
 }
 
 // One workgroup per expert e.  Every token's ids are ascending, so
@@ -565,6 +566,99 @@ __global__ __launch_bounds__(kGroupThreads) void k_router_group(const int32_t* _
     }
 }
 
+// The same grouping over the ids as bytes (E <= 256), which the top-k kernel
+// writes beside the int32 ids: one 16-byte load brings 16 entries instead of 4,
+// so a thread's run is a quarter of the bytes and, up to T * k = 131072 (T =
+// 16384 at top-8), one batch that stays in registers for the writing pass.
+// Entries past T * k in the last 16-byte piece are not counted (every byte
+// value is a valid id, so they are masked by position).
+constexpr int kGroup8Batch = 8;          // 16-byte loads per thread issued together
+
+__device__ __forceinline__ void count_bytes(uint32_t w, int e, int nvalid, int& below, int& hits) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int v = (int)((w >> (8 * b)) & 0xFFu);
+        const bool ok = b < nvalid;
+        below += (ok && v < e) ? 1 : 0;
+        hits += (ok && v == e) ? 1 : 0;
+    }
+}
+
+__global__ __launch_bounds__(kGroupThreads) void k_router_group8(const uint8_t* __restrict__ ids8,
+                                                                 int T, int E, int k,
+                                                                 int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ perm) {
+    __shared__ int s_below[kGroupThreads / kWave];
+    __shared__ int s_hits[kGroupThreads / kWave];
+    const int e = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n = T * k;
+    const int n16 = (n + 15) / 16;
+    const int per = (n16 + kGroupThreads - 1) / kGroupThreads;
+    const int q0 = min(tid * per, n16), q1 = min(q0 + per, n16);
+    int below = 0, hits = 0;
+    u32x4 w[kGroup8Batch];               // the last batch read; the whole run when it fits one
+    for (int qb = q0; qb < q1; qb += kGroup8Batch) {
+#pragma unroll
+        for (int u = 0; u < kGroup8Batch; ++u)
+            if (qb + u < q1) w[u] = *reinterpret_cast<const u32x4*>(ids8 + 16 * (size_t)(qb + u));
+#pragma unroll
+        for (int u = 0; u < kGroup8Batch; ++u) {
+            if (qb + u >= q1) continue;
+            const int nv = n - 16 * (qb + u);          // >= 1 valid entries in this piece
+            count_bytes(w[u].x, e, nv, below, hits);
+            count_bytes(w[u].y, e, nv - 4, below, hits);
+            count_bytes(w[u].z, e, nv - 8, below, hits);
+            count_bytes(w[u].w, e, nv - 12, below, hits);
+        }
+    }
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    int incl = hits, bsum = below;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int vh = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += vh;
+        bsum += __shfl_xor(bsum, o, kWave);
+    }
+    if (lane == kWave - 1) s_hits[wave] = incl;
+    if (lane == 0) s_below[wave] = bsum;
+    __syncthreads();
+    int hits_before = 0, base = 0, total = 0;
+#pragma unroll
+    for (int v = 0; v < kGroupThreads / kWave; ++v) {
+        hits_before += (v < wave) ? s_hits[v] : 0;
+        total += s_hits[v];
+        base += s_below[v];
+    }
+    int pos = base + hits_before + incl - hits;
+    if (tid == 0) {
+        offsets[e] = base;
+        counts[e] = total;
+        if (e == E - 1) offsets[E] = n;
+    }
+    if (hits == 0) return;
+    const bool one_batch = q1 - q0 <= kGroup8Batch;
+    for (int qb = q0; qb < q1; qb += kGroup8Batch) {
+        if (!one_batch) {
+#pragma unroll
+            for (int u = 0; u < kGroup8Batch; ++u)
+                if (qb + u < q1) w[u] = *reinterpret_cast<const u32x4*>(ids8 + 16 * (size_t)(qb + u));
+        }
+#pragma unroll
+        for (int u = 0; u < kGroup8Batch; ++u) {
+            if (qb + u >= q1) continue;
+            const int i0 = 16 * (qb + u);
+            const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                const int v = (int)((ww[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+                if (i0 + b < n && v == e) perm[pos++] = i0 + b;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -618,19 +712,23 @@ hipError_t launch_route_large(const RouteArgs& a, hipStream_t st, KernelTimer& t
     tm.before();
     if (a.E <= 256)
         tm.launch(k_router_topk<4>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
-                           a.T, a.E, a.k, a.ids, a.w);
+                           a.T, a.E, a.k, a.ids, a.w, a.ws_ids8);
     else if (a.E <= 512)
         tm.launch(k_router_topk<8>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
-                           a.T, a.E, a.k, a.ids, a.w);
+                           a.T, a.E, a.k, a.ids, a.w, (uint8_t*)nullptr);
     else
         tm.launch(k_router_topk<16>, dim3((a.T + 3) / 4), dim3(256), 0, st, a.ws_logits, a.br,
-                           a.T, a.E, a.k, a.ids, a.w);
+                           a.T, a.E, a.k, a.ids, a.w, (uint8_t*)nullptr);
     tm.after();
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     tm.before();
-    tm.launch(k_router_group, dim3(a.E), dim3(kGroupThreads), 0, st, a.ids, a.T, a.E, a.k, a.counts,
-                       a.offsets, a.perm);
+    if (a.E <= 256)
+        tm.launch(k_router_group8, dim3(a.E), dim3(kGroupThreads), 0, st, (const uint8_t*)a.ws_ids8,
+                  a.T, a.E, a.k, a.counts, a.offsets, a.perm);
+    else
+        tm.launch(k_router_group, dim3(a.E), dim3(kGroupThreads), 0, st, (const int32_t*)a.ids, a.T,
+                  a.E, a.k, a.counts, a.offsets, a.perm);
     tm.after();
     return hipGetLastError();
 }

@@ -151,7 +151,8 @@ __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E
                                                  float* __restrict__ w_out,
                                                  int32_t* ids_lds = nullptr,
                                                  float* w_lds = nullptr,
-                                                 uint64_t* masks_out = nullptr) {
+                                                 uint64_t* masks_out = nullptr,
+                                                 uint8_t* __restrict__ ids8_out = nullptr) {
     uint32_t key[EPL];
     wave_order_keys<EPL>(vals, E, lane, key);
     bool sel[EPL];
@@ -176,6 +177,7 @@ __device__ __forceinline__ void wave_topk_select(const float (&vals)[EPL], int E
             const int rank = before + bits_below(chosen[j]);
             if (ids_out) ids_out[rank] = lane + kWave * j;
             if (ids_lds) ids_lds[rank] = lane + kWave * j;
+            if (ids8_out) ids8_out[rank] = (uint8_t)(lane + kWave * j);   // E <= 256
             if (w_out) {
                 w_out[rank] = p[j] * inv;
                 if (w_lds) w_lds[rank] = p[j] * inv;
