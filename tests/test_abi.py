@@ -65,11 +65,12 @@ def test_workspace_bytes(lib):
     small = B.moe_w4_workspace_bytes(_dims())
     big = B.moe_w4_workspace_bytes(_dims(T=2048, H=2048, I=512, E=256, top_k=8))
     assert small > 0 and small % 256 == 0
-    # K-split partial logits + bf16 split of the router weight + h (T*k + T rows of I) +
-    # per-(token, slot) bf16 output rows (T*k + T rows of H); no term for expanded expert weights
+    # K-split partial logits + bf16 split of the router weight + the chosen ids as bytes +
+    # h (T*k + T rows of I) + per-(token, slot) bf16 output rows (T*k + T rows of H); no term
+    # for expanded expert weights
     T, H, I, E, k = 2048, 2048, 512, 256, 8
-    expect_min = (B.MOE_W4_CONTROL_BYTES + 8 * T * E * 4 + 3 * E * H * 2 + (T * k + T) * I * 2
-                  + (T * k + T) * H * 2)
+    expect_min = (B.MOE_W4_CONTROL_BYTES + 8 * T * E * 4 + 3 * E * H * 2 + T * k
+                  + (T * k + T) * I * 2 + (T * k + T) * H * 2)
     assert expect_min <= big <= expect_min + 256 * 8
     # far below a bf16 expansion of the routed gate, up and down weights (1.6 GB)
     assert big < 3 * E * I * H * 2 // 10
