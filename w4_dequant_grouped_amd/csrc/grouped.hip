@@ -72,6 +72,12 @@ __device__ __forceinline__ int seg_count(const int32_t* __restrict__ offsets, in
 }
 
 // Per-segment M-tile counts -> exclusive prefix in LDS; returns the total.
+// Segment at sequence position p: the shared expert first (when present), then
+// the routed experts in id order.
+__device__ __forceinline__ int seq_segment(int p, int E, int has_shared) {
+    return has_shared ? (p == 0 ? E : p - 1) : p;
+}
+
 __device__ int build_mtile_prefix(const int32_t* __restrict__ offsets, int E, int T, int k,
                                   int has_shared, int* s_pre, int* s_tmp) {
     const int nseg = E + (has_shared ? 1 : 0);
@@ -80,7 +86,7 @@ __device__ int build_mtile_prefix(const int32_t* __restrict__ offsets, int E, in
     const int per = (nseg + kThreads - 1) / kThreads;
     const int s0 = min(tid * per, nseg), s1 = min(s0 + per, nseg);
     int local = 0;
-    for (int s = s0; s < s1; ++s) local += (seg_count(offsets, s, E, T, k) + kBM - 1) / kBM;
+    for (int s = s0; s < s1; ++s) local += (seg_count(offsets, seq_segment(s, E, has_shared), E, T, k) + kBM - 1) / kBM;
     s_tmp[tid] = local;
     __syncthreads();
     for (int o = 1; o < kThreads; o <<= 1) {
@@ -92,7 +98,7 @@ __device__ int build_mtile_prefix(const int32_t* __restrict__ offsets, int E, in
     int run = s_tmp[tid] - local;
     for (int s = s0; s < s1; ++s) {
         s_pre[s] = run;                  // exclusive prefix
-        run += (seg_count(offsets, s, E, T, k) + kBM - 1) / kBM;
+        run += (seg_count(offsets, seq_segment(s, E, has_shared), E, T, k) + kBM - 1) / kBM;
     }
     if (tid == kThreads - 1) s_pre[nseg] = s_tmp[kThreads - 1];
     __syncthreads();
@@ -113,22 +119,24 @@ __device__ __forceinline__ int find_segment(const int* s_pre, int nseg, int key,
     return (int)__builtin_amdgcn_readfirstlane(cnt - 1);
 }
 
-__device__ __forceinline__ TileCtx locate(int seg, int mt, const int* s_pre, int E, int T, int k,
-                                          const int32_t* __restrict__ offsets) {
+__device__ __forceinline__ TileCtx locate(int pos, int mt, const int* s_pre, int E, int T, int k,
+                                          int has_shared, const int32_t* __restrict__ offsets) {
     // every lane holds the same values: keep them in scalar registers
     TileCtx c;
+    const int seg = seq_segment(pos, E, has_shared);
     c.seg = seg;
     c.shared = (seg >= E);
     c.e = c.shared ? 0 : seg;
-    c.m0 = (int)__builtin_amdgcn_readfirstlane((mt - s_pre[seg]) * kBM);
+    c.m0 = (int)__builtin_amdgcn_readfirstlane((mt - s_pre[pos]) * kBM);
     c.rows = (int)__builtin_amdgcn_readfirstlane(min(kBM, seg_count(offsets, seg, E, T, k) - c.m0));
     c.hbase = (int)__builtin_amdgcn_readfirstlane(seg_first(offsets, seg, E, T, k));
     return c;
 }
 
-// Tile order.  The n_mt * NT tiles form one sequence: segment by segment, each
-// segment's M-tiles in blocks of kMtBlock, and within a block N-tile by N-tile,
-// the block's M-tiles innermost.  The tiles of one block that share an N-tile
+// Tile order.  The n_mt * NT tiles form one sequence: segment by segment (the
+// shared expert, whose M-tiles are all full, first, so that the list does not
+// end on them), each segment's M-tiles in blocks of kMtBlock, and within a block
+// N-tile by N-tile, the block's M-tiles innermost.  The tiles of one block that share an N-tile
 // read the same weight tile, and the NT tiles of one M-tile read the same
 // gathered activation rows; consecutive entries are taken at nearly the same
 // time by the workgroups of one XCD, so both kinds of operand reach that XCD's
@@ -140,8 +148,9 @@ __device__ __forceinline__ int div_small(int q, int d) {
     return d == 4 ? (q >> 2) : d == 3 ? q / 3 : d == 2 ? (q >> 1) : q;
 }
 
-// Sequence entry e -> (segment, global M-tile index, N-tile).  s_pre is the
-// exclusive M-tile prefix over the segments; segment s holds entries
+// Sequence entry e -> (sequence position of its segment, global M-tile index,
+// N-tile).  s_pre is the exclusive M-tile prefix over the segments in sequence
+// order (seq_segment gives the segment at a position); position s holds entries
 // [s_pre[s] * NT, s_pre[s + 1] * NT).
 __device__ __forceinline__ void tile_coords(int e, int NT, const int* s_pre, int nseg, int lane,
                                             int& seg, int& mt, int& nt) {
@@ -585,7 +594,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     uint16_t* __restrict__ h, uint32_t* ctl) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages * kStageBytes];
-    extern __shared__ int s_pre[];       // M-tile prefix over the segments (nseg + 1 entries)
+    extern __shared__ int s_pre[];       // M-tile prefix over the segments in sequence order (nseg + 1)
     __shared__ int s_tok[kBM];
     __shared__ int s_next;
 
@@ -604,7 +613,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
         int seg, mt, nt;
         tile_coords(i, NT, s_pre, nseg, lane, seg, mt, nt);
-        const TileCtx c = locate(seg, mt, s_pre, E, T, k, offsets);
+        const TileCtx c = locate(seg, mt, s_pre, E, T, k, has_shared, offsets);
         const W4Set& Wset = c.shared ? shared : routed;
         __syncthreads();                 // previous tile's readers are done
         for (int r = threadIdx.x; r < c.rows; r += kThreads)
@@ -647,7 +656,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
     const int32_t* __restrict__ perm, const uint16_t* __restrict__ h, uint16_t* __restrict__ y,
     uint32_t* ctl) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages * kStageBytes];
-    extern __shared__ int s_pre[];       // M-tile prefix over the segments (nseg + 1 entries)
+    extern __shared__ int s_pre[];       // M-tile prefix over the segments in sequence order (nseg + 1)
     __shared__ int s_dst[kBM];           // row of y each tile row goes to
     __shared__ float s_w[kBM];
     __shared__ int s_next;
@@ -667,7 +676,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
         int seg, mt, nt;
         tile_coords(i, NT, s_pre, nseg, lane, seg, mt, nt);
-        const TileCtx c = locate(seg, mt, s_pre, E, T, k, offsets);
+        const TileCtx c = locate(seg, mt, s_pre, E, T, k, has_shared, offsets);
         const W4Set& Wset = c.shared ? shared : routed;
         __syncthreads();
         for (int r = threadIdx.x; r < c.rows; r += kThreads) {
