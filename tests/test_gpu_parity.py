@@ -413,6 +413,17 @@ def test_six_way_tie_across_the_top12_boundary(T):
         check_output(out, O.forward_grouped(x, layer, ref, shape.group), what=f"6-way tie T={T}")
 
 
+@pytest.mark.parametrize("T,shared", [(9, True), (131, False)])
+def test_byte_id_grouping_at_256_experts(T, shared):
+    """E = 256 with top-8 and T*k not a multiple of 16 (72 and 1048 entries): the
+    grouping kernel reads the chosen ids as bytes, where every byte value is a
+    real expert id, so the padding of the last 16-byte piece must be masked by
+    position. Without a shared expert (T=131) the tile sequence starts with a
+    routed expert instead of the shared one."""
+    full_check(S(T=T, H=256, I=128, E=256, top_k=8, shared=shared), 120 + T,
+               what=f"E=256 byte ids T={T} shared={shared}")
+
+
 # --- largest sizes the ABI accepts ------------------------------------------------------
 
 @pytest.mark.parametrize("T", [2, 4, 64])
