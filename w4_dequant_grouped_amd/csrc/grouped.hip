@@ -105,10 +105,10 @@ __device__ int build_mtile_prefix(const int32_t* __restrict__ offsets, int E, in
     return s_pre[nseg];
 }
 
-// Last segment s with s_pre[s] <= key.  s_pre is nondecreasing and s_pre[0] = 0,
-// so that is the number of segments with s_pre[s] <= key, minus one: the lanes
-// test 64 segments per step with one LDS read each, and the reads of all steps
-// are independent (one LDS round trip instead of a chain of them).
+// Last sequence position s with s_pre[s] <= key.  s_pre is nondecreasing and
+// s_pre[0] = 0, so that is the number of positions with s_pre[s] <= key, minus
+// one: the lanes test 64 positions per step with one LDS read each, and the
+// reads of all steps are independent (one LDS round trip instead of a chain).
 __device__ __forceinline__ int find_segment(const int* s_pre, int nseg, int key, int lane) {
     int cnt = 0;
     for (int base = 0; base < nseg; base += kWave) {
@@ -153,11 +153,11 @@ __device__ __forceinline__ int div_small(int q, int d) {
 // order (seq_segment gives the segment at a position); position s holds entries
 // [s_pre[s] * NT, s_pre[s + 1] * NT).
 __device__ __forceinline__ void tile_coords(int e, int NT, const int* s_pre, int nseg, int lane,
-                                            int& seg, int& mt, int& nt) {
+                                            int& pos, int& mt, int& nt) {
     static_assert(kMtBlock >= 1 && kMtBlock <= 4, "div_small covers blocks of up to 4 M-tiles");
-    seg = find_segment(s_pre, nseg, e / NT, lane);   // s_pre[s] * NT <= e  <=>  s_pre[s] <= e / NT
-    const int first = s_pre[seg];
-    const int m_s = s_pre[seg + 1] - first;
+    pos = find_segment(s_pre, nseg, e / NT, lane);   // s_pre[s] * NT <= e  <=>  s_pre[s] <= e / NT
+    const int first = s_pre[pos];
+    const int m_s = s_pre[pos + 1] - first;
     const int r = e - first * NT;
     const int b = r / (kMtBlock * NT);
     const int rr = r - b * (kMtBlock * NT);
@@ -611,9 +611,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_gateup(
     if (threadIdx.x == 0) s_next = tq.next(qb, n_mt, NT);
     __syncthreads();
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
-        int seg, mt, nt;
-        tile_coords(i, NT, s_pre, nseg, lane, seg, mt, nt);
-        const TileCtx c = locate(seg, mt, s_pre, E, T, k, has_shared, offsets);
+        int pos, mt, nt;
+        tile_coords(i, NT, s_pre, nseg, lane, pos, mt, nt);
+        const TileCtx c = locate(pos, mt, s_pre, E, T, k, has_shared, offsets);
         const W4Set& Wset = c.shared ? shared : routed;
         __syncthreads();                 // previous tile's readers are done
         for (int r = threadIdx.x; r < c.rows; r += kThreads)
@@ -674,9 +674,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_grouped_down(
     if (threadIdx.x == 0) s_next = tq.next(qb, n_mt, NT);
     __syncthreads();
     for (int i = (int)uniform32(s_next); i >= 0; i = (int)uniform32(s_next)) {
-        int seg, mt, nt;
-        tile_coords(i, NT, s_pre, nseg, lane, seg, mt, nt);
-        const TileCtx c = locate(seg, mt, s_pre, E, T, k, has_shared, offsets);
+        int pos, mt, nt;
+        tile_coords(i, NT, s_pre, nseg, lane, pos, mt, nt);
+        const TileCtx c = locate(pos, mt, s_pre, E, T, k, has_shared, offsets);
         const W4Set& Wset = c.shared ? shared : routed;
         __syncthreads();
         for (int r = threadIdx.x; r < c.rows; r += kThreads) {
