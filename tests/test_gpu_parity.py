@@ -424,6 +424,15 @@ def test_byte_id_grouping_at_256_experts(T, shared):
                what=f"E=256 byte ids T={T} shared={shared}")
 
 
+@pytest.mark.parametrize("T", [16384, 16386])
+def test_byte_id_grouping_batch_boundary(T):
+    """The byte-id grouping at the edge of one batch per thread: T*k = 131072 fills
+    exactly one batch of 16-byte loads per thread, kept in registers for the writing
+    pass; T*k = 131088 needs a second batch, so both passes read the ids again."""
+    full_check(S(T=T, H=256, I=128, E=256, top_k=8), 130 + T % 7,
+               what=f"E=256 byte ids batch boundary T={T}")
+
+
 # --- largest sizes the ABI accepts ------------------------------------------------------
 
 @pytest.mark.parametrize("T", [2, 4, 64])
