@@ -433,6 +433,15 @@ def test_byte_id_grouping_batch_boundary(T):
                what=f"E=256 byte ids batch boundary T={T}")
 
 
+@pytest.mark.parametrize("T", [8192, 8193])
+def test_int32_id_grouping_batch_boundary(T):
+    """E = 512 keeps the grouping on int32 ids: T*k = 65536 fills exactly one batch of
+    16-byte loads per thread, kept in registers for the writing pass; T*k = 65544
+    needs a second batch."""
+    full_check(S(T=T, H=256, I=128, E=512, top_k=8), 140 + T % 7,
+               what=f"E=512 int32 ids batch boundary T={T}")
+
+
 # --- largest sizes the ABI accepts ------------------------------------------------------
 
 @pytest.mark.parametrize("T", [2, 4, 64])
